@@ -1,0 +1,166 @@
+"""CPU fp64 oracle for paged Multi-head Latent Attention decode.
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import this module.  The HIP library
+never calls it and shares no code with it.
+
+What it computes (deepseek.csdn.net, "FlashMLA ... 详解", section 2.2 "DeepSeek-V3
+的MLA机制"):
+
+* The output equation of that section: for query token t and head i,
+  o_{t,i} = sum_{j<=t} Softmax_j(q_{t,i}^T k_{j,i} / sqrt(d_h + d_h^R)) v_{j,i}.
+* The paragraph after it: only c^KV_t and k^R_t are cached; everything else is
+  recovered by matrix absorption.  After absorption a query head is one
+  576-wide row [W^UK^T q^C (512); q^R (64)], its keys are the cached rows
+  [c^KV (512); k^R (64)] (the concatenation order of equations (4) and (9)),
+  and its values are the first ``dv`` = 512 columns of the same rows (c^KV),
+  so the output stays in latent space.
+* The paged cache of section 4.2(1): 64-token blocks, ``block_table`` maps a
+  sequence's logical block to its physical page.
+* The call on the dolphin-ai.jp FlashMLA page ("FlashMLA の使用方法", step 4):
+  ``flash_mla_with_kvcache(q, kvcache, block_table, cache_seqlens, dv, ...,
+  causal)`` returns the output and the log-sum-exp.
+
+Readings where the pages are silent:
+
+* scale sigma = 1/sqrt(192) by default (d_h = 128, d_h^R = 64);
+* LSE = natural log of sum_j exp(sigma * q.k_j), the scale included;
+* causal rows are bottom-right aligned: the s_q new tokens are the last s_q
+  cache entries, query token i sees keys 0 .. L - s_q + i;
+* a row that sees no key returns O = 0, LSE = -inf;
+* query head h uses latent head h // (h_q / h_kv).
+
+Layouts: q [B][s_q][h_q][576], kvcache [P][64][h_kv][576], block_table
+[B][max_pages], cache_seqlens [B].  Returns O [B][s_q][h_q][dv] and LSE
+[B][h_q][s_q], both float64.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+PAGE_SIZE = 64
+DEFAULT_SCALE = 1.0 / math.sqrt(128 + 64)
+
+
+def as_f64(x) -> np.ndarray:
+    """Upcast a numpy array or a CPU torch tensor (bf16 included) to float64.
+    bf16 -> fp64 is exact."""
+    if hasattr(x, "detach"):
+        import torch  # only for the dtype conversion of a host tensor
+
+        return x.detach().to(torch.float64).cpu().numpy()
+    return np.asarray(x, dtype=np.float64)
+
+
+def gather_latent_rows(kvcache, block_table_row, seqlen: int, g: int) -> np.ndarray:
+    """Rows 0..seqlen-1 of one sequence's latent head g, in logical order, as
+    float64: token j lives at page block_table_row[j // 64], slot j % 64.
+    Slots at or beyond ``seqlen`` are never read.  ``kvcache`` may be a numpy
+    array or a host torch tensor; only the gathered slots are upcast."""
+    n_blocks = (seqlen + PAGE_SIZE - 1) // PAGE_SIZE
+    rows = np.empty((seqlen, kvcache.shape[-1]), dtype=np.float64)
+    for blk in range(n_blocks):
+        page = int(block_table_row[blk])
+        count = min(PAGE_SIZE, seqlen - blk * PAGE_SIZE)
+        rows[blk * PAGE_SIZE: blk * PAGE_SIZE + count] = as_f64(kvcache[page, :count, g, :])
+    return rows
+
+
+def visible_keys(seqlen: int, s_q: int, i: int, causal: bool) -> int:
+    """How many leading keys query token i sees (bottom-right causal alignment)."""
+    if not causal:
+        return seqlen
+    return max(0, min(seqlen, seqlen - s_q + i + 1))
+
+
+def attend(q_rows: np.ndarray, keys: np.ndarray, n_vis, dv: int, scale: float, return_p=False):
+    """Softmax attention of each query row r over its first n_vis[r] keys.
+
+    s_j = scale * q.k_j;  LSE = m + ln sum_j exp(s_j - m) with m = max_j s_j;
+    p_j = exp(s_j - LSE);  O = sum_j p_j * k_j[0:dv].
+    Rows with no visible key give O = 0, LSE = -inf."""
+    R = q_rows.shape[0]
+    S = scale * (q_rows @ keys.T) if keys.shape[0] else np.zeros((R, 0))
+    O = np.zeros((R, dv))
+    lse = np.full(R, -np.inf)
+    ps = []
+    for r in range(R):
+        n = int(n_vis[r])
+        if n == 0:
+            ps.append(np.zeros(0))
+            continue
+        s = S[r, :n]
+        m = s.max()
+        lse[r] = m + math.log(np.exp(s - m).sum())
+        p = np.exp(s - lse[r])
+        O[r] = p @ keys[:n, :dv]
+        ps.append(p)
+    return (O, lse, ps) if return_p else (O, lse)
+
+
+def mla_decode_ref(q, kvcache, block_table, cache_seqlens, dv: int = 512, causal: bool = False,
+                   softmax_scale: float | None = None, return_p: bool = False, batch_subset=None):
+    """Paged MLA decode, by definition, in float64.
+
+    For each sequence b and latent head g: gather the sequence's cached rows
+    in logical order, take the s_q * (h_q/h_kv) query rows that share head g,
+    and apply :func:`attend` with each row's causal key count.
+    ``batch_subset`` restricts the work to some sequences (others stay 0/-inf)."""
+    q = as_f64(q)
+    bt = np.asarray(block_table)
+    L = np.asarray(cache_seqlens).astype(np.int64)
+    B, s_q, h_q, D = q.shape
+    h_kv = kvcache.shape[2]
+    assert kvcache.shape[1] == PAGE_SIZE and kvcache.shape[3] == D and h_q % h_kv == 0
+    G = h_q // h_kv
+    scale = DEFAULT_SCALE if softmax_scale is None else float(softmax_scale)
+    O = np.zeros((B, s_q, h_q, dv))
+    LSE = np.full((B, h_q, s_q), -np.inf)
+    P = {}
+    for b in (range(B) if batch_subset is None else batch_subset):
+        for g in range(h_kv):
+            keys = gather_latent_rows(kvcache, bt[b], int(L[b]), g)
+            rows = q[b, :, g * G:(g + 1) * G, :].reshape(s_q * G, D)
+            n_vis = [visible_keys(int(L[b]), s_q, r // G, causal) for r in range(s_q * G)]
+            res = attend(rows, keys, n_vis, dv, scale, return_p)
+            o_bg, lse_bg = res[0], res[1]
+            O[b, :, g * G:(g + 1) * G, :] = o_bg.reshape(s_q, G, dv)
+            LSE[b, g * G:(g + 1) * G, :] = lse_bg.reshape(s_q, G).T
+            if return_p:
+                for r in range(s_q * G):
+                    P[(b, r // G, g * G + r % G)] = res[2][r]
+    return (O, LSE, P) if return_p else (O, LSE)
+
+
+def attend_range(q_rows: np.ndarray, keys: np.ndarray, lo: int, hi: int, n_vis, dv: int, scale: float):
+    """Attention restricted to keys [lo, hi) (and to each row's visible prefix):
+    the normalised partial output and its log-sum-exp, as one split of the key
+    range produces them (deepseek.csdn.net article, section 4.2(1): a split-KV
+    forward kernel followed by a kernel that merges the splits)."""
+    R = q_rows.shape[0]
+    vis = [max(0, min(hi, int(n_vis[r])) - lo) for r in range(R)]
+    sub = keys[lo:hi]
+    return attend(q_rows, sub, vis, dv, scale)
+
+
+def lse_combine_ref(partial_o: np.ndarray, partial_lse: np.ndarray):
+    """Merge n partial results of disjoint key ranges.
+
+    partial_o [n][R][dv] (each normalised by its own sum), partial_lse [n][R].
+    lse = M + ln sum_s exp(lse_s - M) with M = max_s lse_s, and
+    O = sum_s exp(lse_s - lse) * O_s.  Splits with lse_s = -inf carry no
+    weight; if every split is empty the row is O = 0, lse = -inf."""
+    n, R, dv = partial_o.shape
+    O = np.zeros((R, dv))
+    lse = np.full(R, -np.inf)
+    for r in range(R):
+        ls = partial_lse[:, r]
+        M = ls.max() if n else -np.inf
+        if not np.isfinite(M):
+            continue
+        lse[r] = M + math.log(np.exp(ls - M).sum())
+        w = np.exp(ls - lse[r])
+        O[r] = (w[:, None] * partial_o[:, r, :]).sum(axis=0)
+    return O, lse
