@@ -1,0 +1,217 @@
+"""Benchmark of one paged MLA decode step on one MI355X.
+
+A step is the whole hot path over one batch: the split-KV decode kernel and
+the log-sum-exp combine (the scheduler metadata is computed once per batch of
+sequence lengths and timed separately).  Inputs are seeded synthetic bf16
+tensors resident in HBM before timing starts.  Successive steps alternate
+between independent KV pools whose total exceeds the 256 MB Infinity Cache,
+so every step streams its cache from HBM.
+
+Prints one JSON line.  `value` is achieved algorithmic bandwidth (GB/s) of the
+whole step; `roofline` rates the dominant kernel (the decode kernel) against
+MI355X's 8 TB/s HBM or 2.5 PFLOP/s dense bf16 MFMA peak, with its duration
+measured by HIP events on the launch stream.
+
+    python bench.py [--steps K] [--warmup W] [--workload mem_bound] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+METRIC = "paged MLA decode: achieved HBM GB/s & TFLOPS (bf16), % of MI355X roofline"
+HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+MALL_BYTES = 256 << 20
+BOUND = {"mem_bound": "hbm", "var_len": "hbm", "skewed": "hbm", "causal_sq2": "mfma", "tiny": "hbm"}
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="mem_bound")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget-s", type=float, default=15.0)
+    return ap.parse_args()
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for name in ("mla_decode.hip", "mla_kernels.h"):
+        with open(os.path.join(ROOT, "paged_mla_decode_03_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per decode launch from committed rocprofv3 counter runs, if
+    they were taken on the current kernel source (else None)."""
+    path = os.path.join(ROOT, "profiles", f"mla_decode_kernel_{workload}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(inp, budget_s: float) -> dict:
+    """The CPU oracle, untuned, on a bounded sample of the same workload:
+    whole sequences, in order, until the time budget is spent."""
+    from threadpoolctl import threadpool_info
+
+    from oracle.mla_oracle import mla_decode_ref
+    from workloads import algorithmic_counts
+
+    w = inp.workload
+    L = inp.cache_seqlens.numpy()
+    bt = inp.block_table.numpy()
+    done, t0 = [], time.perf_counter()
+    for b in range(w.batch):
+        mla_decode_ref(inp.q, inp.kvcache, bt, L, 512, causal=w.causal, batch_subset=[b])
+        done.append(b)
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    sub = algorithmic_counts(w, L[done], bt.shape[1])
+    threads = max([t.get("num_threads", 1) for t in threadpool_info()] + [1])
+    return {"value": round(sub["total_bytes"] / dt / 1e9, 4), "unit": "GB/s", "cores": int(threads),
+            "kind": "oracle", "tflops": round(sub["flops"] / dt / 1e12, 6), "seconds": round(dt, 3),
+            "sample": f"{len(done)} of {w.batch} sequences ({int(L[done].sum())} cached tokens), float64 numpy"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this benchmark runs on one GPU; a sharded path is not built "
+                          "(the decode shards by sequence with no exchange, see the design notes)",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    import torch
+
+    sys.path.insert(0, ROOT)
+    from paged_mla_decode_03_amd import (DecodeBuffers, get_mla_metadata, mla_combine_splits,
+                                         mla_decode_splitkv)
+    from workloads import WORKLOADS, algorithmic_counts, make_inputs
+
+    dev = torch.device("cuda", 0)
+    w = WORKLOADS[args.workload]
+    print(f"[bench] generating {args.workload} (seed {args.seed})", file=sys.stderr, flush=True)
+    inp = make_inputs(w, args.seed)
+    L = inp.cache_seqlens.numpy()
+    counts = algorithmic_counts(w, L, inp.block_table.shape[1])
+
+    q = inp.q.to(dev)
+    bt = inp.block_table.to(dev)
+    seqlens = inp.cache_seqlens.to(dev)
+    kv_bytes = inp.kvcache.numel() * 2
+    n_pools = max(2, -(-2 * MALL_BYTES // kv_bytes) + 1)
+    pools = [inp.kvcache.to(dev)]
+    for i in range(1, n_pools):
+        pools.append(pools[0].clone())
+    rows = w.s_q * w.h_q // w.h_kv
+
+    # Scheduler metadata (once per batch of lengths), timed on its own.
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    meta, ns = get_mla_metadata(seqlens, rows, w.h_kv)
+    e0.record()
+    for _ in range(10):
+        meta, ns = get_mla_metadata(seqlens, rows, w.h_kv)
+    e1.record()
+    torch.cuda.synchronize()
+    metadata_us = e0.elapsed_time(e1) / 10 * 1e3
+    W = meta.shape[0]
+    buf = DecodeBuffers(q, pools[0], 512, W)
+
+    def step(i, evs=None):
+        kv = pools[i % n_pools]
+        if evs:
+            evs[0].record()
+        mla_decode_splitkv(q, kv, bt, seqlens, 512, meta, ns, causal=w.causal, buffers=buf)
+        if evs:
+            evs[1].record()
+        mla_combine_splits(ns, w.s_q, w.h_q, w.h_kv, 512, W, buf)
+        if evs:
+            evs[2].record()
+
+    print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for i in range(args.steps):
+        step(i, evs[i])
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t_start) * 1e3
+    decode_ms = np.array([a.elapsed_time(b) for a, b, _ in evs])
+    combine_ms = np.array([b.elapsed_time(c) for _, b, c in evs])
+    step_ms = np.array([a.elapsed_time(c) for a, _, c in evs])
+    ms_per_step = wall_ms / args.steps
+    print(f"[bench] {args.steps} steps: {ms_per_step * 1e3:.1f} us/step (wall), decode kernel "
+          f"{decode_ms.mean() * 1e3:.1f} us, combine {combine_ms.mean() * 1e3:.1f} us", file=sys.stderr, flush=True)
+
+    gbs = counts["total_bytes"] / (ms_per_step * 1e-3) / 1e9
+    tflops = counts["flops"] / (ms_per_step * 1e-3) / 1e12
+    dec_s = decode_ms.mean() * 1e-3
+    bound = BOUND.get(args.workload, "hbm")
+    if bound == "hbm":
+        achieved, peak, unit = counts["total_bytes"] / dec_s / 1e9, HBM_PEAK_GBS, "GB/s"
+    else:
+        achieved, peak, unit = counts["flops"] / dec_s / 1e12, MFMA_BF16_PEAK_TFLOPS, "TFLOP/s"
+    traffic = measured_traffic(args.workload)
+    out = {
+        "metric": METRIC,
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "batch": w.batch, "s_q": w.s_q, "h_q": w.h_q, "h_kv": w.h_kv,
+                   "d_qk": 576, "dv": 512, "page_size": 64, "causal": w.causal,
+                   "seqlen_total": int(L.sum()), "seqlen_max": int(L.max()), "seed": args.seed,
+                   "kv_pools": n_pools, "num_workers": W},
+        "tflops": round(tflops, 2),
+        "us_per_step": round(ms_per_step * 1e3, 2),
+        "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+        "mfma_frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+        "decode_kernel_us": round(decode_ms.mean() * 1e3, 2),
+        "combine_kernel_us": round(combine_ms.mean() * 1e3, 2),
+        "step_event_us_p10_p50_p90": [round(float(np.percentile(step_ms, p)) * 1e3, 2) for p in (10, 50, 90)],
+        "metadata_us": round(metadata_us, 2),
+        "algorithmic_bytes": counts["total_bytes"],
+        "algorithmic_flops": counts["flops"],
+        "roofline": {"kernel": "mla_decode_kernel", "bound": bound, "achieved": round(achieved, 2),
+                     "peak": peak, "unit": unit, "frac": round(achieved / peak, 4),
+                     "traffic": traffic,
+                     "per_launch": {"bytes": counts["total_bytes"], "flops": counts["flops"]}},
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(inp, args.cpu_budget_s)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

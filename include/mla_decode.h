@@ -1,0 +1,152 @@
+/*
+ * mla_decode.h -- C ABI of the MI355X (gfx950) paged MLA decode library.
+ *
+ * The operation (deepseek.csdn.net FlashMLA article, section 2.2, the MLA
+ * output equation and the matrix-absorption paragraph after it): for every
+ * sequence b, query token i and query head h,
+ *
+ *     O[b,i,h,:]  = sum_j softmax_j(sigma * q[b,i,h,:] . K_b[j,:]) * K_b[j, 0:dv]
+ *     LSE[b,h,i]  = ln sum_j exp(sigma * q[b,i,h,:] . K_b[j,:])
+ *
+ * where K_b[j] is the cached latent row [c^KV (512); k^R (64)] of token j of
+ * sequence b for latent head h / (h_q / h_kv), the sum runs over the tokens
+ * the query sees (all L_b tokens, or with causal=1 tokens 0 .. L_b - s_q + i),
+ * and sigma defaults to 1/sqrt(192).  Rows that see no token get O = 0 and
+ * LSE = -inf.  The cache is paged in 64-token blocks addressed through
+ * block_table (same article, section 4.2(1)).
+ *
+ * The two calls follow the usage on the dolphin-ai.jp FlashMLA page
+ * ("FlashMLA の使用方法", steps 3 and 4):
+ *     get_mla_metadata(cache_seqlens, s_q*h_q/h_kv, h_kv)
+ *         -> tile_scheduler_metadata, num_splits
+ *     flash_mla_with_kvcache(q, kvcache, block_table, cache_seqlens, dv,
+ *                            tile_scheduler_metadata, num_splits, causal)
+ *         -> o, lse
+ *
+ * Conventions for every entry point:
+ *   - Pointers marked [dev] are device memory; the caller owns every buffer.
+ *     The library allocates nothing and keeps only a per-device cache of the
+ *     compute-unit count.
+ *   - `stream` is a hipStream_t (NULL = the null stream).  Launches are
+ *     asynchronous and stream-ordered; nothing synchronises the host.  Inputs
+ *     must stay alive until the stream has run the work.
+ *   - Calls return MLA_OK or a negative status.  Arguments are checked on the
+ *     host before anything is launched, so an invalid call launches nothing.
+ *     The *contents* of block_table and cache_seqlens cannot be checked on the
+ *     host: page ids outside [0, num_pages) or lengths above
+ *     64 * max_pages_per_seq are undefined behaviour.
+ *   - Fixed sizes: d_qk = 576, dv = 512, page size 64, bf16 q / kvcache / o,
+ *     fp32 lse.  All tensors are dense and row-major in the layouts below.
+ */
+#ifndef MLA_DECODE_H
+#define MLA_DECODE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MLA_OK 0
+#define MLA_ERR_INVALID_ARG (-1)  /* null pointer, non-positive size, h_q % h_kv != 0, ... */
+#define MLA_ERR_UNSUPPORTED (-2)  /* d_qk != 576, dv != 512, misaligned pointer, size limits */
+#define MLA_ERR_WORKSPACE (-3)    /* workspace smaller than mla_workspace_bytes() */
+#define MLA_ERR_METADATA (-4)     /* num_workers inconsistent with the launch */
+#define MLA_ERR_HIP (-5)          /* the HIP runtime reported an error */
+
+#define MLA_PAGE_SIZE 64
+#define MLA_D_QK 576
+#define MLA_D_V 512
+#define MLA_METADATA_INTS 8       /* ints per worker row of tile_scheduler_metadata */
+#define MLA_ROWS_PER_BLOCK 128    /* query rows one workgroup serves */
+#define MLA_MAX_WORKERS 4096
+
+/* Text for a status code (static storage, never NULL). */
+const char* mla_status_string(int status);
+
+/* Number of scheduler workers W for a launch on `device` (-1 = current
+ * device): W = max(1, CUs / (h_kv * ceil(rows_per_kv / 128))), capped at
+ * MLA_MAX_WORKERS.  rows_per_kv = s_q * h_q / h_kv.  Host-only; reads the
+ * device's compute-unit count once and caches it. */
+int mla_num_workers(int device, int rows_per_kv, int h_kv, int* num_workers);
+
+/* The split rule's fixed per-sequence overhead F, in page units. */
+int mla_sched_fixed_overhead(void);
+
+/* Split-KV tile scheduler (dolphin-ai.jp FlashMLA page, "FlashMLA の使用方法"
+ * step 3; balance over variable lengths: deepseek.csdn.net article, section
+ * 4.2(2)).  Each sequence is F overhead units followed by ceil(L_b/64) page
+ * units on one cost line of total T; worker w owns units [w*Q, (w+1)*Q) with
+ * Q = max(1, ceil(T / W)).  Writes, on the device, with one workgroup and no
+ * host synchronisation:
+ *   tile_scheduler_metadata [dev] int32 [num_workers][8]: per worker
+ *       (begin_b, begin_page, end_b, end_page_exclusive, split ordinal of its
+ *        first segment, 0, 0, 0); a worker with no pages gets
+ *       (0, 0, -1, 0, 0, 0, 0, 0);
+ *   num_splits [dev] int32 [batch + 1]: exclusive prefix sums of the number
+ *       of splits of each sequence (num_splits[0] = 0).
+ * cache_seqlens [dev] int32 [batch].  num_workers must be the value
+ * mla_num_workers() gives for the same rows_per_kv and h_kv (any value in
+ * [1, MLA_MAX_WORKERS] is accepted; mla_decode_paged must get the same). */
+int mla_get_metadata(const int32_t* cache_seqlens, int batch, int rows_per_kv, int h_kv,
+                     int num_workers, int32_t* tile_scheduler_metadata, int32_t* num_splits,
+                     void* stream);
+
+/* Bytes of fp32 workspace mla_decode_paged needs for split partials:
+ * (num_workers + batch) * h_kv * (s_q*h_q/h_kv) * (dv + 1) * 4, rounded up to
+ * 256.  Returns 0 for invalid sizes. */
+size_t mla_workspace_bytes(int batch, int s_q, int h_q, int h_kv, int dv, int num_workers);
+
+/* Paged MLA decode: split-KV attention over the paged latent cache followed
+ * by the log-sum-exp merge of the splits (deepseek.csdn.net article, section
+ * 4.2(1)).
+ *   q              [dev] bf16 [batch][s_q][h_q][576], 16-byte aligned
+ *   kvcache        [dev] bf16 [num_pages][64][h_kv][576], 16-byte aligned;
+ *                  row = [c^KV (512); k^R (64)]; V = its first dv columns
+ *   block_table    [dev] int32 [batch][max_pages_per_seq]; entries past
+ *                  ceil(L_b/64) are never read (padding may be -1)
+ *   cache_seqlens  [dev] int32 [batch], 0 <= L_b <= 64 * max_pages_per_seq
+ *   d_qk, dv       must be 576 and 512
+ *   tile_scheduler_metadata, num_splits, num_workers: from mla_get_metadata
+ *                  with rows_per_kv = s_q*h_q/h_kv and the same h_kv
+ *   causal         0 or 1; query token i sits at position L_b - s_q + i
+ *   softmax_scale  <= 0 selects 1/sqrt(192)
+ *   o              [dev] bf16 [batch][s_q][h_q][dv], 16-byte aligned
+ *   lse            [dev] fp32 [batch][h_q][s_q], natural log, scale included
+ *   workspace      [dev] >= mla_workspace_bytes(...) bytes, 256-byte aligned
+ * Launches the decode kernel then the combine kernel on `stream`. */
+int mla_decode_paged(const void* q, const void* kvcache, const int32_t* block_table,
+                     int max_pages_per_seq, int num_pages, const int32_t* cache_seqlens,
+                     int batch, int s_q, int h_q, int h_kv, int d_qk, int dv,
+                     const int32_t* tile_scheduler_metadata, const int32_t* num_splits,
+                     int num_workers, int causal, float softmax_scale, void* o, float* lse,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+/* The first of the two launches of mla_decode_paged alone: the split-KV
+ * decode kernel.  It writes o/lse of every sequence that has exactly one
+ * split and fp32 partials of the others into the workspace.  Same arguments
+ * and checks as mla_decode_paged. */
+int mla_decode_splitkv(const void* q, const void* kvcache, const int32_t* block_table,
+                       int max_pages_per_seq, int num_pages, const int32_t* cache_seqlens,
+                       int batch, int s_q, int h_q, int h_kv, int d_qk, int dv,
+                       const int32_t* tile_scheduler_metadata, const int32_t* num_splits,
+                       int num_workers, int causal, float softmax_scale, void* o, float* lse,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
+/* The second launch alone: the log-sum-exp merge.  For each sequence with
+ * n_b = num_splits[b+1] - num_splits[b] partials: n_b = 0 writes O = 0 and
+ * LSE = -inf, n_b = 1 leaves what the decode kernel wrote, n_b > 1 writes
+ * lse = M + ln sum_s exp(lse_s - M) (M = max_s lse_s) and
+ * O = sum_s exp(lse_s - lse) * O_s in bf16.  The partials sit in the
+ * workspace as fp32 O_s [slot][h_kv][rows][dv] followed by fp32 lse_s
+ * [slot][h_kv][rows], slot = num_splits[b] + split ordinal. */
+int mla_combine_splits(const int32_t* num_splits, int batch, int s_q, int h_q, int h_kv, int dv,
+                       int num_workers, void* o, float* lse, const void* workspace,
+                       size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_DECODE_H */

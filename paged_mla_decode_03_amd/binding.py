@@ -1,0 +1,207 @@
+"""Python binding of the C ABI in ``include/mla_decode.h`` (ctypes).
+
+Argument marshalling only: tensors are checked and their device pointers and
+torch's current HIP stream are handed to the library, which runs every step
+on the GPU.  The names and argument order follow the usage shown on the
+dolphin-ai.jp FlashMLA page ("FlashMLA の使用方法", steps 3 and 4):
+
+    tile_scheduler_metadata, num_splits = get_mla_metadata(cache_seqlens, s_q * h_q // h_kv, h_kv)
+    o, lse = mla_decode_paged(q, kvcache, block_table, cache_seqlens, dv,
+                              tile_scheduler_metadata, num_splits, causal=True)
+
+torch must be imported before the library is loaded: the library binds to
+the HIP runtime torch loaded (same soname), so torch's streams are valid
+handles for it.  There is no fallback: if the library is missing this module
+raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libmla_decode.so")
+
+MLA_OK = 0
+PAGE_SIZE = 64
+D_QK = 576
+D_V = 512
+METADATA_INTS = 8
+
+_lib = None
+
+
+class MlaError(RuntimeError):
+    def __init__(self, func: str, status: int):
+        msg = _load().mla_status_string(status).decode()
+        super().__init__(f"{func} failed: {msg} ({status})")
+        self.status = status
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is not built; run paged_mla_decode_03_amd.build.build() first")
+    lib = ctypes.CDLL(LIB_PATH)
+    c_int, c_size_t, vp, c_float = ctypes.c_int, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_float
+    lib.mla_status_string.restype = ctypes.c_char_p
+    lib.mla_status_string.argtypes = [c_int]
+    lib.mla_num_workers.restype = c_int
+    lib.mla_num_workers.argtypes = [c_int, c_int, c_int, ctypes.POINTER(c_int)]
+    lib.mla_sched_fixed_overhead.restype = c_int
+    lib.mla_sched_fixed_overhead.argtypes = []
+    lib.mla_get_metadata.restype = c_int
+    lib.mla_get_metadata.argtypes = [vp, c_int, c_int, c_int, c_int, vp, vp, vp]
+    lib.mla_workspace_bytes.restype = c_size_t
+    lib.mla_workspace_bytes.argtypes = [c_int, c_int, c_int, c_int, c_int, c_int]
+    decode_args = [vp, vp, vp, c_int, c_int, vp, c_int, c_int, c_int, c_int, c_int, c_int,
+                   vp, vp, c_int, c_int, c_float, vp, vp, vp, c_size_t, vp]
+    for name in ("mla_decode_paged", "mla_decode_splitkv"):
+        f = getattr(lib, name)
+        f.restype = c_int
+        f.argtypes = decode_args
+    lib.mla_combine_splits.restype = c_int
+    lib.mla_combine_splits.argtypes = [vp, c_int, c_int, c_int, c_int, c_int, c_int, vp, vp, vp, c_size_t, vp]
+    _lib = lib
+    return lib
+
+
+def library():
+    """The loaded ctypes library (loads it on first use)."""
+    return _load()
+
+
+def _check(func: str, status: int):
+    if status != MLA_OK:
+        raise MlaError(func, status)
+
+
+def _stream_handle(device: torch.device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _require(t: torch.Tensor, name: str, dtype: torch.dtype, device: torch.device):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def num_workers(rows_per_kv: int, h_kv: int, device: Optional[torch.device] = None) -> int:
+    device = device or torch.device("cuda", torch.cuda.current_device())
+    w = ctypes.c_int(0)
+    _check("mla_num_workers", _load().mla_num_workers(device.index or 0, rows_per_kv, h_kv, ctypes.byref(w)))
+    return w.value
+
+
+def fixed_overhead_pages() -> int:
+    return _load().mla_sched_fixed_overhead()
+
+
+def get_mla_metadata(cache_seqlens: torch.Tensor, rows_per_kv: int, h_kv: int,
+                     num_workers_override: Optional[int] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Split-KV tile scheduler.  Returns (tile_scheduler_metadata int32 [W][8],
+    num_splits int32 [B+1]), computed on the GPU without a host sync."""
+    device = cache_seqlens.device
+    _require(cache_seqlens, "cache_seqlens", torch.int32, device)
+    B = cache_seqlens.numel()
+    W = num_workers_override or num_workers(rows_per_kv, h_kv, device)
+    meta = torch.empty((W, METADATA_INTS), dtype=torch.int32, device=device)
+    ns = torch.empty((B + 1,), dtype=torch.int32, device=device)
+    _check("mla_get_metadata", _load().mla_get_metadata(
+        cache_seqlens.data_ptr(), B, rows_per_kv, h_kv, W, meta.data_ptr(), ns.data_ptr(), _stream_handle(device)))
+    return meta, ns
+
+
+def workspace_bytes(batch: int, s_q: int, h_q: int, h_kv: int, dv: int, W: int) -> int:
+    return int(_load().mla_workspace_bytes(batch, s_q, h_q, h_kv, dv, W))
+
+
+def _decode_call(entry: str, q, kvcache, block_table, cache_seqlens, dv, tile_scheduler_metadata, num_splits,
+                 causal, softmax_scale, o, lse, workspace):
+    device = q.device
+    B, s_q, h_q, d_qk = q.shape
+    P, page, h_kv, d2 = kvcache.shape
+    W = tile_scheduler_metadata.shape[0]
+    stream = _stream_handle(device)
+    _check(entry, getattr(_load(), entry)(
+        q.data_ptr(), kvcache.data_ptr(), block_table.data_ptr(), block_table.shape[1], P,
+        cache_seqlens.data_ptr(), B, s_q, h_q, h_kv, d_qk, dv, tile_scheduler_metadata.data_ptr(),
+        num_splits.data_ptr(), W, int(bool(causal)), float(softmax_scale or 0.0), o.data_ptr(), lse.data_ptr(),
+        workspace.data_ptr(), workspace.numel(), stream))
+
+
+class DecodeBuffers:
+    """Output and workspace tensors for one decode shape, reusable across calls."""
+
+    def __init__(self, q: torch.Tensor, kvcache: torch.Tensor, dv: int, W: int):
+        B, s_q, h_q, _ = q.shape
+        h_kv = kvcache.shape[2]
+        self.o = torch.empty((B, s_q, h_q, dv), dtype=torch.bfloat16, device=q.device)
+        self.lse = torch.empty((B, h_q, s_q), dtype=torch.float32, device=q.device)
+        self.workspace = torch.empty(max(workspace_bytes(B, s_q, h_q, h_kv, dv, W), 256), dtype=torch.uint8,
+                                     device=q.device)
+
+
+def _validate(q, kvcache, block_table, cache_seqlens, tile_scheduler_metadata, num_splits):
+    device = q.device
+    if device.type != "cuda":
+        raise ValueError("mla_decode_paged runs on a GPU; q is on " + str(device))
+    _require(q, "q", torch.bfloat16, device)
+    _require(kvcache, "kvcache", torch.bfloat16, device)
+    _require(block_table, "block_table", torch.int32, device)
+    _require(cache_seqlens, "cache_seqlens", torch.int32, device)
+    _require(tile_scheduler_metadata, "tile_scheduler_metadata", torch.int32, device)
+    _require(num_splits, "num_splits", torch.int32, device)
+    if q.dim() != 4 or kvcache.dim() != 4 or block_table.dim() != 2:
+        raise ValueError("q must be [B][s_q][h_q][576], kvcache [P][64][h_kv][576], block_table [B][max_pages]")
+    if kvcache.shape[1] != PAGE_SIZE:
+        raise ValueError("kvcache pages must hold 64 tokens")
+    if block_table.shape[0] != q.shape[0] or cache_seqlens.numel() != q.shape[0]:
+        raise ValueError("block_table / cache_seqlens batch does not match q")
+    if num_splits.numel() != q.shape[0] + 1:
+        raise ValueError("num_splits must have batch + 1 entries")
+
+
+def mla_decode_paged(q: torch.Tensor, kvcache: torch.Tensor, block_table: torch.Tensor,
+                     cache_seqlens: torch.Tensor, dv: int, tile_scheduler_metadata: torch.Tensor,
+                     num_splits: torch.Tensor, causal: bool = False, softmax_scale: Optional[float] = None,
+                     buffers: Optional[DecodeBuffers] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Paged MLA decode.  Returns (o bf16 [B][s_q][h_q][dv], lse fp32 [B][h_q][s_q])."""
+    _validate(q, kvcache, block_table, cache_seqlens, tile_scheduler_metadata, num_splits)
+    if buffers is None:
+        buffers = DecodeBuffers(q, kvcache, dv, tile_scheduler_metadata.shape[0])
+    _decode_call("mla_decode_paged", q, kvcache, block_table, cache_seqlens, dv, tile_scheduler_metadata,
+                 num_splits, causal, softmax_scale, buffers.o, buffers.lse, buffers.workspace)
+    return buffers.o, buffers.lse
+
+
+def mla_decode_splitkv(q, kvcache, block_table, cache_seqlens, dv, tile_scheduler_metadata, num_splits,
+                       causal=False, softmax_scale=None, buffers: Optional[DecodeBuffers] = None):
+    """The decode kernel alone (first launch of mla_decode_paged)."""
+    _validate(q, kvcache, block_table, cache_seqlens, tile_scheduler_metadata, num_splits)
+    if buffers is None:
+        buffers = DecodeBuffers(q, kvcache, dv, tile_scheduler_metadata.shape[0])
+    _decode_call("mla_decode_splitkv", q, kvcache, block_table, cache_seqlens, dv, tile_scheduler_metadata,
+                 num_splits, causal, softmax_scale, buffers.o, buffers.lse, buffers.workspace)
+    return buffers
+
+
+def mla_combine_splits(num_splits: torch.Tensor, s_q: int, h_q: int, h_kv: int, dv: int, W: int,
+                       buffers: DecodeBuffers) -> Tuple[torch.Tensor, torch.Tensor]:
+    """The combine kernel alone (second launch of mla_decode_paged)."""
+    B = num_splits.numel() - 1
+    stream = _stream_handle(num_splits.device)
+    _check("mla_combine_splits", _load().mla_combine_splits(
+        num_splits.data_ptr(), B, s_q, h_q, h_kv, dv, W, buffers.o.data_ptr(), buffers.lse.data_ptr(),
+        buffers.workspace.data_ptr(), buffers.workspace.numel(), stream))
+    return buffers.o, buffers.lse

@@ -1,0 +1,90 @@
+// Log-sum-exp merge of split-KV partials (gfx950).
+//
+// The deepseek.csdn.net FlashMLA article (section 4.2(1)) pairs the split-KV
+// forward kernel with a kernel that merges the per-split results.  Each split
+// s of a query row left O_s (normalised by its own softmax sum) and lse_s;
+// the merge is exact:
+//     lse = M + ln sum_s exp(lse_s - M),  M = max_s lse_s
+//     O   = sum_s exp(lse_s - lse) * O_s
+// Splits whose keys were all masked carry lse_s = -inf and weigh nothing; a
+// row with no visible key at all gets O = 0, lse = -inf.
+//
+// One wave per (sequence, latent head, query row); each lane owns 8 of the 512
+// output columns.  Splits are summed in slot order, so the result does not
+// depend on scheduling.  Sequences with a single split were finished by the
+// decode kernel and are skipped.
+#include "mla_kernels.h"
+
+namespace mla {
+
+namespace {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ inline float wave_reduce_max(float x) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) x = fmaxf(x, __shfl_xor(x, off));
+  return x;
+}
+
+__device__ inline float wave_reduce_sum(float x) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off);
+  return x;
+}
+
+__device__ inline uint32_t pack_bf16x2(float a, float b) {
+  __bf16 x = (__bf16)a, y = (__bf16)b;
+  return (uint32_t)__builtin_bit_cast(uint16_t, x) | ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
+}
+
+}  // namespace
+
+__global__ __launch_bounds__(kCombineRowsPerBlock * 64) void mla_combine_kernel(CombineParams p) {
+  const int lane = threadIdx.x & 63;
+  const int task = blockIdx.x * kCombineRowsPerBlock + (threadIdx.x >> 6);
+  const int per_seq = p.h_kv * p.rows;
+  if (task >= p.batch * per_seq) return;
+  const int b = task / per_seq;
+  const int g = (task - b * per_seq) / p.rows;
+  const int row = task - b * per_seq - g * p.rows;
+  const int s0 = p.num_splits[b];
+  const int n = p.num_splits[b + 1] - s0;
+  if (n == 1) return;
+
+  const int tok = row / p.group;
+  const int head = g * p.group + (row - tok * p.group);
+  uint16_t* op = p.o + ((size_t)(b * p.s_q + tok) * p.h_q + head) * kDv + lane * 8;
+  float* lp = p.lse + ((size_t)b * p.h_q + head) * p.s_q + tok;
+
+  float M = -__builtin_huge_valf();
+  for (int i = lane; i < n; i += 64) M = fmaxf(M, p.ws_lse[(size_t)((s0 + i) * p.h_kv + g) * p.rows + row]);
+  M = wave_reduce_max(M);
+  if (n == 0 || M == -__builtin_huge_valf()) {
+    *(uint4*)op = uint4{0, 0, 0, 0};
+    if (lane == 0) *lp = -__builtin_huge_valf();
+    return;
+  }
+  float z = 0.f;
+  for (int i = lane; i < n; i += 64) z += expf(p.ws_lse[(size_t)((s0 + i) * p.h_kv + g) * p.rows + row] - M);
+  z = wave_reduce_sum(z);
+  const float lse = M + logf(z);
+
+  f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
+  for (int i = 0; i < n; ++i) {
+    const size_t base = (size_t)((s0 + i) * p.h_kv + g) * p.rows + row;
+    const float w = expf(p.ws_lse[base] - lse);
+    const f32x4* src = (const f32x4*)(p.ws_o + base * kDv + lane * 8);
+    a0 += w * src[0];
+    a1 += w * src[1];
+  }
+  uint4 v;
+  v.x = pack_bf16x2(a0[0], a0[1]);
+  v.y = pack_bf16x2(a0[2], a0[3]);
+  v.z = pack_bf16x2(a1[0], a1[1]);
+  v.w = pack_bf16x2(a1[2], a1[3]);
+  *(uint4*)op = v;
+  if (lane == 0) *lp = lse;
+}
+
+}  // namespace mla

@@ -1,0 +1,71 @@
+// Kernel-side definitions shared by the gfx950 kernels and their host launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mla {
+
+constexpr int kPage = 64;                          // tokens per cache page
+constexpr int kDqk = 576;                          // latent row: c^KV (512) + k^R (64)
+constexpr int kDv = 512;                           // value width = c^KV
+constexpr int kRowsPerBlock = 128;                 // query rows one decode workgroup serves
+constexpr int kWaves = 4;                          // 64-lane waves per decode workgroup
+constexpr int kThreads = kWaves * 64;
+constexpr int kRowsPerWave = kRowsPerBlock / kWaves;   // 32 = one MFMA 32x32 tile
+constexpr int kRowBytes = kDqk * 2;                // 1152 bytes of bf16
+constexpr int kChunksPerRow = kRowBytes / 16;      // 72 chunks of 16 bytes
+constexpr int kPageBytes = kPage * kRowBytes;      // 73728 bytes staged in LDS per page
+constexpr int kPageChunks = kPage * kChunksPerRow; // 4608
+constexpr int kLdsDmaPerWave = kPageChunks / 64 / kWaves;  // 18 wave-wide 16-byte DMA loads
+constexpr int kNumXcd = 8;                         // MI355X: 8 XCDs, round-robin block dispatch
+constexpr int kMetaInts = 8;
+constexpr int kMaxWorkers = 4096;
+constexpr int kSchedThreads = 256;
+constexpr int kCombineRowsPerBlock = 4;            // one wave per (sequence, head, query row)
+
+struct DecodeParams {
+  const uint16_t* q;            // bf16 [B][s_q][h_q][576]
+  const uint16_t* kv;           // bf16 [P][64][h_kv][576]
+  const int32_t* block_table;   // [B][max_pages]
+  const int32_t* seqlens;       // [B]
+  const int32_t* meta;          // [W][8]
+  const int32_t* num_splits;    // [B+1]
+  uint16_t* o;                  // bf16 [B][s_q][h_q][512]
+  float* lse;                   // [B][h_q][s_q]
+  float* ws_o;                  // [W+B][h_kv][R][512]
+  float* ws_lse;                // [W+B][h_kv][R]
+  int batch, s_q, h_q, h_kv;
+  int rows;                     // R = s_q * h_q / h_kv
+  int group;                    // G = h_q / h_kv
+  int max_pages;
+  int num_workers;
+  int row_blocks;               // ceil(R / 128)
+  int causal;
+  float scale_log2;             // softmax scale * log2(e)
+};
+
+struct CombineParams {
+  const int32_t* num_splits;
+  const float* ws_o;
+  const float* ws_lse;
+  uint16_t* o;
+  float* lse;
+  int batch, s_q, h_q, h_kv, rows, group;
+};
+
+struct SchedParams {
+  const int32_t* seqlens;
+  int32_t* meta;
+  int32_t* num_splits;
+  int batch;
+  int num_workers;
+  int fixed_overhead;
+};
+
+template <bool kSingleHead>
+__global__ void mla_decode_kernel(DecodeParams p);
+__global__ void mla_combine_kernel(CombineParams p);
+__global__ void mla_sched_kernel(SchedParams p);
+
+}  // namespace mla

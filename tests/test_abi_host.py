@@ -1,0 +1,104 @@
+"""The C-ABI library on the host: it loads, exports every entry point the
+header declares, and rejects invalid calls before touching the device (so
+these run without a GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+import torch  # noqa: F401  (loads the HIP runtime the library binds to)
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mla_decode.h")
+
+
+def _lib():
+    from paged_mla_decode_03_amd import binding
+    if not os.path.exists(binding.LIB_PATH):
+        from paged_mla_decode_03_amd.build import build
+        build()
+    return binding.library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\*?(mla_\w+)\s*\(", text, flags=re.M)
+
+
+def test_header_declares_the_boundary():
+    names = set(declared_functions())
+    assert {"mla_get_metadata", "mla_decode_paged", "mla_num_workers", "mla_workspace_bytes",
+            "mla_status_string", "mla_decode_splitkv", "mla_combine_splits", "mla_sched_fixed_overhead"} <= names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = _lib()
+    for name in declared_functions():
+        assert hasattr(lib, name), f"{name} declared in the header but not exported"
+
+
+def test_single_hip_runtime_in_process():
+    _lib()
+    maps = open("/proc/self/maps").read().splitlines()
+    runtimes = {l.split()[-1] for l in maps if "libamdhip64" in l}
+    assert len(runtimes) == 1, runtimes
+
+
+def test_status_strings():
+    lib = _lib()
+    for code in (0, -1, -2, -3, -4, -5):
+        assert lib.mla_status_string(code)
+    assert b"WORKSPACE" in lib.mla_status_string(-3)
+
+
+def test_workspace_bytes():
+    lib = _lib()
+    got = lib.mla_workspace_bytes(64, 1, 128, 1, 512, 256)
+    assert got == ((256 + 64) * 128 * 513 * 4 + 255) // 256 * 256
+    assert lib.mla_workspace_bytes(0, 1, 128, 1, 512, 256) == 0
+    assert lib.mla_workspace_bytes(2, 1, 128, 3, 512, 256) == 0     # h_q % h_kv != 0
+    assert lib.mla_workspace_bytes(2, 1, 128, 1, 256, 256) == 0     # dv != 512
+
+
+def test_fixed_overhead_matches_reference_rule():
+    from oracle.sched_ref import FIXED_OVERHEAD_PAGES
+    assert _lib().mla_sched_fixed_overhead() == FIXED_OVERHEAD_PAGES
+
+
+FAKE = 0x10000   # 64 KB-aligned, never dereferenced: every call below fails validation first
+
+
+def _decode(lib, **kw):
+    args = dict(q=FAKE, kv=FAKE, bt=FAKE, max_pages=4, num_pages=8, seqlens=FAKE, batch=2, s_q=1, h_q=16,
+                h_kv=1, d_qk=576, dv=512, meta=FAKE, ns=FAKE, W=256, causal=0, scale=0.0, o=FAKE, lse=FAKE,
+                ws=FAKE, ws_bytes=1 << 30, stream=None)
+    args.update(kw)
+    return lib.mla_decode_paged(*args.values())
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), -1), (dict(kv=None), -1), (dict(o=None), -1), (dict(ws=None), -1),
+    (dict(batch=0), -1), (dict(s_q=0), -1), (dict(h_q=16, h_kv=3), -1), (dict(max_pages=0), -1),
+    (dict(causal=2), -1),
+    (dict(d_qk=512), -2), (dict(dv=576), -2), (dict(q=FAKE + 8), -2), (dict(o=FAKE + 4), -2),
+    (dict(ws=FAKE + 16), -2),
+    (dict(ws_bytes=1024), -3),
+    (dict(W=0), -4), (dict(W=5000), -4),
+])
+def test_decode_rejects_invalid_arguments(kw, status):
+    assert _decode(_lib(), **kw) == status
+
+
+def test_metadata_and_combine_reject_invalid_arguments():
+    lib = _lib()
+    assert lib.mla_get_metadata(None, 2, 16, 1, 256, FAKE, FAKE, None) == -1
+    assert lib.mla_get_metadata(FAKE, 0, 16, 1, 256, FAKE, FAKE, None) == -1
+    assert lib.mla_get_metadata(FAKE, 2, 16, 1, 0, FAKE, FAKE, None) == -4
+    assert lib.mla_get_metadata(FAKE + 2, 2, 16, 1, 256, FAKE, FAKE, None) == -2
+    assert lib.mla_combine_splits(None, 2, 1, 16, 1, 512, 256, FAKE, FAKE, FAKE, 1 << 30, None) == -1
+    assert lib.mla_combine_splits(FAKE, 2, 1, 16, 1, 512, 256, FAKE, FAKE, FAKE, 16, None) == -3
+    assert lib.mla_combine_splits(FAKE, 2, 1, 16, 1, 256, 256, FAKE, FAKE, FAKE, 1 << 30, None) == -2
+    n = ctypes.c_int(0)
+    assert lib.mla_num_workers(0, 0, 1, ctypes.byref(n)) == -1
+    assert lib.mla_num_workers(0, 16, 1, None) == -1

@@ -1,0 +1,103 @@
+"""Parity of the HIP path (through the C ABI) with the CPU fp64 oracle.
+
+Small cases are compared element by element in full; the five measured
+workloads are run at their real sizes in the bench's launch configuration
+and compared on sampled sequences the oracle can compute one by one."""
+import numpy as np
+import pytest
+
+from gpu_helpers import compare, oracle, run_gpu
+from workloads import WORKLOADS, Workload, make_inputs
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_tiny(seed):
+    inp = make_inputs("tiny", seed)
+    o, lse, _, _ = run_gpu(inp)
+    O, LSE = oracle(inp)
+    compare(o, lse, O, LSE, label=f"tiny seed {seed}")
+
+
+def _custom(batch, s_q, h_q, h_kv, causal, seqlens, seed=0, **kw):
+    w = Workload("custom", batch=batch, s_q=s_q, h_q=h_q, h_kv=h_kv, causal=causal,
+                 seqlens=tuple(seqlens), num_pages=None)
+    return make_inputs(w, seed, seqlens=seqlens, **kw)
+
+
+SHAPES = [
+    # (s_q, h_q, h_kv, causal, seqlens): several tiles, ragged tails, row blocks
+    (1, 128, 1, False, [1, 63, 64, 65, 200, 1000]),
+    (1, 64, 1, False, [130, 7, 777]),              # half-empty row block
+    (1, 96, 1, False, [300, 2]),
+    (1, 200, 1, False, [129, 64]),                 # two row blocks, ragged second
+    (2, 128, 1, True, [1, 2, 3, 64, 65, 513]),     # causal s_q = 2, 256 rows
+    (3, 16, 1, True, [1, 2, 5, 70]),               # rows that see nothing
+    (1, 128, 2, False, [100, 257]),                # two latent heads
+    (2, 32, 4, True, [66, 9]),
+    (1, 16, 1, False, [0, 37, 0, 130]),            # empty sequences
+]
+
+
+@pytest.mark.parametrize("s_q,h_q,h_kv,causal,seqlens", SHAPES)
+def test_shapes(s_q, h_q, h_kv, causal, seqlens):
+    inp = _custom(len(seqlens), s_q, h_q, h_kv, causal, seqlens, seed=sum(seqlens))
+    o, lse, _, _ = run_gpu(inp)
+    O, LSE = oracle(inp)
+    compare(o, lse, O, LSE, label=f"{s_q}x{h_q}/{h_kv} causal={causal} L={seqlens}")
+
+
+@pytest.mark.parametrize("W", [1, 3, 17, 256, 1000])
+def test_worker_counts(W):
+    """Any number of workers (so any split layout) gives the same answer."""
+    inp = _custom(3, 1, 128, 1, False, [70, 1300, 5], seed=W)
+    o, lse, _, ns = run_gpu(inp, num_workers=W)
+    O, LSE = oracle(inp)
+    compare(o, lse, O, LSE, label=f"W={W} splits={np.diff(ns).tolist()}")
+
+
+def test_softmax_scale_argument():
+    inp = _custom(2, 1, 32, 1, False, [90, 3], seed=5)
+    o, lse, _, _ = run_gpu(inp, softmax_scale=0.02)
+    O, LSE = oracle(inp, softmax_scale=0.02)
+    compare(o, lse, O, LSE, label="scale 0.02")
+
+
+def test_reference_point_restart():
+    """Later pages score far above the first page: the kernel has to move its
+    softmax reference point (restart the segment) and still match."""
+    inp = _custom(2, 1, 64, 1, False, [64 * 6 + 5, 64 * 3], seed=9)
+    kv = inp.kvcache.float()
+    bt = inp.block_table.numpy()
+    for b in range(2):
+        kv[bt[b, 0]] *= 0.05                  # first page: small scores
+        for j in range(1, 4):
+            kv[bt[b, j]] *= 4.0               # later pages: scores ~16x the first
+    inp.kvcache = kv.to(inp.kvcache.dtype)
+    o, lse, _, _ = run_gpu(inp, num_workers=1)
+    O, LSE = oracle(inp)
+    compare(o, lse, O, LSE, scale=4.0, label="restart")
+
+
+# --------------------------------------------------------------------------
+# The five measured workloads at full size, sampled.
+# --------------------------------------------------------------------------
+
+def _sample(inp, k, rng):
+    B = inp.workload.batch
+    L = inp.cache_seqlens.numpy()
+    picks = set(rng.choice(B, size=min(k, B), replace=False).tolist())
+    picks.add(int(np.argmax(L)))
+    picks.add(int(np.argmin(L)))
+    return sorted(picks)
+
+
+@pytest.mark.parametrize("name,k", [("mem_bound", 3), ("var_len", 4), ("causal_sq2", 2), ("skewed", 3)])
+def test_full_size_workloads(name, k):
+    inp = make_inputs(name, 0)
+    o, lse, _, ns = run_gpu(inp)
+    subset = _sample(inp, k, np.random.default_rng(1))
+    O, LSE = oracle(inp, batch_subset=subset)
+    stats = compare(o, lse, O, LSE, batch_subset=subset, label=name)
+    print(name, "splits per sequence:", np.diff(ns).max(), stats)
