@@ -26,8 +26,8 @@ build's own rule ("rule v0"), written as plain loops:
   segment gets (0, 0, -1, 0, 0, 0, 0, 0).  Only a worker's first segment can
   start inside a sequence, so its later segments have ordinal 0.
 
-W = max(1, N_CU // (h_kv * ceil(R / 128))) for R = s_q*h_q/h_kv query rows per
-latent head, with 128 query rows per workgroup.
+W = max(1, N_CU // (h_kv * ceil(R / 64))) for R = s_q*h_q/h_kv query rows per
+latent head, with 64 query rows per workgroup.
 """
 from __future__ import annotations
 
@@ -35,7 +35,7 @@ import numpy as np
 
 PAGE_SIZE = 64
 FIXED_OVERHEAD_PAGES = 2   # F: cost of one sequence's q load and output, in page units
-ROWS_PER_BLOCK = 128
+ROWS_PER_BLOCK = 64
 METADATA_INTS = 8
 
 

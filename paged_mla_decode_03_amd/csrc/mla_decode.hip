@@ -8,25 +8,29 @@
 // block_table, a split-KV forward kernel, then a combine kernel).
 //
 // Work decomposition (MI355X-native):
-//   * One workgroup = 4 waves = 128 query rows of one latent head, over the
-//     page range the scheduler gave its worker.  All 128 rows share each
-//     staged page, so every latent row is read from HBM once per workgroup.
-//   * Wave v owns query rows 32v..32v+31.  Its absorbed Q (32 x 576 bf16) sits
+//   * One workgroup = 4 waves = 64 query rows of one latent head, over the
+//     page range the scheduler gave its worker.  The workgroups that serve
+//     the other row blocks of the same head read the same pages; they are
+//     dispatched back to back on the same XCD so the second read hits L2.
+//   * Wave v owns query rows 16v..16v+15.  Its absorbed Q (16 x 576 bf16) sits
 //     in VGPRs as MFMA B fragments for the whole segment; its output
-//     O^T (512 x 32 fp32) sits in 16 MFMA 32x32 accumulators.
-//   * Per page: S^T = K * Q^T with v_mfma_f32_32x32x16_bf16 (A = K rows from
-//     LDS, B = Q), online softmax in the accumulator layout (each lane holds
-//     one query row), then O^T += V^T * P^T with the same MFMA (A = V columns
-//     from LDS, B = P straight from the S^T accumulators, no shuffle).
-//   * Pages move HBM -> LDS with global_load_lds_dwordx4 (no VGPR staging),
-//     double-buffered: page i+1 is in flight while page i is computed.  16-byte
-//     chunks are XOR-swizzled by row (chunk c of row r lives at slot
-//     c ^ (r & 7)) so that the MFMA fragment reads hit distinct LDS banks.
+//     O^T (512 x 16 fp32) sits in 32 v_mfma_f32_16x16x32_bf16 accumulators
+//     (128 accumulation registers).
+//   * A page is processed as two k-steps of 32 keys.  Per k-step: S^T = K Q^T
+//     for two 16-key tiles (A = K rows from LDS, B = Q), the softmax weights
+//     in the accumulator layout (each lane holds 4 keys of one query row),
+//     then O^T += V^T P^T (A = V columns read with the transposing
+//     ds_read_b64_tr_b16, B = P taken straight from the S^T accumulators).
+//   * Pages move HBM -> LDS with buffer_load_dwordx4 ... lds (no VGPR
+//     staging; the buffer resource bounds every read to the page), double
+//     buffered: page i+1 is in flight while page i is computed.  The page
+//     sits in LDS as 72 tiles of 1 KB (8 rows x 8 chunks of 16 bytes) with the
+//     16-byte chunks XOR-swizzled by row inside a tile.
 //   * Softmax runs in base 2 with the scale folded into one multiply.  Each
 //     row keeps a reference point m (its maximum over the segment's first
-//     page) and accumulates unnormalised weights 2^(s - m) <= 2^16; that is
+//     k-step) and accumulates unnormalised weights 2^(s - m) <= 2^16; that is
 //     exact math, and bf16/fp32 have the range for it.  The output tile is
-//     therefore never rescaled: only MFMAs touch it.  Should a later page
+//     therefore never rescaled: only MFMAs touch it.  Should a later k-step
 //     exceed a row's reference by more than 16, the workgroup restarts the
 //     segment from its first page with the larger reference (each restart
 //     raises a reference by more than 16, so restarts are few and finite;
@@ -41,41 +45,44 @@ namespace mla {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) const bf16x8 lds_bf16x8;
-typedef __attribute__((address_space(3))) const uint16_t lds_u16;
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 constexpr float kRestartThreshold = 16.0f;   // log2 units: weights stay <= 2^16
 constexpr float kNegInf = -__builtin_huge_valf();
+constexpr uint32_t kBufferConfig = 0x00020000;   // buffer resource word 3 (raw, no swizzle)
 
 __device__ inline int pages_of(int seqlen) { return (seqlen + kPage - 1) / kPage; }
 
 // LDS layout of a staged page: 72 tiles of 1 KB, tile (a, b) = rows 8a..8a+7 x
 // 16-byte chunks 8b..8b+7 at byte (9a + b) * 1024; inside a tile, chunk c of
 // row r sits at slot 8 * (r % 8) + ((c % 8) ^ (r % 8)).  The XOR spreads the
-// 8 rows an MFMA fragment read touches over distinct banks, and one wave-wide
+// rows a fragment read touches over distinct banks, and one wave-wide
 // 16-byte DMA fills exactly one tile.
 __device__ inline int lds_tile_offset(int r, int c) {
   return ((r >> 3) * 9 + (c >> 3)) * 1024 + ((r & 7) * 8 + ((c & 7) ^ (r & 7))) * 16;
 }
 
-// Stage one page of latent head g into LDS with 72 wave-wide DMAs (18 per
+// Stage one page of one latent head into LDS with 72 wave-wide DMAs (18 per
 // wave).  Lane u of the DMA for tile (a, b) fetches row 8a + u/8, chunk
-// 8b + ((u%8) ^ (u/8)), so its source address is a wave-uniform base (SGPRs)
-// plus one per-lane offset, and its destination is the tile's wave-uniform
-// LDS address.  All 64 rows are fetched; rows past the sequence end are
-// zeroed afterwards by zero_tail_rows().
-__device__ inline void stage_page(const char* page_head, uint32_t lane_src_off, int row_stride_bytes,
-                                  char* dst, int wave) {
+// 8b + ((u%8) ^ (u/8)): a per-lane byte offset (lane_off) plus a wave-uniform
+// one, relative to a buffer resource that spans exactly this page's 64 rows.
+// All 64 rows are fetched; rows past the sequence end are zeroed afterwards by
+// zero_tail_rows().
+__device__ inline void stage_page(const char* page_head, uint32_t page_bytes, uint32_t lane_off,
+                                  int row_stride_bytes, char* dst, int wave) {
+  const __amdgpu_buffer_rsrc_t rsrc =
+      __builtin_amdgcn_make_buffer_rsrc((void*)page_head, (short)0, (int)page_bytes, (int)kBufferConfig);
 #pragma unroll
   for (int k = 0; k < kLdsDmaPerWave; ++k) {
     const int j = k * kWaves + wave;            // tile index 9a + b, wave-uniform
     const int a = j / 9, b = j - (j / 9) * 9;
-    const char* src = page_head + (a * 8 * row_stride_bytes + b * 128);
-    __builtin_amdgcn_global_load_lds((const void*)(src + lane_src_off), (lds_void*)(dst + j * 1024), 16, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(dst + j * 1024), 16, lane_off,
+                                             a * 8 * row_stride_bytes + b * 128, 0, 0);
   }
 }
 
@@ -89,9 +96,14 @@ __device__ inline void zero_tail_rows(char* page, int valid, int tid) {
   }
 }
 
-__device__ inline float wave_max_pair(float x) {
-  // rows live in lanes l and l^32; combine the two halves
+// The 4 lanes l, l^16, l^32, l^48 hold the same query row.
+__device__ inline float row_max4(float x) {
+  x = fmaxf(x, __shfl_xor(x, 16));
   return fmaxf(x, __shfl_xor(x, 32));
+}
+__device__ inline float row_sum4(float x) {
+  x += __shfl_xor(x, 16);
+  return x + __shfl_xor(x, 32);
 }
 
 __device__ inline uint32_t pack_bf16x2(float a, float b) {
@@ -99,31 +111,24 @@ __device__ inline uint32_t pack_bf16x2(float a, float b) {
   return (uint32_t)__builtin_bit_cast(uint16_t, x) | ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
 }
 
-struct Cursor {
-  int b, page, end;   // current sequence, page index, end page of this segment
-  bool valid;
-};
-
-__device__ inline void cursor_begin(Cursor& c, const int32_t* meta, const int32_t* seqlens) {
-  c.b = meta[0];
-  c.page = meta[1];
-  c.end = meta[2] == meta[0] ? meta[3] : pages_of(seqlens[meta[0]]);
-  c.valid = meta[2] >= meta[0] && c.page < c.end;
+// End page of sequence b's part of this worker's range.
+__device__ inline int segment_end(const int32_t* meta, const int32_t* seqlens, int b) {
+  return b == meta[2] ? meta[3] : pages_of(seqlens[b]);
 }
 
-__device__ inline void cursor_next(Cursor& c, const int32_t* meta, const int32_t* seqlens) {
-  if (++c.page < c.end) return;
-  const int b_last = meta[2];
-  for (int b = c.b + 1; b <= b_last; ++b) {
-    const int end = b == b_last ? meta[3] : pages_of(seqlens[b]);
-    if (end > 0) {
-      c.b = b;
-      c.page = 0;
-      c.end = end;
-      return;
+// Advance (b, page, end) to the worker's next page; returns false past the end.
+__device__ inline bool next_page(const int32_t* meta, const int32_t* seqlens, int& b, int& page, int& end) {
+  if (++page < end) return true;
+  for (int nb = b + 1; nb <= meta[2]; ++nb) {
+    const int e = segment_end(meta, seqlens, nb);
+    if (e > 0) {
+      b = nb;
+      page = 0;
+      end = e;
+      return true;
     }
   }
-  c.valid = false;
+  return false;
 }
 
 }  // namespace
@@ -137,8 +142,8 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(DecodeParams p)
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
-  const int half = lane >> 5;     // which 8-wide k slice of an MFMA fragment this lane holds
-  const int col = lane & 31;      // query row within the wave's tile / MFMA column
+  const int grp4 = lane >> 4;     // which 4-key / 8-wide k slice of an MFMA fragment
+  const int col = lane & 15;      // query row within the wave's tile / MFMA column
 
   // Block -> (worker, latent head, row block).  Blocks are dispatched to the
   // XCDs round-robin; the row blocks of one (worker, head) share its KV
@@ -152,19 +157,18 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(DecodeParams p)
   const int g = grp - worker * p.h_kv;
 
   const int32_t* meta = p.meta + (size_t)worker * kMetaInts;
-  Cursor cur;
-  cursor_begin(cur, meta, p.seqlens);
-  if (!cur.valid) return;
-  Cursor ld = cur;
+  if (meta[2] < meta[0]) return;                       // worker without pages
+  // Compute cursor (cb, cpage, cend) and load cursor (lb, lpage, lend).
+  int cb = meta[0], cpage = meta[1], cend = segment_end(meta, p.seqlens, cb);
+  if (cpage >= cend) return;
+  int lb = cb, lpage = cpage, lend = cend;
+  bool lvalid = true;
 
   const int row_stride_bytes = kSingleHead ? kRowBytes : p.h_kv * kRowBytes;   // bytes between tokens
   const size_t page_stride_bytes = (size_t)kPage * row_stride_bytes;
+  const uint32_t page_span = (uint32_t)(kPage * row_stride_bytes);              // resource size
   const char* kv_head = (const char*)p.kv + (size_t)g * kRowBytes;
   const uint32_t lane_src_off = (lane >> 3) * row_stride_bytes + ((lane & 7) ^ (lane >> 3)) * 16;
-  auto page_ptr = [&](const Cursor& c) {
-    const int page_id = __builtin_amdgcn_readfirstlane(p.block_table[(size_t)c.b * p.max_pages + c.page]);
-    return kv_head + (size_t)page_id * page_stride_bytes;
-  };
 
   // This lane's query row.
   const int qrow = rb * kRowsPerBlock + wave * kRowsPerWave + col;
@@ -173,27 +177,32 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(DecodeParams p)
   const int q_head = g * p.group + (row_ok ? qrow - q_tok * p.group : 0);
 
   // First page in flight before anything else.
-  stage_page(page_ptr(ld), lane_src_off, row_stride_bytes, lds_page[0], wave);
-  cursor_next(ld, meta, p.seqlens);
+  {
+    const int page_id = __builtin_amdgcn_readfirstlane(p.block_table[(size_t)lb * p.max_pages + lpage]);
+    stage_page(kv_head + (size_t)page_id * page_stride_bytes, page_span, lane_src_off, row_stride_bytes,
+               lds_page[0], wave);
+    lvalid = next_page(meta, p.seqlens, lb, lpage, lend);
+  }
 
   int it = 0;
   while (true) {
-    // ---------------- segment: pages [cur.page, cur.end) of sequence cur.b ----------------
-    const int b = cur.b;
+    // ---------------- segment: pages [cpage, cend) of sequence cb ----------------
+    const int b = cb;
     const int L = p.seqlens[b];
     const int s0 = p.num_splits[b];
     const int nsplit = p.num_splits[b + 1] - s0;
     const int slot = s0 + (b == meta[0] ? meta[4] : 0);
     const int n_vis_min = p.causal ? L - p.s_q + 1 : L;
     const int n_vis_row = p.causal ? L - p.s_q + q_tok + 1 : L;
-    const Cursor seg_start = cur;
+    const int seg_page0 = cpage;
 
-    bf16x8 qf[kDqk / 16];
+    // Q fragments: lane (col, grp4) holds row qrow, dims 32*ks + 8*grp4 .. +7.
+    bf16x8 qf[kDqk / 32];
     {
-      const uint16_t* qp = p.q + ((size_t)(b * p.s_q + q_tok) * p.h_q + q_head) * kDqk + half * 8;
+      const uint16_t* qp = p.q + ((size_t)(b * p.s_q + q_tok) * p.h_q + q_head) * kDqk + grp4 * 8;
 #pragma unroll
-      for (int ks = 0; ks < kDqk / 16; ++ks) {
-        u32x4 v = row_ok ? *(const u32x4*)(qp + ks * 16) : u32x4{0, 0, 0, 0};
+      for (int ks = 0; ks < kDqk / 32; ++ks) {
+        u32x4 v = row_ok ? *(const u32x4*)(qp + ks * 32) : u32x4{0, 0, 0, 0};
         qf[ks] = __builtin_bit_cast(bf16x8, v);
       }
     }
@@ -201,195 +210,183 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(DecodeParams p)
     float m_seen = kNegInf;     // largest score seen in the segment
     float l_run = 0.f;          // this lane's share of sum_j 2^(s_j - m_ref)
     int restart = 0;            // this lane's row outgrew its reference
-    f32x16 acc[kDv / 32];
+    f32x4 acc[kDv / 16];
 
     // One attempt per reference point; the output tiles are zeroed here and
     // only MFMAs touch them until the segment epilogue.
     while (true) {
 #pragma unroll
-    for (int nt = 0; nt < kDv / 32; ++nt) acc[nt] = f32x16{};
-    l_run = 0.f;
-    bool done = false;          // the segment's last page has been computed
-    int vote = 0;
+      for (int nt = 0; nt < kDv / 16; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      l_run = 0.f;
+      bool done = false;        // the segment's last page has been computed
+      int vote = 0;
 
-    while (true) {
-      // Page `it` has landed in every wave's share; the buffer of page it-1
-      // is free; and every wave has voted on a restart.
-      __builtin_amdgcn_s_waitcnt(0);
-      vote = __syncthreads_or(restart);
-      if (vote || done) break;
-      char* buf = lds_page[it & 1];
-      const int valid = min(kPage, L - cur.page * kPage);
-      if (valid < kPage) {
-        zero_tail_rows(buf, valid, tid);
-        __syncthreads();
-      }
-      if (ld.valid) {
-        stage_page(page_ptr(ld), lane_src_off, row_stride_bytes, lds_page[(it + 1) & 1], wave);
-        cursor_next(ld, meta, p.seqlens);
-      }
+      while (true) {
+        // Page `it` has landed in every wave's share; the buffer of page it-1
+        // is free; and every wave has voted on a restart.
+        __builtin_amdgcn_s_waitcnt(0);
+        vote = __syncthreads_or(restart);
+        if (vote || done) break;
+        char* buf = lds_page[it & 1];
+        const int valid = min(kPage, L - cpage * kPage);
+        if (valid < kPage) {
+          zero_tail_rows(buf, valid, tid);
+          __syncthreads();
+        }
+        if (lvalid) {
+          const int page_id = __builtin_amdgcn_readfirstlane(p.block_table[(size_t)lb * p.max_pages + lpage]);
+          stage_page(kv_head + (size_t)page_id * page_stride_bytes, page_span, lane_src_off, row_stride_bytes,
+                     lds_page[(it + 1) & 1], wave);
+          lvalid = next_page(meta, p.seqlens, lb, lpage, lend);
+        }
 
-      // The page is processed as two halves of 32 keys (mt = 0, 1), each a
-      // 32-key S^T tile, its weights, and its two 16-key k-steps of the output.
-      const int key0 = cur.page * kPage;
-      const bool need_mask = key0 + kPage > n_vis_min;
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
-        // Per-lane bases of this half page's fragment reads (its rows start
-        // 36 KB into the page); every read is one of them plus a compile-time
-        // offset.  They are recomputed here from the lane id rather than kept
-        // live across the loop, and the empty asm statements stop the compiler
-        // from hoisting them again or turning base + offset into an OR that
-        // the DS immediate offset cannot absorb.
+        // Per-lane LDS bases of this page's fragment reads; every read is one
+        // of them plus a compile-time offset below 64 KB.  They are formed
+        // here from the lane id rather than kept live across the loop, and the
+        // empty asm statements stop the compiler from hoisting them or turning
+        // base + offset into an OR that the DS immediate offset cannot absorb.
         int ln = lane;
         asm volatile("" : "+v"(ln));
-        const int c32 = ln & 31, hf = ln >> 5;
-        const uint32_t hp = (uint32_t)(uintptr_t)(buf + mt * 36 * 1024);
-        uint32_t kb[4], vb[2][4];
-#pragma unroll
-        for (int k4 = 0; k4 < 4; ++k4) {
-          kb[k4] = hp + lds_tile_offset(c32, 2 * k4 + hf);
-          asm volatile("" : "+v"(kb[k4]));
-        }
+        const uint32_t page_base = (uint32_t)(uintptr_t)buf;
+        uint32_t kb[2], vb[4];
 #pragma unroll
         for (int par = 0; par < 2; ++par) {
+          // K row (ln & 15) (+16 per key tile), chunk 4*par + (ln >> 4) (+8 per 2 k-steps)
+          kb[par] = page_base + lds_tile_offset(ln & 15, 4 * par + (ln >> 4));
+          asm volatile("" : "+v"(kb[par]));
+        }
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            vb[par][j] = hp + lds_tile_offset(4 * hf + j, 4 * par + (c32 >> 3)) + (c32 & 7) * 2;
-            asm volatile("" : "+v"(vb[par][j]));
-          }
+        for (int m4 = 0; m4 < 4; ++m4) {
+          // V row (ln >> 2) (+16 per read), columns 16*m4 + 4*(ln & 3) (+64 per 4 tiles)
+          vb[m4] = page_base + lds_tile_offset(ln >> 2, 2 * m4 + ((ln & 3) >> 1)) + 8 * (ln & 1);
+          asm volatile("" : "+v"(vb[m4]));
         }
 
-        // ---- S^T = K * Q^T over 36 k-steps of 16 ----
-        // Lane (col, half) reads key 32*mt + col, chunk 2*ks + half, which sits
-        // at kb[ks % 4] + (ks/4) KB.
-        f32x16 s;
+        const int key0 = cpage * kPage;
+        const bool need_mask = key0 + kPage > n_vis_min;
 #pragma unroll
-        for (int ks = 0; ks < kDqk / 16; ++ks) {
-          const bf16x8 kf = *(const lds_bf16x8*)(kb[ks & 3] + (ks >> 2) * 1024);
-          s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], ks == 0 ? f32x16{} : s, 0, 0, 0);
-          // keep at most a few fragments in flight (bounded register use)
-          if ((ks & 1) == 1) __builtin_amdgcn_sched_barrier(0);
-        }
-
-        // ---- softmax weights (base 2) ----
-        // Lane (col, half) holds, for its query row, keys
-        // key0 + 32*mt + 8*r + 4*half + t in s[4*r + t].
-        float rmax = kNegInf;
+        for (int kk = 0; kk < 2; ++kk) {
+          // ---- S^T = K Q^T for key tiles t = 2kk, 2kk+1 (16 keys each), 18 k-steps of 32 ----
+          // Lane (col, grp4) reads key 16t + col, chunk 4*ks + grp4.
+          f32x4 s[2];
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          float x = s[e] * p.scale_log2;
-          if (need_mask) {
-            const int key = key0 + mt * 32 + (e >> 2) * 8 + half * 4 + (e & 3);
-            x = key < n_vis_row ? x : kNegInf;
-          }
-          s[e] = x;
-          rmax = fmaxf(rmax, x);
-        }
-        rmax = wave_max_pair(rmax);
-        m_seen = fmaxf(m_seen, rmax);
-        if (m_ref == kNegInf) {
-          m_ref = rmax;           // nothing accumulated yet: adopt this maximum
-        } else if (rmax > m_ref + kRestartThreshold) {
-          restart = 1;            // this page is still computed, then thrown away
-        }
-        const float m_use = m_ref == kNegInf ? 0.f : m_ref;
-        float psum = 0.f;
-        bf16x8 pf[2];
+          for (int tt = 0; tt < 2; ++tt) {
+            const int t = 2 * kk + tt;
+            s[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int q2 = 0; q2 < 2; ++q2) {
-          uint32_t w[4];
-#pragma unroll
-          for (int e = 0; e < 8; e += 2) {
-            const float a = __builtin_amdgcn_exp2f(s[q2 * 8 + e] - m_use);
-            const float c = __builtin_amdgcn_exp2f(s[q2 * 8 + e + 1] - m_use);
-            psum += a + c;
-            w[e >> 1] = pack_bf16x2(a, c);
-          }
-          pf[q2] = __builtin_bit_cast(bf16x8, u32x4{w[0], w[1], w[2], w[3]});
-        }
-        l_run += psum;
-
-        // ---- O^T += V^T * P^T : 16 column tiles x 2 k-steps of 16 keys ----
-        // k-step kk = 2*mt + q2 covers keys 32*mt + 16*q2 + {4*half + j, 8 + 4*half + j},
-        // j = 0..3 (the order in which the S^T accumulator holds them).  Column
-        // n = 32*nt + col of such a key sits at vb[nt % 2][j] plus a constant.
-#pragma unroll
-        for (int nt = 0; nt < kDv / 32; ++nt) {
-#pragma unroll
-          for (int q2 = 0; q2 < 2; ++q2) {
-            const int krow8 = q2 * 2;   // (first key of the k-step within the half page) / 8
-            uint32_t w[4];
-#pragma unroll
-            for (int e = 0; e < 8; e += 2) {
-              const int j = e & 3;
-              const uint32_t off = ((krow8 + (e >> 2)) * 9 + (nt >> 1)) * 1024;
-              const uint16_t lo = *(const lds_u16*)(vb[nt & 1][j] + off);
-              const uint16_t hi = *(const lds_u16*)(vb[nt & 1][j + 1] + off);
-              w[e >> 1] = (uint32_t)lo | ((uint32_t)hi << 16);
+            for (int ks = 0; ks < kDqk / 32; ++ks) {
+              const bf16x8 kf = *(lds_bf16x8*)(kb[ks & 1] + (uint32_t)((2 * t * 9 + (ks >> 1)) * 1024));
+              s[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[ks], s[tt], 0, 0, 0);
             }
-            const bf16x8 vf = __builtin_bit_cast(bf16x8, u32x4{w[0], w[1], w[2], w[3]});
-            acc[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[q2], acc[nt], 0, 0, 0);
-            __builtin_amdgcn_sched_barrier(0);
+          }
+
+          // ---- softmax weights (base 2) ----
+          // Lane (col, grp4) holds, for its query row, key key0 + 32kk + 16tt + 4*grp4 + i in s[tt][i].
+          float rmax = kNegInf;
+#pragma unroll
+          for (int tt = 0; tt < 2; ++tt) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              float x = s[tt][i] * p.scale_log2;
+              if (need_mask) {
+                const int key = key0 + 32 * kk + 16 * tt + 4 * grp4 + i;
+                x = key < n_vis_row ? x : kNegInf;
+              }
+              s[tt][i] = x;
+              rmax = fmaxf(rmax, x);
+            }
+          }
+          rmax = row_max4(rmax);
+          m_seen = fmaxf(m_seen, rmax);
+          if (m_ref == kNegInf) {
+            m_ref = rmax;           // nothing accumulated yet: adopt this maximum
+          } else if (rmax > m_ref + kRestartThreshold) {
+            restart = 1;            // this page is still computed, then thrown away
+          }
+          const float m_use = m_ref == kNegInf ? 0.f : m_ref;
+          float w[8];
+#pragma unroll
+          for (int tt = 0; tt < 2; ++tt) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              w[4 * tt + i] = __builtin_amdgcn_exp2f(s[tt][i] - m_use);
+              l_run += w[4 * tt + i];
+            }
+          }
+          // B operand of the output MFMA: slot e holds key 16*(e/4) + 4*grp4 + e%4 of this k-step.
+          const bf16x8 pf = __builtin_bit_cast(
+              bf16x8, u32x4{pack_bf16x2(w[0], w[1]), pack_bf16x2(w[2], w[3]), pack_bf16x2(w[4], w[5]),
+                            pack_bf16x2(w[6], w[7])});
+
+          // ---- O^T += V^T P^T : 32 column tiles of 16 ----
+          // The A operand needs, in lane (n = col, grp4), V[key][n] for the same
+          // keys: two transposing reads of 4 rows x 16 columns (rows 4*grp4 + m
+          // and 16 + 4*grp4 + m).  Lane l of such a read fetches row l/4,
+          // columns 4*(l%4)..+3 of the 16-column tile.
+#pragma unroll
+          for (int nt = 0; nt < kDv / 16; ++nt) {
+            const uint32_t o0 = (uint32_t)(((4 * kk + 0) * 9 + (nt >> 2)) * 1024);
+            const uint32_t o1 = (uint32_t)(((4 * kk + 2) * 9 + (nt >> 2)) * 1024);
+            const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vb[nt & 3] + o0));
+            const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vb[nt & 3] + o1));
+            const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
+            acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf, acc[nt], 0, 0, 0);
           }
         }
-      }
 
-      ++it;
-      if (cur.page + 1 == cur.end)
-        done = true;            // leave after the next restart vote
-      else
-        ++cur.page;
-    }
-    if (!vote) break;
-    // Restart: recompute the segment from its first page with the larger
-    // references.  Every wave has passed the vote, so both buffers are free.
-    restart = 0;
-    m_ref = m_seen;
-    cur = seg_start;
-    ld = seg_start;
-    stage_page(page_ptr(ld), lane_src_off, row_stride_bytes, lds_page[it & 1], wave);
-    cursor_next(ld, meta, p.seqlens);
+        ++it;
+        if (cpage + 1 == cend)
+          done = true;            // leave after the next restart vote
+        else
+          ++cpage;
+      }
+      if (!vote) break;
+      // Restart: recompute the segment from its first page with the larger
+      // references.  Every wave has passed the vote, so both buffers are free.
+      restart = 0;
+      m_ref = m_seen;
+      cpage = seg_page0;
+      lb = b;
+      lpage = seg_page0;
+      lend = cend;
+      const int page_id = __builtin_amdgcn_readfirstlane(p.block_table[(size_t)lb * p.max_pages + lpage]);
+      stage_page(kv_head + (size_t)page_id * page_stride_bytes, page_span, lane_src_off, row_stride_bytes,
+                 lds_page[it & 1], wave);
+      lvalid = next_page(meta, p.seqlens, lb, lpage, lend);
     }
 
     // ---------------- segment epilogue ----------------
-    const float l_tot = l_run + __shfl_xor(l_run, 32);
+    const float l_tot = row_sum4(l_run);
     const bool empty = l_tot == 0.f;
     const float inv = empty ? 0.f : 1.f / l_tot;
     const float lse_nat = empty ? kNegInf : (m_ref + __log2f(l_tot)) * 0.69314718055994531f;
+    // Lane (col, grp4) holds O[qrow][16*nt + 4*grp4 + i] in acc[nt][i].
     if (row_ok) {
       if (nsplit == 1) {
-        uint16_t* op = p.o + ((size_t)(b * p.s_q + q_tok) * p.h_q + q_head) * kDv;
+        uint16_t* op = p.o + ((size_t)(b * p.s_q + q_tok) * p.h_q + q_head) * kDv + 4 * grp4;
 #pragma unroll
-        for (int nt = 0; nt < kDv / 32; ++nt) {
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int n = nt * 32 + r * 8 + half * 4;
-            uint2 v;
-            v.x = pack_bf16x2(acc[nt][4 * r] * inv, acc[nt][4 * r + 1] * inv);
-            v.y = pack_bf16x2(acc[nt][4 * r + 2] * inv, acc[nt][4 * r + 3] * inv);
-            *(uint2*)(op + n) = v;
-          }
+        for (int nt = 0; nt < kDv / 16; ++nt) {
+          uint2 v;
+          v.x = pack_bf16x2(acc[nt][0] * inv, acc[nt][1] * inv);
+          v.y = pack_bf16x2(acc[nt][2] * inv, acc[nt][3] * inv);
+          *(uint2*)(op + 16 * nt) = v;
         }
-        if (half == 0) p.lse[((size_t)b * p.h_q + q_head) * p.s_q + q_tok] = lse_nat;
+        if (grp4 == 0) p.lse[((size_t)b * p.h_q + q_head) * p.s_q + q_tok] = lse_nat;
       } else {
-        float* wp = p.ws_o + ((size_t)(slot * p.h_kv + g) * p.rows + qrow) * kDv;
+        float* wp = p.ws_o + ((size_t)(slot * p.h_kv + g) * p.rows + qrow) * kDv + 4 * grp4;
 #pragma unroll
-        for (int nt = 0; nt < kDv / 32; ++nt) {
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int n = nt * 32 + r * 8 + half * 4;
-            f32x4 v = {acc[nt][4 * r] * inv, acc[nt][4 * r + 1] * inv, acc[nt][4 * r + 2] * inv,
-                       acc[nt][4 * r + 3] * inv};
-            *(f32x4*)(wp + n) = v;
-          }
-        }
-        if (half == 0) p.ws_lse[(size_t)(slot * p.h_kv + g) * p.rows + qrow] = lse_nat;
+        for (int nt = 0; nt < kDv / 16; ++nt) *(f32x4*)(wp + 16 * nt) = acc[nt] * inv;
+        if (grp4 == 0) p.ws_lse[(size_t)(slot * p.h_kv + g) * p.rows + qrow] = lse_nat;
       }
     }
 
-    cursor_next(cur, meta, p.seqlens);
-    if (!cur.valid) break;
+    // Next segment: the sequence after this one in the worker's range.
+    if (cb == meta[2]) break;
+    int nb = cb, np = cpage, ne = cend;
+    if (!next_page(meta, p.seqlens, nb, np, ne)) break;
+    cb = nb;
+    cpage = np;
+    cend = ne;
   }
 }
 

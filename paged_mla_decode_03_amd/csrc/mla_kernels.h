@@ -9,10 +9,10 @@ namespace mla {
 constexpr int kPage = 64;                          // tokens per cache page
 constexpr int kDqk = 576;                          // latent row: c^KV (512) + k^R (64)
 constexpr int kDv = 512;                           // value width = c^KV
-constexpr int kRowsPerBlock = 128;                 // query rows one decode workgroup serves
+constexpr int kRowsPerBlock = 64;                  // query rows one decode workgroup serves
 constexpr int kWaves = 4;                          // 64-lane waves per decode workgroup
 constexpr int kThreads = kWaves * 64;
-constexpr int kRowsPerWave = kRowsPerBlock / kWaves;   // 32 = one MFMA 32x32 tile
+constexpr int kRowsPerWave = kRowsPerBlock / kWaves;   // 16 = one MFMA 16x16 tile
 constexpr int kRowBytes = kDqk * 2;                // 1152 bytes of bf16
 constexpr int kChunksPerRow = kRowBytes / 16;      // 72 chunks of 16 bytes
 constexpr int kPageBytes = kPage * kRowBytes;      // 73728 bytes staged in LDS per page

@@ -90,9 +90,9 @@ def test_uniform_workload_is_balanced():
 
 
 def test_num_workers():
-    assert num_workers_ref(256, 128, 1) == 256
-    assert num_workers_ref(256, 256, 1) == 128
+    assert num_workers_ref(256, 128, 1) == 128
+    assert num_workers_ref(256, 256, 1) == 64
     assert num_workers_ref(256, 16, 1) == 256
-    assert num_workers_ref(256, 128, 2) == 128
-    assert num_workers_ref(80, 129, 1) == 40
+    assert num_workers_ref(256, 64, 2) == 128
+    assert num_workers_ref(80, 129, 1) == 26
     assert num_workers_ref(1, 1024, 8) == 1
