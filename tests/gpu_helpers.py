@@ -50,15 +50,16 @@ def compare(o, lse, O, LSE, batch_subset=None, scale=1.0, ulp_aware=False, label
     """Assert the GPU result (o, lse) matches the oracle (O, LSE) on the
     sequences in batch_subset (all when None).  `scale` widens the O bars for
     inputs whose values are larger than N(0, 1).  With `ulp_aware`, an output
-    element may also differ by up to one bf16 ulp of its exact value: for
-    |O| >= 4 (rows that average one to three cached values) the final bf16
-    rounding alone exceeds 1e-2."""
+    element may also differ by one bf16 ulp of its exact value plus 2e-3 (the
+    kernel's error before the final rounding, which may round to the far
+    neighbour): where |O| approaches 4 (rows that average one to three cached
+    values) the final bf16 rounding alone exceeds 1e-2."""
     idx = slice(None) if batch_subset is None else np.asarray(batch_subset)
     o, O, lse, LSE = o[idx], O[idx], lse[idx], LSE[idx]
     assert np.isfinite(o).all(), f"{label}: non-finite output"
     d = np.abs(o - O)
     if ulp_aware:
-        d = np.where(d <= bf16_ulp(O), 0.0, d)
+        d = np.where(d <= bf16_ulp(O) + 2e-3, 0.0, d)
     neg = np.isneginf(LSE)
     assert (np.isneginf(lse) == neg).all(), f"{label}: -inf LSE pattern differs"
     dl = np.abs(lse[~neg] - LSE[~neg]) if (~neg).any() else np.zeros(1)
