@@ -1,8 +1,9 @@
 """Benchmark of one paged MLA decode step on one MI355X.
 
-A step is the whole hot path over one batch: the split-KV decode kernel and
-the log-sum-exp combine (the scheduler metadata is computed once per batch of
-sequence lengths and timed separately).  Inputs are seeded synthetic bf16
+A step is the whole hot path over one batch: the split-KV decode kernel, the
+redo launch (which recomputes overflowed splits and for these inputs only
+scans their flags) and the log-sum-exp combine (the scheduler metadata is
+computed once per batch of sequence lengths and timed separately).  Inputs are seeded synthetic bf16
 tensors resident in HBM before timing starts.  Successive steps alternate
 between independent KV pools whose total exceeds the 256 MB Infinity Cache,
 so every step streams its cache from HBM.
@@ -103,7 +104,7 @@ def main():
 
     sys.path.insert(0, ROOT)
     from paged_mla_decode_03_amd import (DecodeBuffers, get_mla_metadata, mla_combine_splits,
-                                         mla_decode_splitkv)
+                                         mla_decode_redo, mla_decode_splitkv)
     from workloads import WORKLOADS, algorithmic_counts, make_inputs
 
     dev = torch.device("cuda", 0)
@@ -136,6 +137,8 @@ def main():
     W = meta.shape[0]
     buf = DecodeBuffers(q, pools[0], 512, W)
 
+    # The three launches of one step, each bracketed by events on the stream
+    # they run on (torch's current stream, which the binding launches on).
     def step(i, evs=None):
         kv = pools[i % n_pools]
         if evs:
@@ -143,28 +146,33 @@ def main():
         mla_decode_splitkv(q, kv, bt, seqlens, 512, meta, ns, causal=w.causal, buffers=buf)
         if evs:
             evs[1].record()
-        mla_combine_splits(ns, w.s_q, w.h_q, w.h_kv, 512, W, buf)
+        mla_decode_redo(q, kv, bt, seqlens, 512, meta, ns, causal=w.causal, buffers=buf)
         if evs:
             evs[2].record()
+        mla_combine_splits(ns, w.s_q, w.h_q, w.h_kv, 512, W, buf)
+        if evs:
+            evs[3].record()
 
     print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
 
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     for i in range(args.steps):
         step(i, evs[i])
     torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - t_start) * 1e3
-    decode_ms = np.array([a.elapsed_time(b) for a, b, _ in evs])
-    combine_ms = np.array([b.elapsed_time(c) for _, b, c in evs])
-    step_ms = np.array([a.elapsed_time(c) for a, _, c in evs])
+    decode_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
+    redo_ms = np.array([e[1].elapsed_time(e[2]) for e in evs])
+    combine_ms = np.array([e[2].elapsed_time(e[3]) for e in evs])
+    step_ms = np.array([e[0].elapsed_time(e[3]) for e in evs])
     ms_per_step = wall_ms / args.steps
     print(f"[bench] {args.steps} steps: {ms_per_step * 1e3:.1f} us/step (wall), decode kernel "
-          f"{decode_ms.mean() * 1e3:.1f} us, combine {combine_ms.mean() * 1e3:.1f} us", file=sys.stderr, flush=True)
+          f"{decode_ms.mean() * 1e3:.1f} us, redo scan {redo_ms.mean() * 1e3:.1f} us, combine "
+          f"{combine_ms.mean() * 1e3:.1f} us", file=sys.stderr, flush=True)
 
     gbs = counts["total_bytes"] / (ms_per_step * 1e-3) / 1e9
     tflops = counts["flops"] / (ms_per_step * 1e-3) / 1e12
@@ -197,6 +205,7 @@ def main():
         "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
         "mfma_frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
         "decode_kernel_us": round(decode_ms.mean() * 1e3, 2),
+        "redo_kernel_us": round(redo_ms.mean() * 1e3, 2),
         "combine_kernel_us": round(combine_ms.mean() * 1e3, 2),
         "step_event_us_p10_p50_p90": [round(float(np.percentile(step_ms, p)) * 1e3, 2) for p in (10, 50, 90)],
         "metadata_us": round(metadata_us, 2),

@@ -61,7 +61,7 @@ def _load():
     lib.mla_workspace_bytes.argtypes = [c_int, c_int, c_int, c_int, c_int, c_int]
     decode_args = [vp, vp, vp, c_int, c_int, vp, c_int, c_int, c_int, c_int, c_int, c_int,
                    vp, vp, c_int, c_int, c_float, vp, vp, vp, c_size_t, vp]
-    for name in ("mla_decode_paged", "mla_decode_splitkv"):
+    for name in ("mla_decode_paged", "mla_decode_splitkv", "mla_decode_redo"):
         f = getattr(lib, name)
         f.restype = c_int
         f.argtypes = decode_args
@@ -196,9 +196,21 @@ def mla_decode_splitkv(q, kvcache, block_table, cache_seqlens, dv, tile_schedule
     return buffers
 
 
+def mla_decode_redo(q, kvcache, block_table, cache_seqlens, dv, tile_scheduler_metadata, num_splits,
+                    causal=False, softmax_scale=None, buffers: Optional[DecodeBuffers] = None):
+    """The redo launch alone (second launch of mla_decode_paged): recomputes the
+    splits mla_decode_splitkv flagged as overflowed; same arguments and buffers."""
+    _validate(q, kvcache, block_table, cache_seqlens, tile_scheduler_metadata, num_splits)
+    if buffers is None:
+        raise ValueError("mla_decode_redo needs the buffers mla_decode_splitkv wrote")
+    _decode_call("mla_decode_redo", q, kvcache, block_table, cache_seqlens, dv, tile_scheduler_metadata,
+                 num_splits, causal, softmax_scale, buffers.o, buffers.lse, buffers.workspace)
+    return buffers
+
+
 def mla_combine_splits(num_splits: torch.Tensor, s_q: int, h_q: int, h_kv: int, dv: int, W: int,
                        buffers: DecodeBuffers) -> Tuple[torch.Tensor, torch.Tensor]:
-    """The combine kernel alone (second launch of mla_decode_paged)."""
+    """The combine kernel alone (last launch of mla_decode_paged)."""
     B = num_splits.numel() - 1
     stream = _stream_handle(num_splits.device)
     _check("mla_combine_splits", _load().mla_combine_splits(

@@ -23,11 +23,8 @@ SOURCES = ["mla_api.hip", "mla_sched.hip", "mla_decode.hip", "mla_combine.hip"]
 ARCH = "gfx950"
 
 # Packed fp32 VALU forms are kept out of the generated code; -O3 would
-# otherwise form them from ordinary float code.  MFMAs start in VGPR form so
-# that score tiles and output tiles can be split between the VGPR and AGPR
-# files (the output tiles alone fill the 256 AGPRs).
-DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-                "-mllvm", "-amdgpu-mfma-vgpr-form=1"]
+# otherwise form them from ordinary float code.
+DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 
 
 def hipcc() -> str:

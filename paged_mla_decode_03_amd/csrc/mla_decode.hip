@@ -28,13 +28,16 @@
 //     16-byte chunks XOR-swizzled by row inside a tile.
 //   * Softmax runs in base 2 with the scale folded into one multiply.  Each
 //     row keeps a reference point m (its maximum over the segment's first
-//     k-step) and accumulates unnormalised weights 2^(s - m) <= 2^16; that is
-//     exact math, and bf16/fp32 have the range for it.  The output tile is
-//     therefore never rescaled: only MFMAs touch it.  Should a later k-step
-//     exceed a row's reference by more than 16, the workgroup restarts the
-//     segment from its first page with the larger reference (each restart
-//     raises a reference by more than 16, so restarts are few and finite;
-//     for ordinary attention scores they never happen).
+//     k-step) and accumulates unnormalised weights 2^(s - m) <= 2^48; that is
+//     exact math, and bf16/fp32 have the range for it (sums stay below 2^65
+//     times the largest cached value for 2^17 keys).  The output tile is
+//     therefore never rescaled: only MFMAs touch it, which keeps it in the
+//     accumulation registers with no copies.  Should a later k-step exceed a
+//     row's reference by more than 48, the segment is void: the workgroup
+//     records it, with every row's maximum over the segment, and a second
+//     launch of one workgroup recomputes it with those maxima as references,
+//     where no weight exceeds 1.  For attention scores of any ordinary spread
+//     nothing is recorded and the second launch only scans the flags.
 //   * Keys a query may not see (tail slots of the last page, causal future)
 //     get weight 0, and tail rows of the last page are zeroed in LDS so that
 //     whatever the cache holds there never reaches O.
@@ -52,11 +55,22 @@ typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) const bf16x8 lds_bf16x8;
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
-constexpr float kRestartThreshold = 16.0f;   // log2 units: weights stay <= 2^16
+constexpr float kOverflowThreshold = 48.0f;   // log2 units: weights stay <= 2^48
 constexpr float kNegInf = -__builtin_huge_valf();
 constexpr uint32_t kBufferConfig = 0x00020000;   // buffer resource word 3 (raw, no swizzle)
+// s_waitcnt immediate for vmcnt(0) alone (expcnt and lgkmcnt at their maxima).
+// Issued through the builtin, the compiler knows every vector memory
+// operation -- its own and the page DMAs -- is complete after it.
+constexpr int kWaitVmcnt0 = 0x0F70;
 
 __device__ inline int pages_of(int seqlen) { return (seqlen + kPage - 1) / kPage; }
+
+// Read-only table entry at a wave-uniform address, through the constant
+// address space: a scalar load, counted by lgkmcnt.  Keeping the kernel's own
+// table reads off vmcnt means waiting for them never waits for page DMAs.
+__device__ inline int32_t ld_uniform(const int32_t* ptr) {
+  return *(const __attribute__((address_space(4))) int32_t*)ptr;
+}
 
 // LDS layout of a staged page: 72 tiles of 1 KB, tile (a, b) = rows 8a..8a+7 x
 // 16-byte chunks 8b..8b+7 at byte (9a + b) * 1024; inside a tile, chunk c of
@@ -73,16 +87,28 @@ __device__ inline int lds_tile_offset(int r, int c) {
 // one, relative to a buffer resource that spans exactly this page's 64 rows.
 // All 64 rows are fetched; rows past the sequence end are zeroed afterwards by
 // zero_tail_rows().
+//
+// The DMAs are issued from inline assembly (buffer_load_dwordx4 ... lds, with
+// M0 holding the tile's LDS address), as composable_kernel does for gfx950:
+// the compiler then does not know they write LDS and does not make the reads
+// of the other buffer wait for them.  The kernel waits for them itself
+// (s_waitcnt vmcnt(0) at the top of each page step) before any wave reads
+// the buffer, and issues no vector load of its own between a DMA and that
+// wait.  They write no registers.
 __device__ inline void stage_page(const char* page_head, uint32_t page_bytes, uint32_t lane_off,
-                                  int row_stride_bytes, char* dst, int wave) {
+                                  int row_stride_bytes, uint32_t lds_dst, int wave) {
   const __amdgpu_buffer_rsrc_t rsrc =
       __builtin_amdgcn_make_buffer_rsrc((void*)page_head, (short)0, (int)page_bytes, (int)kBufferConfig);
 #pragma unroll
   for (int k = 0; k < kLdsDmaPerWave; ++k) {
     const int j = k * kWaves + wave;            // tile index 9a + b, wave-uniform
     const int a = j / 9, b = j - (j / 9) * 9;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(dst + j * 1024), 16, lane_off,
-                                             a * 8 * row_stride_bytes + b * 128, 0, 0);
+    const uint32_t m0 = lds_dst + j * 1024;
+    const uint32_t soff = a * 8 * row_stride_bytes + b * 128;
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                 :
+                 : "s"(m0), "v"(lane_off), "s"(rsrc), "s"(soff)
+                 : "memory", "m0");
   }
 }
 
@@ -96,15 +122,25 @@ __device__ inline void zero_tail_rows(char* page, int valid, int tid) {
   }
 }
 
-// The 4 lanes l, l^16, l^32, l^48 hold the same query row.
-__device__ inline float row_max4(float x) {
-  x = fmaxf(x, __shfl_xor(x, 16));
-  return fmaxf(x, __shfl_xor(x, 32));
+// The 4 lanes l, l^16, l^32, l^48 hold the same query row.  With both
+// operands equal to x, v_permlane16_swap leaves {x[l], x[l^16]} in lane l's
+// pair of results and v_permlane32_swap {x[l], x[l^32]}; a symmetric
+// reduction of the pair is the xor-shuffle step, without an LDS round trip
+// (which would also wait for the fragment reads in flight).
+__device__ inline float xor16_pair(float x, bool max_op) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(uint32_t, x), __builtin_bit_cast(uint32_t, x),
+                                                  false, false);
+  const float a = __builtin_bit_cast(float, (uint32_t)r[0]), b = __builtin_bit_cast(float, (uint32_t)r[1]);
+  return max_op ? fmaxf(a, b) : a + b;
 }
-__device__ inline float row_sum4(float x) {
-  x += __shfl_xor(x, 16);
-  return x + __shfl_xor(x, 32);
+__device__ inline float xor32_pair(float x, bool max_op) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x), __builtin_bit_cast(uint32_t, x),
+                                                  false, false);
+  const float a = __builtin_bit_cast(float, (uint32_t)r[0]), b = __builtin_bit_cast(float, (uint32_t)r[1]);
+  return max_op ? fmaxf(a, b) : a + b;
 }
+__device__ inline float row_max4(float x) { return xor32_pair(xor16_pair(x, true), true); }
+__device__ inline float row_sum4(float x) { return xor32_pair(xor16_pair(x, false), false); }
 
 __device__ inline uint32_t pack_bf16x2(float a, float b) {
   __bf16 x = (__bf16)a, y = (__bf16)b;
@@ -113,13 +149,13 @@ __device__ inline uint32_t pack_bf16x2(float a, float b) {
 
 // End page of sequence b's part of this worker's range.
 __device__ inline int segment_end(const int32_t* meta, const int32_t* seqlens, int b) {
-  return b == meta[2] ? meta[3] : pages_of(seqlens[b]);
+  return b == ld_uniform(meta + 2) ? ld_uniform(meta + 3) : pages_of(ld_uniform(seqlens + b));
 }
 
 // Advance (b, page, end) to the worker's next page; returns false past the end.
 __device__ inline bool next_page(const int32_t* meta, const int32_t* seqlens, int& b, int& page, int& end) {
   if (++page < end) return true;
-  for (int nb = b + 1; nb <= meta[2]; ++nb) {
+  for (int nb = b + 1; nb <= ld_uniform(meta + 2); ++nb) {
     const int e = segment_end(meta, seqlens, nb);
     if (e > 0) {
       b = nb;
@@ -133,33 +169,28 @@ __device__ inline bool next_page(const int32_t* meta, const int32_t* seqlens, in
 
 }  // namespace
 
+// One worker's pages for latent head g and row block rb: every segment in the
+// worker's range [meta[0], meta[1]) .. [meta[2], meta[3]).
+//
 // kSingleHead: h_kv == 1, so a page's rows are contiguous 1152-byte rows and
 // every stride is a compile-time constant.
-template <bool kSingleHead>
-__global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(DecodeParams p) {
-  __shared__ __attribute__((aligned(1024))) char lds_page[2][kPageBytes];
-
+// kRedo: the worker is one segment that overflowed in the first launch
+// (meta is its redo record); each row starts from the reference point
+// recorded for it, which is its maximum score over the segment.
+template <bool kSingleHead, bool kRedo>
+__device__ __forceinline__ void decode_worker(const DecodeParams& p, char (*lds_page)[kPageBytes],
+                                              const int32_t* meta, int g, int rb, int redo_item) {
+  const uint32_t lds_base = (uint32_t)(uintptr_t)&lds_page[0][0];   // LDS byte address
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
   const int grp4 = lane >> 4;     // which 4-key / 8-wide k slice of an MFMA fragment
   const int col = lane & 15;      // query row within the wave's tile / MFMA column
 
-  // Block -> (worker, latent head, row block).  Blocks are dispatched to the
-  // XCDs round-robin; the row blocks of one (worker, head) share its KV
-  // stream, so they are given ids on the same XCD, issued back to back.
-  const int xcd = blockIdx.x % kNumXcd;
-  const int k = blockIdx.x / kNumXcd;
-  const int rb = k % p.row_blocks;
-  const int grp = (k / p.row_blocks) * kNumXcd + xcd;
-  if (grp >= p.num_workers * p.h_kv) return;
-  const int worker = grp / p.h_kv;
-  const int g = grp - worker * p.h_kv;
-
-  const int32_t* meta = p.meta + (size_t)worker * kMetaInts;
-  if (meta[2] < meta[0]) return;                       // worker without pages
+  const int meta_b0 = ld_uniform(meta + 0), meta_b1 = ld_uniform(meta + 2);
+  if (meta_b1 < meta_b0) return;                       // worker without pages
   // Compute cursor (cb, cpage, cend) and load cursor (lb, lpage, lend).
-  int cb = meta[0], cpage = meta[1], cend = segment_end(meta, p.seqlens, cb);
+  int cb = meta_b0, cpage = ld_uniform(meta + 1), cend = segment_end(meta, p.seqlens, cb);
   if (cpage >= cend) return;
   int lb = cb, lpage = cpage, lend = cend;
   bool lvalid = true;
@@ -178,20 +209,20 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(DecodeParams p)
 
   // First page in flight before anything else.
   {
-    const int page_id = __builtin_amdgcn_readfirstlane(p.block_table[(size_t)lb * p.max_pages + lpage]);
-    stage_page(kv_head + (size_t)page_id * page_stride_bytes, page_span, lane_src_off, row_stride_bytes,
-               lds_page[0], wave);
+    const int page_id = ld_uniform(p.block_table + (size_t)lb * p.max_pages + lpage);
     lvalid = next_page(meta, p.seqlens, lb, lpage, lend);
+    stage_page(kv_head + (size_t)page_id * page_stride_bytes, page_span, lane_src_off, row_stride_bytes,
+               lds_base, wave);
   }
 
   int it = 0;
   while (true) {
     // ---------------- segment: pages [cpage, cend) of sequence cb ----------------
     const int b = cb;
-    const int L = p.seqlens[b];
-    const int s0 = p.num_splits[b];
-    const int nsplit = p.num_splits[b + 1] - s0;
-    const int slot = s0 + (b == meta[0] ? meta[4] : 0);
+    const int L = ld_uniform(p.seqlens + b);
+    const int s0 = ld_uniform(p.num_splits + b);
+    const int nsplit = ld_uniform(p.num_splits + b + 1) - s0;
+    const int slot = s0 + (b == meta_b0 ? ld_uniform(meta + 4) : 0);
     const int n_vis_min = p.causal ? L - p.s_q + 1 : L;
     const int n_vis_row = p.causal ? L - p.s_q + q_tok + 1 : L;
     const int seg_page0 = cpage;
@@ -207,26 +238,32 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(DecodeParams p)
       }
     }
     float m_ref = kNegInf;      // this row's reference point (log2 units)
+    if constexpr (kRedo) m_ref = p.redo_m[(size_t)redo_item * kRowsPerBlock + wave * kRowsPerWave + col];
     float m_seen = kNegInf;     // largest score seen in the segment
     float l_run = 0.f;          // this lane's share of sum_j 2^(s_j - m_ref)
-    int restart = 0;            // this lane's row outgrew its reference
+    int overflow = 0;           // this lane's row outgrew its reference
     f32x4 acc[kDv / 16];
 
-    // One attempt per reference point; the output tiles are zeroed here and
-    // only MFMAs touch them until the segment epilogue.
-    while (true) {
+    // One pass over the segment's pages.  The output tiles are zeroed here
+    // and only MFMAs touch them until the segment epilogue.  The page
+    // prefetched for the next segment (if any) is waited for at the top of
+    // that segment's first page step.
+    auto pass = [&]() __attribute__((always_inline)) {
+      // Zero from an MFMA, so that the tiles are born in the accumulation
+      // registers rather than copied there from VGPRs on every page.
+      const bf16x8 zero8 = __builtin_bit_cast(bf16x8, u32x4{0, 0, 0, 0});
+      const f32x4 zero4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(zero8, zero8, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
 #pragma unroll
-      for (int nt = 0; nt < kDv / 16; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int nt = 0; nt < kDv / 16; ++nt) acc[nt] = zero4;
       l_run = 0.f;
-      bool done = false;        // the segment's last page has been computed
-      int vote = 0;
-
+      // The loop leaves at its bottom, so the tiles' loop-carried value has
+      // the next page's first MFMA as its only use and every MFMA can
+      // accumulate in place.
       while (true) {
-        // Page `it` has landed in every wave's share; the buffer of page it-1
-        // is free; and every wave has voted on a restart.
-        __builtin_amdgcn_s_waitcnt(0);
-        vote = __syncthreads_or(restart);
-        if (vote || done) break;
+        // Page `it` has landed in every wave's share and the buffer of page
+        // it-1 is free.
+        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+        __syncthreads();
         char* buf = lds_page[it & 1];
         const int valid = min(kPage, L - cpage * kPage);
         if (valid < kPage) {
@@ -234,10 +271,12 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(DecodeParams p)
           __syncthreads();
         }
         if (lvalid) {
-          const int page_id = __builtin_amdgcn_readfirstlane(p.block_table[(size_t)lb * p.max_pages + lpage]);
-          stage_page(kv_head + (size_t)page_id * page_stride_bytes, page_span, lane_src_off, row_stride_bytes,
-                     lds_page[(it + 1) & 1], wave);
+          // The cursor moves first: its table reads are complete before the
+          // DMAs go out.
+          const int page_id = ld_uniform(p.block_table + (size_t)lb * p.max_pages + lpage);
           lvalid = next_page(meta, p.seqlens, lb, lpage, lend);
+          stage_page(kv_head + (size_t)page_id * page_stride_bytes, page_span, lane_src_off, row_stride_bytes,
+                     lds_base + ((it + 1) & 1) * kPageBytes, wave);
         }
 
         // Per-lane LDS bases of this page's fragment reads; every read is one
@@ -264,21 +303,52 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(DecodeParams p)
 
         const int key0 = cpage * kPage;
         const bool need_mask = key0 + kPage > n_vis_min;
+
+        // Fragment reads.  K: lane (col, grp4) of read i = 2*ks + tt of
+        // k-step kk holds key 32kk + 16tt + col, chunk 4*ks + grp4 (the A
+        // operand of S^T = K Q^T).  V: the A operand of O^T += V^T P^T for
+        // column tile nt needs, in lane (n = col, grp4), V[key][16nt + n] for
+        // keys 32kk + 4*grp4 + m and 32kk + 16 + 4*grp4 + m: two transposing
+        // reads of 4 rows x 16 columns, where lane l fetches row l/4,
+        // columns 4*(l%4)..+3 of the 16-column tile.
+        auto read_k = [&](int kk, int i) __attribute__((always_inline)) {
+          const int ks = i >> 1, tt = i & 1;
+          return *(lds_bf16x8*)(kb[ks & 1] + (uint32_t)((2 * (2 * kk + tt) * 9 + (ks >> 1)) * 1024));
+        };
+        auto read_v = [&](int kk, int nt) __attribute__((always_inline)) {
+          const uint32_t o0 = (uint32_t)(((4 * kk + 0) * 9 + (nt >> 2)) * 1024);
+          const uint32_t o1 = (uint32_t)(((4 * kk + 2) * 9 + (nt >> 2)) * 1024);
+          const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vb[nt & 3] + o0));
+          const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vb[nt & 3] + o1));
+          return __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
+        };
+
+        // The page's instruction stream is laid out here in issue order --
+        // every fragment read kKAhead (K) or kVAhead (V) MFMAs ahead of its
+        // use, the first K reads of the next k-step under the last output
+        // MFMAs of this one -- and sched_barrier(0) pins that order, so LDS
+        // latency stays behind the MFMA pipeline.
+        constexpr int kKReads = 2 * (kDqk / 32);   // 36 per k-step
+        constexpr int kKAhead = 8;
+        constexpr int kVAhead = 4;
+        bf16x8 kf[2][kKReads];
+        bf16x8 vf[kDv / 16];
+#pragma unroll
+        for (int i = 0; i < kKAhead; ++i) kf[0][i] = read_k(0, i);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
-          // ---- S^T = K Q^T for key tiles t = 2kk, 2kk+1 (16 keys each), 18 k-steps of 32 ----
-          // Lane (col, grp4) reads key 16t + col, chunk 4*ks + grp4.
-          f32x4 s[2];
+          // ---- S^T = K Q^T for key tiles 2kk, 2kk+1: two interleaved MFMA chains ----
+          f32x4 s[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
-          for (int tt = 0; tt < 2; ++tt) {
-            const int t = 2 * kk + tt;
-            s[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int ks = 0; ks < kDqk / 32; ++ks) {
-              const bf16x8 kf = *(lds_bf16x8*)(kb[ks & 1] + (uint32_t)((2 * t * 9 + (ks >> 1)) * 1024));
-              s[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[ks], s[tt], 0, 0, 0);
-            }
+          for (int i = 0; i < kKReads; ++i) {
+            s[i & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kk][i], qf[i >> 1], s[i & 1], 0, 0, 0);
+            if (i + kKAhead < kKReads) kf[kk][i + kKAhead] = read_k(kk, i + kKAhead);
+            __builtin_amdgcn_sched_barrier(0);
           }
+#pragma unroll
+          for (int nt = 0; nt < kVAhead; ++nt) vf[nt] = read_v(kk, nt);
+          __builtin_amdgcn_sched_barrier(0);
 
           // ---- softmax weights (base 2) ----
           // Lane (col, grp4) holds, for its query row, key key0 + 32kk + 16tt + 4*grp4 + i in s[tt][i].
@@ -300,8 +370,8 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(DecodeParams p)
           m_seen = fmaxf(m_seen, rmax);
           if (m_ref == kNegInf) {
             m_ref = rmax;           // nothing accumulated yet: adopt this maximum
-          } else if (rmax > m_ref + kRestartThreshold) {
-            restart = 1;            // this page is still computed, then thrown away
+          } else if (rmax > m_ref + kOverflowThreshold) {
+            overflow = 1;           // this segment's result for the row is void
           }
           const float m_use = m_ref == kNegInf ? 0.f : m_ref;
           float w[8];
@@ -317,42 +387,47 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(DecodeParams p)
           const bf16x8 pf = __builtin_bit_cast(
               bf16x8, u32x4{pack_bf16x2(w[0], w[1]), pack_bf16x2(w[2], w[3]), pack_bf16x2(w[4], w[5]),
                             pack_bf16x2(w[6], w[7])});
+          __builtin_amdgcn_sched_barrier(0);
 
           // ---- O^T += V^T P^T : 32 column tiles of 16 ----
-          // The A operand needs, in lane (n = col, grp4), V[key][n] for the same
-          // keys: two transposing reads of 4 rows x 16 columns (rows 4*grp4 + m
-          // and 16 + 4*grp4 + m).  Lane l of such a read fetches row l/4,
-          // columns 4*(l%4)..+3 of the 16-column tile.
 #pragma unroll
           for (int nt = 0; nt < kDv / 16; ++nt) {
-            const uint32_t o0 = (uint32_t)(((4 * kk + 0) * 9 + (nt >> 2)) * 1024);
-            const uint32_t o1 = (uint32_t)(((4 * kk + 2) * 9 + (nt >> 2)) * 1024);
-            const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vb[nt & 3] + o0));
-            const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vb[nt & 3] + o1));
-            const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
-            acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf, acc[nt], 0, 0, 0);
+            acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[nt], pf, acc[nt], 0, 0, 0);
+            if (nt + kVAhead < kDv / 16) {
+              vf[nt + kVAhead] = read_v(kk, nt + kVAhead);
+            } else if (kk == 0) {
+              // first K reads of the next k-step, two per remaining MFMA
+              const int i = 2 * (nt + kVAhead - kDv / 16);
+              kf[1][i] = read_k(1, i);
+              kf[1][i + 1] = read_k(1, i + 1);
+            }
+            __builtin_amdgcn_sched_barrier(0);
           }
         }
 
         ++it;
-        if (cpage + 1 == cend)
-          done = true;            // leave after the next restart vote
-        else
-          ++cpage;
+        if (cpage + 1 == cend) break;
+        ++cpage;
       }
-      if (!vote) break;
-      // Restart: recompute the segment from its first page with the larger
-      // references.  Every wave has passed the vote, so both buffers are free.
-      restart = 0;
-      m_ref = m_seen;
-      cpage = seg_page0;
-      lb = b;
-      lpage = seg_page0;
-      lend = cend;
-      const int page_id = __builtin_amdgcn_readfirstlane(p.block_table[(size_t)lb * p.max_pages + lpage]);
-      stage_page(kv_head + (size_t)page_id * page_stride_bytes, page_span, lane_src_off, row_stride_bytes,
-                 lds_page[it & 1], wave);
-      lvalid = next_page(meta, p.seqlens, lb, lpage, lend);
+    };
+
+    pass();
+    bool write_out = row_ok;
+    if constexpr (!kRedo) {
+      // A segment where some row overflowed is recorded for the redo launch
+      // (with every row's maximum) and leaves its outputs to it.  Every
+      // segment writes its flag, so stale flags never survive a call.
+      const int item = (slot * p.h_kv + g) * p.row_blocks + rb;
+      const int ovf = __syncthreads_or(overflow);
+      if (tid == 0) p.redo_flag[item] = ovf;
+      if (ovf) {
+        if (tid < kMetaInts) {
+          const int rec[kMetaInts] = {b, seg_page0, b, cend, slot - s0, 0, 0, 0};
+          p.redo_meta[(size_t)item * kMetaInts + tid] = rec[tid];
+        }
+        if (grp4 == 0) p.redo_m[(size_t)item * kRowsPerBlock + wave * kRowsPerWave + col] = m_seen;
+        write_out = false;
+      }
     }
 
     // ---------------- segment epilogue ----------------
@@ -361,7 +436,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(DecodeParams p)
     const float inv = empty ? 0.f : 1.f / l_tot;
     const float lse_nat = empty ? kNegInf : (m_ref + __log2f(l_tot)) * 0.69314718055994531f;
     // Lane (col, grp4) holds O[qrow][16*nt + 4*grp4 + i] in acc[nt][i].
-    if (row_ok) {
+    if (write_out) {
       if (nsplit == 1) {
         uint16_t* op = p.o + ((size_t)(b * p.s_q + q_tok) * p.h_q + q_head) * kDv + 4 * grp4;
 #pragma unroll
@@ -381,7 +456,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(DecodeParams p)
     }
 
     // Next segment: the sequence after this one in the worker's range.
-    if (cb == meta[2]) break;
+    if (cb == meta_b1) break;
     int nb = cb, np = cpage, ne = cend;
     if (!next_page(meta, p.seqlens, nb, np, ne)) break;
     cb = nb;
@@ -390,7 +465,51 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(DecodeParams p)
   }
 }
 
+template <bool kSingleHead>
+__global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(DecodeParams p) {
+  __shared__ __attribute__((aligned(1024))) char lds_page[2][kPageBytes];
+  // Block -> (worker, latent head, row block).  Blocks are dispatched to the
+  // XCDs round-robin; the row blocks of one (worker, head) share its KV
+  // stream, so they are given ids on the same XCD, issued back to back.
+  const int xcd = blockIdx.x % kNumXcd;
+  const int k = blockIdx.x / kNumXcd;
+  const int rb = k % p.row_blocks;
+  const int grp = (k / p.row_blocks) * kNumXcd + xcd;
+  if (grp >= p.num_workers * p.h_kv) return;
+  const int worker = grp / p.h_kv;
+  const int g = grp - worker * p.h_kv;
+  decode_worker<kSingleHead, false>(p, lds_page, p.meta + (size_t)worker * kMetaInts, g, rb, -1);
+}
+
+// One workgroup redoes, one after another, the segments the decode launch
+// flagged (none for ordinary scores: the launch then only scans the flags).
+template <bool kSingleHead>
+__global__ __launch_bounds__(kThreads, 1) void mla_redo_kernel(DecodeParams p) {
+  __shared__ __attribute__((aligned(1024))) char lds_page[2][kPageBytes];
+  __shared__ int list[kRedoScan];
+  __shared__ int n_list;
+  const int tid = threadIdx.x;
+  const int total = p.num_splits[p.batch] * p.h_kv * p.row_blocks;
+  for (int base = 0; base < total; base += kRedoScan) {
+    if (tid == 0) n_list = 0;
+    __syncthreads();
+    for (int i = base + tid; i < min(total, base + kRedoScan); i += kThreads)
+      if (p.redo_flag[i]) list[atomicAdd(&n_list, 1)] = i;
+    __syncthreads();
+    const int n = n_list;
+    for (int e = 0; e < n; ++e) {
+      const int item = list[e];
+      const int rb = item % p.row_blocks;
+      const int g = (item / p.row_blocks) % p.h_kv;
+      decode_worker<kSingleHead, true>(p, lds_page, p.redo_meta + (size_t)item * kMetaInts, g, rb, item);
+      __syncthreads();
+    }
+  }
+}
+
 template __global__ void mla_decode_kernel<true>(DecodeParams p);
 template __global__ void mla_decode_kernel<false>(DecodeParams p);
+template __global__ void mla_redo_kernel<true>(DecodeParams p);
+template __global__ void mla_redo_kernel<false>(DecodeParams p);
 
 }  // namespace mla

@@ -23,6 +23,7 @@ constexpr int kMetaInts = 8;
 constexpr int kMaxWorkers = 4096;
 constexpr int kSchedThreads = 256;
 constexpr int kCombineRowsPerBlock = 4;            // one wave per (sequence, head, query row)
+constexpr int kRedoScan = 1024;                    // redo flags one scan step of the redo launch reads
 
 struct DecodeParams {
   const uint16_t* q;            // bf16 [B][s_q][h_q][576]
@@ -35,12 +36,15 @@ struct DecodeParams {
   float* lse;                   // [B][h_q][s_q]
   float* ws_o;                  // [W+B][h_kv][R][512]
   float* ws_lse;                // [W+B][h_kv][R]
+  int32_t* redo_flag;           // [W+B][h_kv][row_blocks]: segment overflowed (1) or not (0)
+  int32_t* redo_meta;           // [W+B][h_kv][row_blocks][8]: a flagged segment as a one-segment worker
+  float* redo_m;                // [W+B][h_kv][row_blocks][64]: its rows' maximum scores (log2 units)
   int batch, s_q, h_q, h_kv;
   int rows;                     // R = s_q * h_q / h_kv
   int group;                    // G = h_q / h_kv
   int max_pages;
   int num_workers;
-  int row_blocks;               // ceil(R / 128)
+  int row_blocks;               // ceil(R / 64)
   int causal;
   float scale_log2;             // softmax scale * log2(e)
 };
@@ -65,6 +69,8 @@ struct SchedParams {
 
 template <bool kSingleHead>
 __global__ void mla_decode_kernel(DecodeParams p);
+template <bool kSingleHead>
+__global__ void mla_redo_kernel(DecodeParams p);
 __global__ void mla_combine_kernel(CombineParams p);
 __global__ void mla_sched_kernel(SchedParams p);
 

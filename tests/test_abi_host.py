@@ -29,7 +29,8 @@ def declared_functions():
 def test_header_declares_the_boundary():
     names = set(declared_functions())
     assert {"mla_get_metadata", "mla_decode_paged", "mla_num_workers", "mla_workspace_bytes",
-            "mla_status_string", "mla_decode_splitkv", "mla_combine_splits", "mla_sched_fixed_overhead"} <= names
+            "mla_status_string", "mla_decode_splitkv", "mla_decode_redo", "mla_combine_splits",
+            "mla_sched_fixed_overhead"} <= names
 
 
 def test_library_exports_every_declared_symbol():
@@ -55,7 +56,11 @@ def test_status_strings():
 def test_workspace_bytes():
     lib = _lib()
     got = lib.mla_workspace_bytes(64, 1, 128, 1, 512, 256)
-    assert got == ((256 + 64) * 128 * 513 * 4 + 255) // 256 * 256
+    a256 = lambda x: (x + 255) // 256 * 256
+    slots, rows = 256 + 64, 128
+    items = slots * 1 * 2                     # two row blocks of 64
+    assert got == (a256(slots * rows * 512 * 4) + a256(slots * rows * 4)
+                   + a256(items * 4) + a256(items * 8 * 4) + a256(items * 64 * 4))
     assert lib.mla_workspace_bytes(0, 1, 128, 1, 512, 256) == 0
     assert lib.mla_workspace_bytes(2, 1, 128, 3, 512, 256) == 0     # h_q % h_kv != 0
     assert lib.mla_workspace_bytes(2, 1, 128, 1, 256, 256) == 0     # dv != 512
@@ -69,12 +74,12 @@ def test_fixed_overhead_matches_reference_rule():
 FAKE = 0x10000   # 64 KB-aligned, never dereferenced: every call below fails validation first
 
 
-def _decode(lib, **kw):
+def _decode(lib, entry="mla_decode_paged", **kw):
     args = dict(q=FAKE, kv=FAKE, bt=FAKE, max_pages=4, num_pages=8, seqlens=FAKE, batch=2, s_q=1, h_q=16,
                 h_kv=1, d_qk=576, dv=512, meta=FAKE, ns=FAKE, W=256, causal=0, scale=0.0, o=FAKE, lse=FAKE,
                 ws=FAKE, ws_bytes=1 << 30, stream=None)
     args.update(kw)
-    return lib.mla_decode_paged(*args.values())
+    return getattr(lib, entry)(*args.values())
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -86,8 +91,9 @@ def _decode(lib, **kw):
     (dict(ws_bytes=1024), -3),
     (dict(W=0), -4), (dict(W=5000), -4),
 ])
-def test_decode_rejects_invalid_arguments(kw, status):
-    assert _decode(_lib(), **kw) == status
+@pytest.mark.parametrize("entry", ["mla_decode_paged", "mla_decode_splitkv", "mla_decode_redo"])
+def test_decode_rejects_invalid_arguments(kw, status, entry):
+    assert _decode(_lib(), entry, **kw) == status
 
 
 def test_metadata_and_combine_reject_invalid_arguments():

@@ -71,22 +71,25 @@ def test_softmax_scale_argument():
     compare(o, lse, O, LSE, ulp_aware=True, label="scale 0.02")
 
 
-def test_reference_point_restart():
-    """Later pages score far above the first page: the kernel has to move its
-    softmax reference point (restart the segment) and still match."""
+@pytest.mark.parametrize("W", [1, 3])
+def test_reference_point_overflow(W):
+    """Scores on later pages rise far above the first 32 keys of the split
+    (more than 2^48 in the kernel's base-2 weights): the decode launch must
+    flag the split and the redo launch recompute it, unsplit (W=1) and split
+    (W=3) alike.  Only the k^R columns are scaled, so V stays N(0, 1)."""
     inp = _custom(2, 1, 64, 1, False, [64 * 6 + 5, 64 * 3], seed=9)
     kv = inp.kvcache.float()
     bt = inp.block_table.numpy()
     for b in range(2):
-        kv[int(bt[b, 0])] *= 0.05             # first page: small scores
+        kv[int(bt[b, 0])] *= 0.05                       # first page: scores near 0
         for j in range(1, 3):
-            kv[int(bt[b, j])] *= 4.0          # next pages: scores ~80x the first
+            kv[int(bt[b, j]), :, :, 512:] *= 40.0       # next pages: k^R . q^R std ~ 320
     inp.kvcache = kv.to(inp.kvcache.dtype)
-    o, lse, _, _ = run_gpu(inp, num_workers=1)
     O, LSE = oracle(inp)
-    # values up to 4x larger and a very peaked softmax: bf16 weights give
-    # errors proportional to the largest cached values
-    compare(o, lse, O, LSE, scale=8.0, label="restart")
+    # the rise the kernel sees, in log2 units: far beyond its 48 threshold
+    assert (LSE.max() - 0.0) / np.log(2) > 48
+    o, lse, _, _ = run_gpu(inp, num_workers=W)
+    compare(o, lse, O, LSE, ulp_aware=True, label=f"overflow W={W}")
 
 
 # --------------------------------------------------------------------------
