@@ -36,7 +36,7 @@ def hipcc() -> str:
 
 def build(verbose: bool = False, extra_flags=()) -> str:
     """Compile every HIP source for gfx950 and link the shared library."""
-    cmd = [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++20", "-fPIC", "-shared",
            "-munsafe-fp-atomics", "-I", os.path.join(ROOT, "include"), *DEVICE_FLAGS, *extra_flags,
            *[os.path.join(CSRC, s) for s in SOURCES], "-o", LIB_PATH + ".tmp"]
     if verbose:

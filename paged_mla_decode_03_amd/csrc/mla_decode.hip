@@ -41,6 +41,8 @@
 //   * Keys a query may not see (tail slots of the last page, causal future)
 //     get weight 0, and tail rows of the last page are zeroed in LDS so that
 //     whatever the cache holds there never reaches O.
+#include <utility>
+
 #include "mla_kernels.h"
 
 namespace mla {
@@ -82,7 +84,8 @@ __device__ inline int lds_tile_offset(int r, int c) {
 }
 
 // Stage one page of one latent head into LDS with 72 wave-wide DMAs (18 per
-// wave).  Lane u of the DMA for tile (a, b) fetches row 8a + u/8, chunk
+// wave), either at once (stage_page) or one at a time (stage_tile) spread
+// through the previous page's MFMAs.  Lane u of the DMA for tile (a, b) fetches row 8a + u/8, chunk
 // 8b + ((u%8) ^ (u/8)): a per-lane byte offset (lane_off) plus a wave-uniform
 // one, relative to a buffer resource that spans exactly this page's 64 rows.
 // All 64 rows are fetched; rows past the sequence end are zeroed afterwards by
@@ -95,21 +98,29 @@ __device__ inline int lds_tile_offset(int r, int c) {
 // (s_waitcnt vmcnt(0) at the top of each page step) before any wave reads
 // the buffer, and issues no vector load of its own between a DMA and that
 // wait.  They write no registers.
+__device__ inline __amdgpu_buffer_rsrc_t page_resource(const char* page_head, uint32_t page_bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc((void*)page_head, (short)0, (int)page_bytes, (int)kBufferConfig);
+}
+
+// DMA number k (0 .. kLdsDmaPerWave-1) of this wave for one page: tile
+// j = 4k + wave, i.e. rows 8a..8a+7 x chunks 8b..8b+7 with j = 9a + b.
+__device__ inline void stage_tile(__amdgpu_buffer_rsrc_t rsrc, uint32_t lane_off, int row_stride_bytes,
+                                  uint32_t lds_dst, int wave, int k) {
+  const int j = k * kWaves + wave;            // tile index 9a + b, wave-uniform
+  const int a = j / 9, b = j - (j / 9) * 9;
+  const uint32_t m0 = lds_dst + j * 1024;
+  const uint32_t soff = a * 8 * row_stride_bytes + b * 128;
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               :
+               : "s"(m0), "v"(lane_off), "s"(rsrc), "s"(soff)
+               : "memory", "m0");
+}
+
 __device__ inline void stage_page(const char* page_head, uint32_t page_bytes, uint32_t lane_off,
                                   int row_stride_bytes, uint32_t lds_dst, int wave) {
-  const __amdgpu_buffer_rsrc_t rsrc =
-      __builtin_amdgcn_make_buffer_rsrc((void*)page_head, (short)0, (int)page_bytes, (int)kBufferConfig);
+  const __amdgpu_buffer_rsrc_t rsrc = page_resource(page_head, page_bytes);
 #pragma unroll
-  for (int k = 0; k < kLdsDmaPerWave; ++k) {
-    const int j = k * kWaves + wave;            // tile index 9a + b, wave-uniform
-    const int a = j / 9, b = j - (j / 9) * 9;
-    const uint32_t m0 = lds_dst + j * 1024;
-    const uint32_t soff = a * 8 * row_stride_bytes + b * 128;
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
-                 :
-                 : "s"(m0), "v"(lane_off), "s"(rsrc), "s"(soff)
-                 : "memory", "m0");
-  }
+  for (int k = 0; k < kLdsDmaPerWave; ++k) stage_tile(rsrc, lane_off, row_stride_bytes, lds_dst, wave, k);
 }
 
 // Zero rows [valid, 64) of a staged page (its cache slots lie past the
@@ -207,12 +218,15 @@ __device__ __forceinline__ void decode_worker(const DecodeParams& p, char (*lds_
   const int q_tok = row_ok ? qrow / p.group : 0;
   const int q_head = g * p.group + (row_ok ? qrow - q_tok * p.group : 0);
 
-  // First page in flight before anything else.
+  // First page in flight before anything else; the id of the page after it
+  // is read now, one page ahead of its DMAs.
+  int next_pid = 0;
   {
     const int page_id = ld_uniform(p.block_table + (size_t)lb * p.max_pages + lpage);
     lvalid = next_page(meta, p.seqlens, lb, lpage, lend);
     stage_page(kv_head + (size_t)page_id * page_stride_bytes, page_span, lane_src_off, row_stride_bytes,
                lds_base, wave);
+    if (lvalid) next_pid = ld_uniform(p.block_table + (size_t)lb * p.max_pages + lpage);
   }
 
   int it = 0;
@@ -223,7 +237,6 @@ __device__ __forceinline__ void decode_worker(const DecodeParams& p, char (*lds_
     const int s0 = ld_uniform(p.num_splits + b);
     const int nsplit = ld_uniform(p.num_splits + b + 1) - s0;
     const int slot = s0 + (b == meta_b0 ? ld_uniform(meta + 4) : 0);
-    const int n_vis_min = p.causal ? L - p.s_q + 1 : L;
     const int n_vis_row = p.causal ? L - p.s_q + q_tok + 1 : L;
     const int seg_page0 = cpage;
 
@@ -270,13 +283,16 @@ __device__ __forceinline__ void decode_worker(const DecodeParams& p, char (*lds_
           zero_tail_rows(buf, valid, tid);
           __syncthreads();
         }
+        // The next page's DMAs go out one by one inside this page's MFMA
+        // stream (below); its id was read a page ago.  The cursor moves on
+        // and the id after it is read now.
+        const bool dma = lvalid;
+        const __amdgpu_buffer_rsrc_t dma_rsrc =
+            page_resource(kv_head + (size_t)next_pid * page_stride_bytes, page_span);
+        const uint32_t dma_dst = lds_base + ((it + 1) & 1) * kPageBytes;
         if (lvalid) {
-          // The cursor moves first: its table reads are complete before the
-          // DMAs go out.
-          const int page_id = ld_uniform(p.block_table + (size_t)lb * p.max_pages + lpage);
           lvalid = next_page(meta, p.seqlens, lb, lpage, lend);
-          stage_page(kv_head + (size_t)page_id * page_stride_bytes, page_span, lane_src_off, row_stride_bytes,
-                     lds_base + ((it + 1) & 1) * kPageBytes, wave);
+          if (lvalid) next_pid = ld_uniform(p.block_table + (size_t)lb * p.max_pages + lpage);
         }
 
         // Per-lane LDS bases of this page's fragment reads; every read is one
@@ -302,7 +318,6 @@ __device__ __forceinline__ void decode_worker(const DecodeParams& p, char (*lds_
         }
 
         const int key0 = cpage * kPage;
-        const bool need_mask = key0 + kPage > n_vis_min;
 
         // Fragment reads.  K: lane (col, grp4) of read i = 2*ks + tt of
         // k-step kk holds key 32kk + 16tt + col, chunk 4*ks + grp4 (the A
@@ -323,87 +338,102 @@ __device__ __forceinline__ void decode_worker(const DecodeParams& p, char (*lds_
           return __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
         };
 
-        // The page's instruction stream is laid out here in issue order --
-        // every fragment read kKAhead (K) or kVAhead (V) MFMAs ahead of its
-        // use, the first K reads of the next k-step under the last output
-        // MFMAs of this one -- and sched_barrier(0) pins that order, so LDS
-        // latency stays behind the MFMA pipeline.
-        constexpr int kKReads = 2 * (kDqk / 32);   // 36 per k-step
+        // Softmax weights (base 2) of k-step kk in eight short stages, each
+        // placed between two MFMAs of the stream so that its VALU work and
+        // latency hide behind the matrix pipe.  Lane (col, grp4) holds, for
+        // its query row, key key0 + 32kk + 16tt + 4*grp4 + i in s[kk][tt][i];
+        // keys the row may not see get weight 0 (no branch: every page masks).
+        f32x4 s[2][2];
+        float x[2][8], rm[2], mu[2], w[2][8];
+        bf16x8 pf[2];
+        auto softmax_stage = [&](int kk, int st) __attribute__((always_inline)) {
+          if (st == 0) {
+            float r = kNegInf;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const int key = key0 + 32 * kk + 16 * (e >> 2) + 4 * grp4 + (e & 3);
+              const float v = s[kk][e >> 2][e & 3] * p.scale_log2;
+              x[kk][e] = key < n_vis_row ? v : kNegInf;
+              r = fmaxf(r, x[kk][e]);
+            }
+            rm[kk] = r;
+          } else if (st == 1) {
+            rm[kk] = xor16_pair(rm[kk], true);
+          } else if (st == 2) {
+            const float r = xor32_pair(rm[kk], true);
+            m_seen = fmaxf(m_seen, r);
+            if (m_ref == kNegInf) {
+              m_ref = r;            // nothing accumulated yet: adopt this maximum
+            } else if (r > m_ref + kOverflowThreshold) {
+              overflow = 1;         // this segment's result for the row is void
+            }
+            mu[kk] = m_ref == kNegInf ? 0.f : m_ref;
+          } else if (st < 7) {
+            const int e = 2 * (st - 3);
+            w[kk][e] = __builtin_amdgcn_exp2f(x[kk][e] - mu[kk]);
+            w[kk][e + 1] = __builtin_amdgcn_exp2f(x[kk][e + 1] - mu[kk]);
+            l_run += w[kk][e] + w[kk][e + 1];
+          } else {
+            // B operand of the output MFMA: slot e holds key 16*(e/4) + 4*grp4 + e%4.
+            pf[kk] = __builtin_bit_cast(
+                bf16x8, u32x4{pack_bf16x2(w[kk][0], w[kk][1]), pack_bf16x2(w[kk][2], w[kk][3]),
+                              pack_bf16x2(w[kk][4], w[kk][5]), pack_bf16x2(w[kk][6], w[kk][7])});
+          }
+        };
+
+        // The page's instruction stream, in issue order: 72 score MFMAs (two
+        // k-steps, two interleaved chains each) then 64 output MFMAs.  After
+        // MFMA g come: the K read kKAhead MFMAs ahead, the V read kVAhead
+        // output MFMAs ahead, every kDmaEvery-th MFMA one DMA of the next
+        // page, and the softmax stages of k-step 0 (during the k-step 1
+        // scores) and of k-step 1 (during the k-step 0 outputs).
+        // sched_barrier(0) pins that order.
+        constexpr int kKReads = 2 * (kDqk / 32);   // 36 score MFMAs per k-step
+        constexpr int kQk = 2 * kKReads;           // 72
+        constexpr int kPv = 2 * (kDv / 16);        // 64
         constexpr int kKAhead = 8;
         constexpr int kVAhead = 4;
-        bf16x8 kf[2][kKReads];
-        bf16x8 vf[kDv / 16];
+        constexpr int kDmaEvery = 5;
+        constexpr int kSm0At = kKReads + 1;        // first stage of k-step 0's softmax
+        constexpr int kSm1At = kQk + 1;            // first stage of k-step 1's softmax
+        constexpr int kSmEvery = 3;
+        static_assert(kSm0At + 7 * kSmEvery < kQk, "k-step 0 weights ready before its outputs");
+        static_assert(kSm1At + 7 * kSmEvery < kQk + kPv / 2, "k-step 1 weights ready before its outputs");
+        static_assert(kDmaEvery * kLdsDmaPerWave <= kQk + kPv, "every DMA inside the stream");
+        bf16x8 kf[kQk];
+        bf16x8 vf[kPv];
 #pragma unroll
-        for (int i = 0; i < kKAhead; ++i) kf[0][i] = read_k(0, i);
+        for (int i = 0; i < kKAhead; ++i) kf[i] = read_k(i / kKReads, i % kKReads);
         __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-          // ---- S^T = K Q^T for key tiles 2kk, 2kk+1: two interleaved MFMA chains ----
-          f32x4 s[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-#pragma unroll
-          for (int i = 0; i < kKReads; ++i) {
-            s[i & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kk][i], qf[i >> 1], s[i & 1], 0, 0, 0);
-            if (i + kKAhead < kKReads) kf[kk][i + kKAhead] = read_k(kk, i + kKAhead);
-            __builtin_amdgcn_sched_barrier(0);
+        // One step of the stream; G is a template parameter so that every
+        // array index and schedule decision is a compile-time constant.
+        auto step = [&]<int G>() __attribute__((always_inline)) {
+          constexpr int g = G;
+          if constexpr (g < kQk) {
+            constexpr int kk = g / kKReads, i = g % kKReads;
+            const f32x4 c = i < 2 ? f32x4{0.f, 0.f, 0.f, 0.f} : s[kk][i & 1];
+            s[kk][i & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[g], qf[i >> 1], c, 0, 0, 0);
+          } else {
+            constexpr int n = g - kQk, kk = n / (kPv / 2), nt = n % (kPv / 2);
+            acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[n], pf[kk], acc[nt], 0, 0, 0);
           }
-#pragma unroll
-          for (int nt = 0; nt < kVAhead; ++nt) vf[nt] = read_v(kk, nt);
+          if constexpr (g + kKAhead < kQk) kf[g + kKAhead] = read_k((g + kKAhead) / kKReads, (g + kKAhead) % kKReads);
+          {
+            constexpr int v = g + kVAhead - kQk;   // V read issued after MFMA g
+            if constexpr (v >= 0 && v < kPv) vf[v] = read_v(v / (kPv / 2), v % (kPv / 2));
+          }
+          if constexpr (g % kDmaEvery == 0 && g / kDmaEvery < kLdsDmaPerWave) {
+            if (dma) stage_tile(dma_rsrc, lane_src_off, row_stride_bytes, dma_dst, wave, g / kDmaEvery);
+          }
+          if constexpr (g >= kSm0At && (g - kSm0At) % kSmEvery == 0 && (g - kSm0At) / kSmEvery < 8)
+            softmax_stage(0, (g - kSm0At) / kSmEvery);
+          if constexpr (g >= kSm1At && (g - kSm1At) % kSmEvery == 0 && (g - kSm1At) / kSmEvery < 8)
+            softmax_stage(1, (g - kSm1At) / kSmEvery);
           __builtin_amdgcn_sched_barrier(0);
-
-          // ---- softmax weights (base 2) ----
-          // Lane (col, grp4) holds, for its query row, key key0 + 32kk + 16tt + 4*grp4 + i in s[tt][i].
-          float rmax = kNegInf;
-#pragma unroll
-          for (int tt = 0; tt < 2; ++tt) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              float x = s[tt][i] * p.scale_log2;
-              if (need_mask) {
-                const int key = key0 + 32 * kk + 16 * tt + 4 * grp4 + i;
-                x = key < n_vis_row ? x : kNegInf;
-              }
-              s[tt][i] = x;
-              rmax = fmaxf(rmax, x);
-            }
-          }
-          rmax = row_max4(rmax);
-          m_seen = fmaxf(m_seen, rmax);
-          if (m_ref == kNegInf) {
-            m_ref = rmax;           // nothing accumulated yet: adopt this maximum
-          } else if (rmax > m_ref + kOverflowThreshold) {
-            overflow = 1;           // this segment's result for the row is void
-          }
-          const float m_use = m_ref == kNegInf ? 0.f : m_ref;
-          float w[8];
-#pragma unroll
-          for (int tt = 0; tt < 2; ++tt) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              w[4 * tt + i] = __builtin_amdgcn_exp2f(s[tt][i] - m_use);
-              l_run += w[4 * tt + i];
-            }
-          }
-          // B operand of the output MFMA: slot e holds key 16*(e/4) + 4*grp4 + e%4 of this k-step.
-          const bf16x8 pf = __builtin_bit_cast(
-              bf16x8, u32x4{pack_bf16x2(w[0], w[1]), pack_bf16x2(w[2], w[3]), pack_bf16x2(w[4], w[5]),
-                            pack_bf16x2(w[6], w[7])});
-          __builtin_amdgcn_sched_barrier(0);
-
-          // ---- O^T += V^T P^T : 32 column tiles of 16 ----
-#pragma unroll
-          for (int nt = 0; nt < kDv / 16; ++nt) {
-            acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[nt], pf, acc[nt], 0, 0, 0);
-            if (nt + kVAhead < kDv / 16) {
-              vf[nt + kVAhead] = read_v(kk, nt + kVAhead);
-            } else if (kk == 0) {
-              // first K reads of the next k-step, two per remaining MFMA
-              const int i = 2 * (nt + kVAhead - kDv / 16);
-              kf[1][i] = read_k(1, i);
-              kf[1][i + 1] = read_k(1, i + 1);
-            }
-            __builtin_amdgcn_sched_barrier(0);
-          }
-        }
+        };
+        [&]<int... G>(std::integer_sequence<int, G...>) __attribute__((always_inline)) {
+          (step.template operator()<G>(), ...);
+        }(std::make_integer_sequence<int, kQk + kPv>{});
 
         ++it;
         if (cpage + 1 == cend) break;
