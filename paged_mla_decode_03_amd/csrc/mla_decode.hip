@@ -180,8 +180,23 @@ __device__ inline bool next_page(const int32_t* meta, const int32_t* seqlens, in
 
 }  // namespace
 
+// LDS of one decode workgroup besides the two page buffers: the softmax
+// weights P of the current page in the output MFMA's operand order, and one
+// float per (key half, row) for the row statistics the two key halves swap.
+struct DecodeShared {
+  char p[kPBytes];
+  float x[2][kRowsPerBlock];
+};
+
 // One worker's pages for latent head g and row block rb: every segment in the
 // worker's range [meta[0], meta[1]) .. [meta[2], meta[3]).
+//
+// Roles of the four waves.  Scores: wave w takes query rows 32*(w>>1) ..+31
+// (its Q, 32 x 576 bf16, sits in VGPRs) against keys 32*(w&1) ..+31 of each
+// page, so every K fragment it reads feeds two MFMAs.  Outputs: wave w owns
+// output columns 128w ..+127 for all 64 rows (O^T, 128 x 64 fp32, in 32
+// MFMA accumulators), reading P of all rows from LDS and V columns
+// 128w ..+127 only.  Per page the LDS reads are K 144 KB + V 64 KB + P 32 KB.
 //
 // kSingleHead: h_kv == 1, so a page's rows are contiguous 1152-byte rows and
 // every stride is a compile-time constant.
@@ -190,13 +205,17 @@ __device__ inline bool next_page(const int32_t* meta, const int32_t* seqlens, in
 // recorded for it, which is its maximum score over the segment.
 template <bool kSingleHead, bool kRedo>
 __device__ __forceinline__ void decode_worker(const DecodeParams& p, char (*lds_page)[kPageBytes],
-                                              const int32_t* meta, int g, int rb, int redo_item) {
+                                              DecodeShared& sh, const int32_t* meta, int g, int rb,
+                                              int redo_item) {
   const uint32_t lds_base = (uint32_t)(uintptr_t)&lds_page[0][0];   // LDS byte address
+  const uint32_t lds_p = (uint32_t)(uintptr_t)&sh.p[0];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
+  const int rh = wave >> 1;       // score rows 32rh .. 32rh+31
+  const int kh = wave & 1;        // score keys 32kh .. 32kh+31 of each page
   const int grp4 = lane >> 4;     // which 4-key / 8-wide k slice of an MFMA fragment
-  const int col = lane & 15;      // query row within the wave's tile / MFMA column
+  const int col = lane & 15;      // row (or output column) within an MFMA tile
 
   const int meta_b0 = ld_uniform(meta + 0), meta_b1 = ld_uniform(meta + 2);
   if (meta_b1 < meta_b0) return;                       // worker without pages
@@ -212,11 +231,16 @@ __device__ __forceinline__ void decode_worker(const DecodeParams& p, char (*lds_
   const char* kv_head = (const char*)p.kv + (size_t)g * kRowBytes;
   const uint32_t lane_src_off = (lane >> 3) * row_stride_bytes + ((lane & 7) ^ (lane >> 3)) * 16;
 
-  // This lane's query row.
-  const int qrow = rb * kRowsPerBlock + wave * kRowsPerWave + col;
-  const bool row_ok = qrow < p.rows;
-  const int q_tok = row_ok ? qrow / p.group : 0;
-  const int q_head = g * p.group + (row_ok ? qrow - q_tok * p.group : 0);
+  // The rows this lane serves.  Scores / softmax: rows 32rh + 16rt + col,
+  // rt = 0, 1.  Outputs: rows 16rt4 + col, rt4 = 0..3.
+  auto row_tok = [&](int r) __attribute__((always_inline)) {
+    const int qrow = rb * kRowsPerBlock + r;
+    return qrow < p.rows ? qrow / p.group : 0;
+  };
+  auto row_head = [&](int r) __attribute__((always_inline)) {
+    const int qrow = rb * kRowsPerBlock + r;
+    return qrow < p.rows ? g * p.group + (qrow - (qrow / p.group) * p.group) : 0;
+  };
 
   // First page in flight before anything else; the id of the page after it
   // is read now, one page ahead of its DMAs.
@@ -237,251 +261,315 @@ __device__ __forceinline__ void decode_worker(const DecodeParams& p, char (*lds_
     const int s0 = ld_uniform(p.num_splits + b);
     const int nsplit = ld_uniform(p.num_splits + b + 1) - s0;
     const int slot = s0 + (b == meta_b0 ? ld_uniform(meta + 4) : 0);
-    const int n_vis_row = p.causal ? L - p.s_q + q_tok + 1 : L;
     const int seg_page0 = cpage;
 
-    // Q fragments: lane (col, grp4) holds row qrow, dims 32*ks + 8*grp4 .. +7.
-    bf16x8 qf[kDqk / 32];
-    {
-      const uint16_t* qp = p.q + ((size_t)(b * p.s_q + q_tok) * p.h_q + q_head) * kDqk + grp4 * 8;
+    // Q fragments of the two score row tiles: lane (col, grp4) holds row
+    // 32rh + 16rt + col, dims 32*ks + 8*grp4 .. +7.
+    bf16x8 qf[2][kDqk / 32];
+    int n_vis[2];              // keys each of this lane's score rows may see
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt) {
+      const int r = 32 * rh + 16 * rt + col;
+      const bool ok = rb * kRowsPerBlock + r < p.rows;
+      const int tok = row_tok(r);
+      n_vis[rt] = p.causal ? L - p.s_q + tok + 1 : L;
+      const uint16_t* qp = p.q + ((size_t)(b * p.s_q + tok) * p.h_q + row_head(r)) * kDqk + grp4 * 8;
 #pragma unroll
       for (int ks = 0; ks < kDqk / 32; ++ks) {
-        u32x4 v = row_ok ? *(const u32x4*)(qp + ks * 32) : u32x4{0, 0, 0, 0};
-        qf[ks] = __builtin_bit_cast(bf16x8, v);
+        u32x4 v = ok ? *(const u32x4*)(qp + ks * 32) : u32x4{0, 0, 0, 0};
+        qf[rt][ks] = __builtin_bit_cast(bf16x8, v);
       }
     }
-    float m_ref = kNegInf;      // this row's reference point (log2 units)
-    if constexpr (kRedo) m_ref = p.redo_m[(size_t)redo_item * kRowsPerBlock + wave * kRowsPerWave + col];
-    float m_seen = kNegInf;     // largest score seen in the segment
-    float l_run = 0.f;          // this lane's share of sum_j 2^(s_j - m_ref)
-    int overflow = 0;           // this lane's row outgrew its reference
-    f32x4 acc[kDv / 16];
+    float m_ref[2], m_seen[2], l_run[2];   // per score row, log2 units / this lane's share
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt) {
+      m_ref[rt] = kNegInf;
+      if constexpr (kRedo)
+        m_ref[rt] = p.redo_m[(size_t)redo_item * kRowsPerBlock + 32 * rh + 16 * rt + col];
+      m_seen[rt] = kNegInf;
+      l_run[rt] = 0.f;
+    }
+    int overflow = 0;          // a score rose more than kOverflowThreshold above its reference
 
-    // One pass over the segment's pages.  The output tiles are zeroed here
-    // and only MFMAs touch them until the segment epilogue.  The page
-    // prefetched for the next segment (if any) is waited for at the top of
-    // that segment's first page step.
-    auto pass = [&]() __attribute__((always_inline)) {
-      // Zero from an MFMA, so that the tiles are born in the accumulation
-      // registers rather than copied there from VGPRs on every page.
+    // Output tiles, zeroed from an MFMA so that they are born in the
+    // accumulation registers.
+    f32x4 acc[8][4];
+    {
       const bf16x8 zero8 = __builtin_bit_cast(bf16x8, u32x4{0, 0, 0, 0});
       const f32x4 zero4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(zero8, zero8, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
 #pragma unroll
-      for (int nt = 0; nt < kDv / 16; ++nt) acc[nt] = zero4;
-      l_run = 0.f;
-      // The loop leaves at its bottom, so the tiles' loop-carried value has
-      // the next page's first MFMA as its only use and every MFMA can
-      // accumulate in place.
-      while (true) {
-        // Page `it` has landed in every wave's share and the buffer of page
-        // it-1 is free.
-        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+      for (int d = 0; d < 8; ++d)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) acc[d][t] = zero4;
+    }
+
+    // The loop leaves at its bottom, so the tiles' loop-carried value has
+    // the next page's first MFMA as its only use and every MFMA can
+    // accumulate in place.
+    while (true) {
+      // Page `it` has landed in every wave's share, the buffer of page it-1
+      // and the P buffer are free.
+      __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+      __syncthreads();
+      char* buf = lds_page[it & 1];
+      const int valid = min(kPage, L - cpage * kPage);
+      if (valid < kPage) {
+        zero_tail_rows(buf, valid, tid);
         __syncthreads();
-        char* buf = lds_page[it & 1];
-        const int valid = min(kPage, L - cpage * kPage);
-        if (valid < kPage) {
-          zero_tail_rows(buf, valid, tid);
-          __syncthreads();
-        }
-        // The next page's DMAs go out one by one inside this page's MFMA
-        // stream (below); its id was read a page ago.  The cursor moves on
-        // and the id after it is read now.
-        const bool dma = lvalid;
-        const __amdgpu_buffer_rsrc_t dma_rsrc =
-            page_resource(kv_head + (size_t)next_pid * page_stride_bytes, page_span);
-        const uint32_t dma_dst = lds_base + ((it + 1) & 1) * kPageBytes;
-        if (lvalid) {
-          lvalid = next_page(meta, p.seqlens, lb, lpage, lend);
-          if (lvalid) next_pid = ld_uniform(p.block_table + (size_t)lb * p.max_pages + lpage);
-        }
-
-        // Per-lane LDS bases of this page's fragment reads; every read is one
-        // of them plus a compile-time offset below 64 KB.  They are formed
-        // here from the lane id rather than kept live across the loop, and the
-        // empty asm statements stop the compiler from hoisting them or turning
-        // base + offset into an OR that the DS immediate offset cannot absorb.
-        int ln = lane;
-        asm volatile("" : "+v"(ln));
-        const uint32_t page_base = (uint32_t)(uintptr_t)buf;
-        uint32_t kb[2], vb[4];
-#pragma unroll
-        for (int par = 0; par < 2; ++par) {
-          // K row (ln & 15) (+16 per key tile), chunk 4*par + (ln >> 4) (+8 per 2 k-steps)
-          kb[par] = page_base + lds_tile_offset(ln & 15, 4 * par + (ln >> 4));
-          asm volatile("" : "+v"(kb[par]));
-        }
-#pragma unroll
-        for (int m4 = 0; m4 < 4; ++m4) {
-          // V row (ln >> 2) (+16 per read), columns 16*m4 + 4*(ln & 3) (+64 per 4 tiles)
-          vb[m4] = page_base + lds_tile_offset(ln >> 2, 2 * m4 + ((ln & 3) >> 1)) + 8 * (ln & 1);
-          asm volatile("" : "+v"(vb[m4]));
-        }
-
-        const int key0 = cpage * kPage;
-
-        // Fragment reads.  K: lane (col, grp4) of read i = 2*ks + tt of
-        // k-step kk holds key 32kk + 16tt + col, chunk 4*ks + grp4 (the A
-        // operand of S^T = K Q^T).  V: the A operand of O^T += V^T P^T for
-        // column tile nt needs, in lane (n = col, grp4), V[key][16nt + n] for
-        // keys 32kk + 4*grp4 + m and 32kk + 16 + 4*grp4 + m: two transposing
-        // reads of 4 rows x 16 columns, where lane l fetches row l/4,
-        // columns 4*(l%4)..+3 of the 16-column tile.
-        auto read_k = [&](int kk, int i) __attribute__((always_inline)) {
-          const int ks = i >> 1, tt = i & 1;
-          return *(lds_bf16x8*)(kb[ks & 1] + (uint32_t)((2 * (2 * kk + tt) * 9 + (ks >> 1)) * 1024));
-        };
-        auto read_v = [&](int kk, int nt) __attribute__((always_inline)) {
-          const uint32_t o0 = (uint32_t)(((4 * kk + 0) * 9 + (nt >> 2)) * 1024);
-          const uint32_t o1 = (uint32_t)(((4 * kk + 2) * 9 + (nt >> 2)) * 1024);
-          const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vb[nt & 3] + o0));
-          const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vb[nt & 3] + o1));
-          return __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
-        };
-
-        // Softmax weights (base 2) of k-step kk in eight short stages, each
-        // placed between two MFMAs of the stream so that its VALU work and
-        // latency hide behind the matrix pipe.  Lane (col, grp4) holds, for
-        // its query row, key key0 + 32kk + 16tt + 4*grp4 + i in s[kk][tt][i];
-        // keys the row may not see get weight 0 (no branch: every page masks).
-        f32x4 s[2][2];
-        float x[2][8], rm[2], mu[2], w[2][8];
-        bf16x8 pf[2];
-        auto softmax_stage = [&](int kk, int st) __attribute__((always_inline)) {
-          if (st == 0) {
-            float r = kNegInf;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              const int key = key0 + 32 * kk + 16 * (e >> 2) + 4 * grp4 + (e & 3);
-              const float v = s[kk][e >> 2][e & 3] * p.scale_log2;
-              x[kk][e] = key < n_vis_row ? v : kNegInf;
-              r = fmaxf(r, x[kk][e]);
-            }
-            rm[kk] = r;
-          } else if (st == 1) {
-            rm[kk] = xor16_pair(rm[kk], true);
-          } else if (st == 2) {
-            const float r = xor32_pair(rm[kk], true);
-            m_seen = fmaxf(m_seen, r);
-            if (m_ref == kNegInf) {
-              m_ref = r;            // nothing accumulated yet: adopt this maximum
-            } else if (r > m_ref + kOverflowThreshold) {
-              overflow = 1;         // this segment's result for the row is void
-            }
-            mu[kk] = m_ref == kNegInf ? 0.f : m_ref;
-          } else if (st < 7) {
-            const int e = 2 * (st - 3);
-            w[kk][e] = __builtin_amdgcn_exp2f(x[kk][e] - mu[kk]);
-            w[kk][e + 1] = __builtin_amdgcn_exp2f(x[kk][e + 1] - mu[kk]);
-            l_run += w[kk][e] + w[kk][e + 1];
-          } else {
-            // B operand of the output MFMA: slot e holds key 16*(e/4) + 4*grp4 + e%4.
-            pf[kk] = __builtin_bit_cast(
-                bf16x8, u32x4{pack_bf16x2(w[kk][0], w[kk][1]), pack_bf16x2(w[kk][2], w[kk][3]),
-                              pack_bf16x2(w[kk][4], w[kk][5]), pack_bf16x2(w[kk][6], w[kk][7])});
-          }
-        };
-
-        // The page's instruction stream, in issue order: 72 score MFMAs (two
-        // k-steps, two interleaved chains each) then 64 output MFMAs.  After
-        // MFMA g come: the K read kKAhead MFMAs ahead, the V read kVAhead
-        // output MFMAs ahead, every kDmaEvery-th MFMA one DMA of the next
-        // page, and the softmax stages of k-step 0 (during the k-step 1
-        // scores) and of k-step 1 (during the k-step 0 outputs).
-        // sched_barrier(0) pins that order.
-        constexpr int kKReads = 2 * (kDqk / 32);   // 36 score MFMAs per k-step
-        constexpr int kQk = 2 * kKReads;           // 72
-        constexpr int kPv = 2 * (kDv / 16);        // 64
-        constexpr int kKAhead = 8;
-        constexpr int kVAhead = 4;
-        constexpr int kDmaEvery = 5;
-        constexpr int kSm0At = kKReads + 1;        // first stage of k-step 0's softmax
-        constexpr int kSm1At = kQk + 1;            // first stage of k-step 1's softmax
-        constexpr int kSmEvery = 3;
-        static_assert(kSm0At + 7 * kSmEvery < kQk, "k-step 0 weights ready before its outputs");
-        static_assert(kSm1At + 7 * kSmEvery < kQk + kPv / 2, "k-step 1 weights ready before its outputs");
-        static_assert(kDmaEvery * kLdsDmaPerWave <= kQk + kPv, "every DMA inside the stream");
-        bf16x8 kf[kQk];
-        bf16x8 vf[kPv];
-#pragma unroll
-        for (int i = 0; i < kKAhead; ++i) kf[i] = read_k(i / kKReads, i % kKReads);
-        __builtin_amdgcn_sched_barrier(0);
-        // One step of the stream; G is a template parameter so that every
-        // array index and schedule decision is a compile-time constant.
-        auto step = [&]<int G>() __attribute__((always_inline)) {
-          constexpr int g = G;
-          if constexpr (g < kQk) {
-            constexpr int kk = g / kKReads, i = g % kKReads;
-            const f32x4 c = i < 2 ? f32x4{0.f, 0.f, 0.f, 0.f} : s[kk][i & 1];
-            s[kk][i & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[g], qf[i >> 1], c, 0, 0, 0);
-          } else {
-            constexpr int n = g - kQk, kk = n / (kPv / 2), nt = n % (kPv / 2);
-            acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[n], pf[kk], acc[nt], 0, 0, 0);
-          }
-          if constexpr (g + kKAhead < kQk) kf[g + kKAhead] = read_k((g + kKAhead) / kKReads, (g + kKAhead) % kKReads);
-          {
-            constexpr int v = g + kVAhead - kQk;   // V read issued after MFMA g
-            if constexpr (v >= 0 && v < kPv) vf[v] = read_v(v / (kPv / 2), v % (kPv / 2));
-          }
-          if constexpr (g % kDmaEvery == 0 && g / kDmaEvery < kLdsDmaPerWave) {
-            if (dma) stage_tile(dma_rsrc, lane_src_off, row_stride_bytes, dma_dst, wave, g / kDmaEvery);
-          }
-          if constexpr (g >= kSm0At && (g - kSm0At) % kSmEvery == 0 && (g - kSm0At) / kSmEvery < 8)
-            softmax_stage(0, (g - kSm0At) / kSmEvery);
-          if constexpr (g >= kSm1At && (g - kSm1At) % kSmEvery == 0 && (g - kSm1At) / kSmEvery < 8)
-            softmax_stage(1, (g - kSm1At) / kSmEvery);
-          __builtin_amdgcn_sched_barrier(0);
-        };
-        [&]<int... G>(std::integer_sequence<int, G...>) __attribute__((always_inline)) {
-          (step.template operator()<G>(), ...);
-        }(std::make_integer_sequence<int, kQk + kPv>{});
-
-        ++it;
-        if (cpage + 1 == cend) break;
-        ++cpage;
       }
-    };
+      // The next page's DMAs go out one by one inside this page's MFMA
+      // streams (below); its id was read a page ago.  The cursor moves on
+      // and the id after it is read now.
+      const bool dma = lvalid;
+      const __amdgpu_buffer_rsrc_t dma_rsrc = page_resource(kv_head + (size_t)next_pid * page_stride_bytes, page_span);
+      const uint32_t dma_dst = lds_base + ((it + 1) & 1) * kPageBytes;
+      if (lvalid) {
+        lvalid = next_page(meta, p.seqlens, lb, lpage, lend);
+        if (lvalid) next_pid = ld_uniform(p.block_table + (size_t)lb * p.max_pages + lpage);
+      }
 
-    pass();
-    bool write_out = row_ok;
+      // Per-lane LDS bases of this page's fragment reads; every read is one
+      // of them plus a compile-time offset below 64 KB.  They are formed
+      // here from the lane id rather than kept live across the loop, and the
+      // empty asm statements stop the compiler from hoisting them or turning
+      // base + offset into an OR that the DS immediate offset cannot absorb.
+      int ln = lane;
+      asm volatile("" : "+v"(ln));
+      const uint32_t page_base = (uint32_t)(uintptr_t)buf;
+      uint32_t kb[2], vb[4], pw, pr;
+#pragma unroll
+      for (int par = 0; par < 2; ++par) {
+        // K row 32kh + (ln & 15) (+16 per key tile), chunk 4*par + (ln >> 4) (+8 per 2 k-steps)
+        kb[par] = page_base + kh * (4 * 9 * 1024) + lds_tile_offset(ln & 15, 4 * par + (ln >> 4));
+        asm volatile("" : "+v"(kb[par]));
+      }
+#pragma unroll
+      for (int m4 = 0; m4 < 4; ++m4) {
+        // V row (ln >> 2) (+16 per read), columns 128*wave + 16*m4 + 4*(ln & 3) (+64 per 4 tiles)
+        vb[m4] = page_base + wave * (2 * 1024) + lds_tile_offset(ln >> 2, 2 * m4 + ((ln & 3) >> 1)) + 8 * (ln & 1);
+        asm volatile("" : "+v"(vb[m4]));
+      }
+      // P: row r at r * kPRowBytes; 16-byte chunk 4*kk + slot/8 of that row.
+      pw = lds_p + (32 * rh + (ln & 15)) * kPRowBytes + (4 * kh + (ln >> 4)) * 16;
+      pr = lds_p + (ln & 15) * kPRowBytes + (ln >> 4) * 16;
+      asm volatile("" : "+v"(pw));
+      asm volatile("" : "+v"(pr));
+
+      const int key0 = cpage * kPage + 32 * kh;
+
+      auto read_k = [&](int kt, int ks) __attribute__((always_inline)) {
+        return *(lds_bf16x8*)(kb[ks & 1] + (uint32_t)((2 * kt * 9 + (ks >> 1)) * 1024));
+      };
+      // A operand of O^T += V^T P^T for output tile d of k-step kk: lane
+      // (n = col, grp4) gets V[key][128*wave + 16d + n] for keys 32kk +
+      // 4*grp4 + m and 32kk + 16 + 4*grp4 + m, from two transposing reads of
+      // 4 rows x 16 columns (lane l fetches row l/4, columns 4*(l%4)..+3).
+      auto read_v = [&](int kk, int d) __attribute__((always_inline)) {
+        const uint32_t o0 = (uint32_t)(((4 * kk + 0) * 9 + (d >> 2)) * 1024);
+        const uint32_t o1 = (uint32_t)(((4 * kk + 2) * 9 + (d >> 2)) * 1024);
+        const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vb[d & 3] + o0));
+        const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vb[d & 3] + o1));
+        return __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
+      };
+      // B operand for output row tile t of k-step kk: lane (col, grp4) gets
+      // P[16t + col][slots 8*grp4 .. +7 of k-step kk].
+      auto read_p = [&](int kk, int t) __attribute__((always_inline)) {
+        return *(lds_bf16x8*)(pr + (uint32_t)(t * 16 * kPRowBytes + kk * 64));
+      };
+
+      // ---- scores: S^T = K Q^T for key tiles kt = 0, 1 and row tiles rt = 0, 1 ----
+      // 72 MFMAs in issue order (kt, ks, rt); every K fragment feeds the two
+      // row tiles; reads run kKAhead fragments ahead; one DMA of the next
+      // page after every kDmaEvery-th MFMA of the page (scores and outputs).
+      constexpr int kKs = kDqk / 32;             // 18
+      constexpr int kQk = 2 * kKs * 2;           // 72 score MFMAs
+      constexpr int kPv = 2 * 8 * 4;             // 64 output MFMAs
+      constexpr int kKAhead = 4;
+      constexpr int kDmaEvery = 7;
+      static_assert(kDmaEvery * (kLdsDmaPerWave - 1) < kQk + kPv, "every DMA inside the streams");
+      f32x4 s[2][2];
+      bf16x8 kf[2 * kKs];
+#pragma unroll
+      for (int r = 0; r < kKAhead; ++r) kf[r] = read_k(r / kKs, r % kKs);
+      __builtin_amdgcn_sched_barrier(0);
+      auto dma_step = [&]<int G>() __attribute__((always_inline)) {
+        if constexpr (G % kDmaEvery == 0 && G / kDmaEvery < kLdsDmaPerWave) {
+          if (dma) stage_tile(dma_rsrc, lane_src_off, row_stride_bytes, dma_dst, wave, G / kDmaEvery);
+        }
+      };
+      auto qk_step = [&]<int G>() __attribute__((always_inline)) {
+        constexpr int r = G / 2, rt = G % 2, kt = r / kKs, ks = r % kKs;
+        const f32x4 c = ks == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : s[kt][rt];
+        s[kt][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[r], qf[rt][ks], c, 0, 0, 0);
+        if constexpr (rt == 1 && r + kKAhead < 2 * kKs) kf[r + kKAhead] = read_k((r + kKAhead) / kKs, (r + kKAhead) % kKs);
+        dma_step.template operator()<G>();
+        __builtin_amdgcn_sched_barrier(0);
+      };
+      [&]<int... G>(std::integer_sequence<int, G...>) __attribute__((always_inline)) {
+        (qk_step.template operator()<G>(), ...);
+      }(std::make_integer_sequence<int, kQk>{});
+
+      // ---- softmax weights (base 2), elementwise against the row reference ----
+      // Lane (col, grp4) holds, for score row rt, key key0 + 16kt + 4*grp4 + i
+      // in s[kt][rt][i]; keys a row may not see get weight 0.
+      float x[2][2][4];
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int key = key0 + 16 * kt + 4 * grp4 + i;
+            const float v = s[kt][rt][i] * p.scale_log2;
+            x[rt][kt][i] = key < n_vis[rt] ? v : kNegInf;
+          }
+      if (!kRedo && cpage == seg_page0) {
+        // First page of the segment: each row's reference is its maximum
+        // over the page's 64 keys, from both key halves.
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt) {
+          float r = kNegInf;
+#pragma unroll
+          for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) r = fmaxf(r, x[rt][kt][i]);
+          r = row_max4(r);
+          if (grp4 == 0) sh.x[kh][32 * rh + 16 * rt + col] = r;
+          m_ref[rt] = r;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt) m_ref[rt] = fmaxf(m_ref[rt], sh.x[kh ^ 1][32 * rh + 16 * rt + col]);
+      }
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt) {
+        const float mu = m_ref[rt] == kNegInf ? 0.f : m_ref[rt];
+        float w[2][4];
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float v = x[rt][kt][i];
+            // A row with no reference yet that sees a key here, or a score far
+            // above the reference, voids the segment's result for this pass.
+            overflow |= v > m_ref[rt] + kOverflowThreshold;
+            m_seen[rt] = fmaxf(m_seen[rt], v);
+            w[kt][i] = __builtin_amdgcn_exp2f(v - mu);
+            l_run[rt] += w[kt][i];
+          }
+        // Slot 8*grp4 + 4kt + i of this row's k-step kh = key 16kt + 4*grp4 + i.
+        const u32x4 pv = u32x4{pack_bf16x2(w[0][0], w[0][1]), pack_bf16x2(w[0][2], w[0][3]),
+                               pack_bf16x2(w[1][0], w[1][1]), pack_bf16x2(w[1][2], w[1][3])};
+        *(__attribute__((address_space(3))) u32x4*)(pw + (uint32_t)(rt * 16 * kPRowBytes)) = pv;
+      }
+      __syncthreads();            // P of all 64 rows is in LDS
+
+      // ---- outputs: O^T += V^T P^T, 8 column tiles x 4 row tiles per k-step ----
+      // 64 MFMAs in issue order (kk, d, t); V fragments kVAhead ahead; the
+      // four P fragments of a k-step read before its first MFMA.
+      constexpr int kVAhead = 2;
+      bf16x8 vf[2][8], pfr[2][4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) pfr[0][t] = read_p(0, t);
+#pragma unroll
+      for (int d = 0; d < kVAhead; ++d) vf[0][d] = read_v(0, d);
+      __builtin_amdgcn_sched_barrier(0);
+      auto pv_step = [&]<int G>() __attribute__((always_inline)) {
+        constexpr int n = G - kQk, kk = n / 32, d = (n % 32) / 4, t = n % 4;
+        acc[d][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[kk][d], pfr[kk][t], acc[d][t], 0, 0, 0);
+        if constexpr (t == 3) {
+          constexpr int nv = kk * 8 + d + kVAhead;   // next V fragment to read
+          if constexpr (nv < 16) vf[nv / 8][nv % 8] = read_v(nv / 8, nv % 8);
+        }
+        if constexpr (kk == 0 && d == 5) pfr[1][t] = read_p(1, t);
+        dma_step.template operator()<G>();
+        __builtin_amdgcn_sched_barrier(0);
+      };
+      [&]<int... G>(std::integer_sequence<int, G...>) __attribute__((always_inline)) {
+        (pv_step.template operator()<G + kQk>(), ...);
+      }(std::make_integer_sequence<int, kPv>{});
+
+      ++it;
+      if (cpage + 1 == cend) break;
+      ++cpage;
+    }
+
+    // ---------------- segment epilogue ----------------
+    // Every wave is past its last output MFMA before the exchanges below
+    // reuse sh.x; the page buffers are not touched here.
+    const int ovf = __syncthreads_or(overflow);
+    bool write_out = true;
     if constexpr (!kRedo) {
       // A segment where some row overflowed is recorded for the redo launch
-      // (with every row's maximum) and leaves its outputs to it.  Every
-      // segment writes its flag, so stale flags never survive a call.
+      // (with every row's maximum over both key halves) and leaves its
+      // outputs to it.  Every segment writes its flag, so stale flags never
+      // survive a call.
       const int item = (slot * p.h_kv + g) * p.row_blocks + rb;
-      const int ovf = __syncthreads_or(overflow);
       if (tid == 0) p.redo_flag[item] = ovf;
       if (ovf) {
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt) {
+          const float r = row_max4(m_seen[rt]);
+          if (grp4 == 0) sh.x[kh][32 * rh + 16 * rt + col] = r;
+        }
+        __syncthreads();
         if (tid < kMetaInts) {
           const int rec[kMetaInts] = {b, seg_page0, b, cend, slot - s0, 0, 0, 0};
           p.redo_meta[(size_t)item * kMetaInts + tid] = rec[tid];
         }
-        if (grp4 == 0) p.redo_m[(size_t)item * kRowsPerBlock + wave * kRowsPerWave + col] = m_seen;
+        if (tid < kRowsPerBlock)
+          p.redo_m[(size_t)item * kRowsPerBlock + tid] = fmaxf(sh.x[0][tid], sh.x[1][tid]);
+        __syncthreads();
         write_out = false;
       }
     }
-
-    // ---------------- segment epilogue ----------------
-    const float l_tot = row_sum4(l_run);
-    const bool empty = l_tot == 0.f;
-    const float inv = empty ? 0.f : 1.f / l_tot;
-    const float lse_nat = empty ? kNegInf : (m_ref + __log2f(l_tot)) * 0.69314718055994531f;
-    // Lane (col, grp4) holds O[qrow][16*nt + 4*grp4 + i] in acc[nt][i].
     if (write_out) {
-      if (nsplit == 1) {
-        uint16_t* op = p.o + ((size_t)(b * p.s_q + q_tok) * p.h_q + q_head) * kDv + 4 * grp4;
+      // Row sums: each score wave's share over its key half, then both halves.
 #pragma unroll
-        for (int nt = 0; nt < kDv / 16; ++nt) {
-          uint2 v;
-          v.x = pack_bf16x2(acc[nt][0] * inv, acc[nt][1] * inv);
-          v.y = pack_bf16x2(acc[nt][2] * inv, acc[nt][3] * inv);
-          *(uint2*)(op + 16 * nt) = v;
+      for (int rt = 0; rt < 2; ++rt) {
+        const float l = row_sum4(l_run[rt]);
+        if (grp4 == 0) sh.x[kh][32 * rh + 16 * rt + col] = l;
+      }
+      __syncthreads();
+      // LSE of the score rows, written by the key-half-0 waves.
+      if (kh == 0 && grp4 == 0) {
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt) {
+          const int r = 32 * rh + 16 * rt + col;
+          const int qrow = rb * kRowsPerBlock + r;
+          const float l = sh.x[0][r] + sh.x[1][r];
+          const float lse_nat = l == 0.f ? kNegInf : (m_ref[rt] + __log2f(l)) * 0.69314718055994531f;
+          if (qrow < p.rows) {
+            if (nsplit == 1)
+              p.lse[((size_t)b * p.h_q + row_head(r)) * p.s_q + row_tok(r)] = lse_nat;
+            else
+              p.ws_lse[(size_t)(slot * p.h_kv + g) * p.rows + qrow] = lse_nat;
+          }
         }
-        if (grp4 == 0) p.lse[((size_t)b * p.h_q + q_head) * p.s_q + q_tok] = lse_nat;
-      } else {
-        float* wp = p.ws_o + ((size_t)(slot * p.h_kv + g) * p.rows + qrow) * kDv + 4 * grp4;
+      }
+      // O: lane (col, grp4) holds O[16t + col][128*wave + 16d + 4*grp4 + i] in acc[d][t][i].
 #pragma unroll
-        for (int nt = 0; nt < kDv / 16; ++nt) *(f32x4*)(wp + 16 * nt) = acc[nt] * inv;
-        if (grp4 == 0) p.ws_lse[(size_t)(slot * p.h_kv + g) * p.rows + qrow] = lse_nat;
+      for (int t = 0; t < 4; ++t) {
+        const int r = 16 * t + col;
+        const int qrow = rb * kRowsPerBlock + r;
+        const float l = sh.x[0][r] + sh.x[1][r];
+        const float inv = l == 0.f ? 0.f : 1.f / l;
+        if (qrow < p.rows) {
+          if (nsplit == 1) {
+            uint16_t* op = p.o + ((size_t)(b * p.s_q + row_tok(r)) * p.h_q + row_head(r)) * kDv + 128 * wave + 4 * grp4;
+#pragma unroll
+            for (int d = 0; d < 8; ++d) {
+              uint2 v;
+              v.x = pack_bf16x2(acc[d][t][0] * inv, acc[d][t][1] * inv);
+              v.y = pack_bf16x2(acc[d][t][2] * inv, acc[d][t][3] * inv);
+              *(uint2*)(op + 16 * d) = v;
+            }
+          } else {
+            float* wp = p.ws_o + ((size_t)(slot * p.h_kv + g) * p.rows + qrow) * kDv + 128 * wave + 4 * grp4;
+#pragma unroll
+            for (int d = 0; d < 8; ++d) *(f32x4*)(wp + 16 * d) = acc[d][t] * inv;
+          }
+        }
       }
     }
 
@@ -498,6 +586,7 @@ __device__ __forceinline__ void decode_worker(const DecodeParams& p, char (*lds_
 template <bool kSingleHead>
 __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(DecodeParams p) {
   __shared__ __attribute__((aligned(1024))) char lds_page[2][kPageBytes];
+  __shared__ __attribute__((aligned(16))) DecodeShared sh;
   // Block -> (worker, latent head, row block).  Blocks are dispatched to the
   // XCDs round-robin; the row blocks of one (worker, head) share its KV
   // stream, so they are given ids on the same XCD, issued back to back.
@@ -508,7 +597,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(DecodeParams p)
   if (grp >= p.num_workers * p.h_kv) return;
   const int worker = grp / p.h_kv;
   const int g = grp - worker * p.h_kv;
-  decode_worker<kSingleHead, false>(p, lds_page, p.meta + (size_t)worker * kMetaInts, g, rb, -1);
+  decode_worker<kSingleHead, false>(p, lds_page, sh, p.meta + (size_t)worker * kMetaInts, g, rb, -1);
 }
 
 // One workgroup redoes, one after another, the segments the decode launch
@@ -516,6 +605,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(DecodeParams p)
 template <bool kSingleHead>
 __global__ __launch_bounds__(kThreads, 1) void mla_redo_kernel(DecodeParams p) {
   __shared__ __attribute__((aligned(1024))) char lds_page[2][kPageBytes];
+  __shared__ __attribute__((aligned(16))) DecodeShared sh;
   __shared__ int list[kRedoScan];
   __shared__ int n_list;
   const int tid = threadIdx.x;
@@ -531,7 +621,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_redo_kernel(DecodeParams p) {
       const int item = list[e];
       const int rb = item % p.row_blocks;
       const int g = (item / p.row_blocks) % p.h_kv;
-      decode_worker<kSingleHead, true>(p, lds_page, p.redo_meta + (size_t)item * kMetaInts, g, rb, item);
+      decode_worker<kSingleHead, true>(p, lds_page, sh, p.redo_meta + (size_t)item * kMetaInts, g, rb, item);
       __syncthreads();
     }
   }

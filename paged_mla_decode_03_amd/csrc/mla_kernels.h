@@ -23,7 +23,9 @@ constexpr int kMetaInts = 8;
 constexpr int kMaxWorkers = 4096;
 constexpr int kSchedThreads = 256;
 constexpr int kCombineRowsPerBlock = 4;            // one wave per (sequence, head, query row)
-constexpr int kRedoScan = 1024;                    // redo flags one scan step of the redo launch reads
+constexpr int kRedoScan = 256;                     // redo flags one scan step of the redo launch reads
+constexpr int kPRowBytes = 2 * kPage + 16;         // one row of softmax weights in LDS, padded against bank conflicts
+constexpr int kPBytes = kRowsPerBlock * kPRowBytes;
 
 struct DecodeParams {
   const uint16_t* q;            // bf16 [B][s_q][h_q][576]
