@@ -267,6 +267,8 @@ __device__ __forceinline__ void decode_worker(const DecodeParams& p, char (*lds_
     // 32rh + 16rt + col, dims 32*ks + 8*grp4 .. +7.
     bf16x8 qf[2][kDqk / 32];
     int n_vis[2];              // keys each of this lane's score rows may see
+    // Fewest keys any row of the block sees (causal rows: the block's first token).
+    const int n_vis_min = p.causal ? L - p.s_q + row_tok(0) + 1 : L;
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt) {
       const int r = 32 * rh + 16 * rt + col;
@@ -318,15 +320,10 @@ __device__ __forceinline__ void decode_worker(const DecodeParams& p, char (*lds_
         __syncthreads();
       }
       // The next page's DMAs go out one by one inside this page's MFMA
-      // streams (below); its id was read a page ago.  The cursor moves on
-      // and the id after it is read now.
+      // streams (below); its id was read a page ago.
       const bool dma = lvalid;
       const __amdgpu_buffer_rsrc_t dma_rsrc = page_resource(kv_head + (size_t)next_pid * page_stride_bytes, page_span);
       const uint32_t dma_dst = lds_base + ((it + 1) & 1) * kPageBytes;
-      if (lvalid) {
-        lvalid = next_page(meta, p.seqlens, lb, lpage, lend);
-        if (lvalid) next_pid = ld_uniform(p.block_table + (size_t)lb * p.max_pages + lpage);
-      }
 
       // Per-lane LDS bases of this page's fragment reads; every read is one
       // of them plus a compile-time offset below 64 KB.  They are formed
@@ -385,7 +382,7 @@ __device__ __forceinline__ void decode_worker(const DecodeParams& p, char (*lds_
       constexpr int kQk = 2 * kKs * 2;           // 72 score MFMAs
       constexpr int kPv = 2 * 8 * 4;             // 64 output MFMAs
       constexpr int kKAhead = 4;
-      constexpr int kDmaEvery = 7;
+      constexpr int kDmaEvery = 5;
       static_assert(kDmaEvery * (kLdsDmaPerWave - 1) < kQk + kPv, "every DMA inside the streams");
       f32x4 s[2][2];
       bf16x8 kf[2 * kKs];
@@ -409,31 +406,54 @@ __device__ __forceinline__ void decode_worker(const DecodeParams& p, char (*lds_
         (qk_step.template operator()<G>(), ...);
       }(std::make_integer_sequence<int, kQk>{});
 
+      // The load cursor moves on and the id of the page after the next is
+      // read here, where waiting for the scalar load costs nothing.
+      if (lvalid) {
+        lvalid = next_page(meta, p.seqlens, lb, lpage, lend);
+        if (lvalid) next_pid = ld_uniform(p.block_table + (size_t)lb * p.max_pages + lpage);
+      }
+
       // ---- softmax weights (base 2), elementwise against the row reference ----
       // Lane (col, grp4) holds, for score row rt, key key0 + 16kt + 4*grp4 + i
       // in s[kt][rt][i]; keys a row may not see get weight 0.
+      // Masking is needed only on a page that holds keys some row may not
+      // see (the sequence's last page, or causal rows); the test is uniform.
+      const bool mask = key0 + 32 > n_vis_min;
       float x[2][2][4];
 #pragma unroll
       for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int key = key0 + 16 * kt + 4 * grp4 + i;
-            const float v = s[kt][rt][i] * p.scale_log2;
-            x[rt][kt][i] = key < n_vis[rt] ? v : kNegInf;
-          }
+          for (int i = 0; i < 4; ++i) x[rt][kt][i] = s[kt][rt][i];
+      if (mask) {
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+          for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int key = key0 + 16 * kt + 4 * grp4 + i;
+              x[rt][kt][i] = key < n_vis[rt] ? x[rt][kt][i] : kNegInf;
+            }
+      }
+      // Row maxima of this lane's 8 raw scores per row (scale > 0 keeps the order).
+      float xm[2];
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt) {
+        float r = kNegInf;
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) r = fmaxf(r, x[rt][kt][i]);
+        xm[rt] = r * p.scale_log2;
+      }
       if (!kRedo && cpage == seg_page0) {
         // First page of the segment: each row's reference is its maximum
         // over the page's 64 keys, from both key halves.
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt) {
-          float r = kNegInf;
-#pragma unroll
-          for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) r = fmaxf(r, x[rt][kt][i]);
-          r = row_max4(r);
+          const float r = row_max4(xm[rt]);
           if (grp4 == 0) sh.x[kh][32 * rh + 16 * rt + col] = r;
           m_ref[rt] = r;
         }
@@ -443,18 +463,17 @@ __device__ __forceinline__ void decode_worker(const DecodeParams& p, char (*lds_
       }
 #pragma unroll
       for (int rt = 0; rt < 2; ++rt) {
+        // A row with no reference yet that sees a key here, or a score far
+        // above the reference, voids the segment's result for this pass.
+        overflow |= xm[rt] > m_ref[rt] + kOverflowThreshold;
+        m_seen[rt] = fmaxf(m_seen[rt], xm[rt]);
         const float mu = m_ref[rt] == kNegInf ? 0.f : m_ref[rt];
         float w[2][4];
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const float v = x[rt][kt][i];
-            // A row with no reference yet that sees a key here, or a score far
-            // above the reference, voids the segment's result for this pass.
-            overflow |= v > m_ref[rt] + kOverflowThreshold;
-            m_seen[rt] = fmaxf(m_seen[rt], v);
-            w[kt][i] = __builtin_amdgcn_exp2f(v - mu);
+            w[kt][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[rt][kt][i], p.scale_log2, -mu));
             l_run[rt] += w[kt][i];
           }
         // Slot 8*grp4 + 4kt + i of this row's k-step kh = key 16kt + 4*grp4 + i.
