@@ -153,9 +153,11 @@ __device__ inline float xor32_pair(float x, bool max_op) {
 __device__ inline float row_max4(float x) { return xor32_pair(xor16_pair(x, true), true); }
 __device__ inline float row_sum4(float x) { return xor32_pair(xor16_pair(x, false), false); }
 
+// Two floats to two bf16 (round to nearest even) in one v_cvt_pk_bf16_f32.
 __device__ inline uint32_t pack_bf16x2(float a, float b) {
-  __bf16 x = (__bf16)a, y = (__bf16)b;
-  return (uint32_t)__builtin_bit_cast(uint16_t, x) | ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){a, b}, bf16x2));
 }
 
 // End page of sequence b's part of this worker's range.
@@ -386,6 +388,75 @@ __device__ __forceinline__ void decode_worker(const DecodeParams& p, char (*lds_
       static_assert(kDmaEvery * (kLdsDmaPerWave - 1) < kQk + kPv, "every DMA inside the streams");
       f32x4 s[2][2];
       bf16x8 kf[2 * kKs];
+
+      // ---- softmax weights (base 2), elementwise against the row reference ----
+      // Lane (col, grp4) holds, for score row rt, key key0 + 16kt + 4*grp4 + i
+      // in s[kt][rt][i]; keys a row may not see get weight 0.  The work of key
+      // tile 0 runs in short stages between the key-tile-1 MFMAs; tile 1's
+      // runs after the stream.  Masking is needed only on a page that holds
+      // keys some row may not see (the sequence's last page, or causal rows).
+      const bool mask = key0 + 32 > n_vis_min;
+      float x[2][2][4], xm[2][2], mu[2];
+      uint32_t pk[2][2][2];
+      auto sm_load = [&](int kt) __attribute__((always_inline)) {
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) x[kt][rt][i] = s[kt][rt][i];
+        if (mask) {
+#pragma unroll
+          for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int key = key0 + 16 * kt + 4 * grp4 + i;
+              x[kt][rt][i] = key < n_vis[rt] ? x[kt][rt][i] : kNegInf;
+            }
+        }
+        // Row maxima of this lane's 4 raw scores per row (the scale is > 0).
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt)
+          xm[kt][rt] = fmaxf(fmaxf(x[kt][rt][0], x[kt][rt][1]), fmaxf(x[kt][rt][2], x[kt][rt][3])) * p.scale_log2;
+      };
+      auto sm_check = [&](int kt) __attribute__((always_inline)) {
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt) {
+          // A row with no reference yet that sees a key here, or a score far
+          // above the reference, voids the segment's result for this pass.
+          overflow |= xm[kt][rt] > m_ref[rt] + kOverflowThreshold;
+          m_seen[rt] = fmaxf(m_seen[rt], xm[kt][rt]);
+          mu[rt] = m_ref[rt] == kNegInf ? 0.f : m_ref[rt];
+        }
+      };
+      auto sm_exp = [&](int kt, int rt, int i0) __attribute__((always_inline)) {
+        const float w0 = __builtin_amdgcn_exp2f(__builtin_fmaf(x[kt][rt][i0], p.scale_log2, -mu[rt]));
+        const float w1 = __builtin_amdgcn_exp2f(__builtin_fmaf(x[kt][rt][i0 + 1], p.scale_log2, -mu[rt]));
+        l_run[rt] += w0 + w1;
+        pk[kt][rt][i0 >> 1] = pack_bf16x2(w0, w1);
+      };
+      // Slots 8*grp4 + 4kt + i of row 32rh + 16rt + col, k-step kh, hold key 16kt + 4*grp4 + i.
+      auto sm_write = [&](int kt) __attribute__((always_inline)) {
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt)
+          *(__attribute__((address_space(3))) uint2*)(pw + (uint32_t)(rt * 16 * kPRowBytes + kt * 8)) =
+              uint2{pk[kt][rt][0], pk[kt][rt][1]};
+      };
+      // First page of the segment: each row's reference is its maximum over
+      // key tile 0 of both key halves (32 of the page's keys, key 0 among
+      // them, so every row that sees the page has a finite reference).
+      auto first_page_reference = [&]() __attribute__((always_inline)) {
+        if (!kRedo && cpage == seg_page0) {
+#pragma unroll
+          for (int rt = 0; rt < 2; ++rt) {
+            const float r = row_max4(xm[0][rt]);
+            if (grp4 == 0) sh.x[kh][32 * rh + 16 * rt + col] = r;
+            m_ref[rt] = r;
+          }
+          __syncthreads();
+#pragma unroll
+          for (int rt = 0; rt < 2; ++rt) m_ref[rt] = fmaxf(m_ref[rt], sh.x[kh ^ 1][32 * rh + 16 * rt + col]);
+        }
+      };
+
 #pragma unroll
       for (int r = 0; r < kKAhead; ++r) kf[r] = read_k(r / kKs, r % kKs);
       __builtin_amdgcn_sched_barrier(0);
@@ -394,12 +465,25 @@ __device__ __forceinline__ void decode_worker(const DecodeParams& p, char (*lds_
           if (dma) stage_tile(dma_rsrc, lane_src_off, row_stride_bytes, dma_dst, wave, G / kDmaEvery);
         }
       };
+      // After score MFMA g (key tile 1): the stages of key tile 0's softmax.
+      auto sm0_step = [&]<int G>() __attribute__((always_inline)) {
+        if constexpr (G == kQk / 2 - 1) {
+          sm_load(0);
+          first_page_reference();
+        } else if constexpr (G >= kQk / 2 + 1 && (G - kQk / 2 - 1) % 3 == 0 && (G - kQk / 2 - 1) / 3 < 6) {
+          constexpr int st = (G - kQk / 2 - 1) / 3;
+          if constexpr (st == 0) sm_check(0);
+          else if constexpr (st <= 4) sm_exp(0, (st - 1) >> 1, 2 * ((st - 1) & 1));
+          else sm_write(0);
+        }
+      };
       auto qk_step = [&]<int G>() __attribute__((always_inline)) {
         constexpr int r = G / 2, rt = G % 2, kt = r / kKs, ks = r % kKs;
         const f32x4 c = ks == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : s[kt][rt];
         s[kt][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[r], qf[rt][ks], c, 0, 0, 0);
         if constexpr (rt == 1 && r + kKAhead < 2 * kKs) kf[r + kKAhead] = read_k((r + kKAhead) / kKs, (r + kKAhead) % kKs);
         dma_step.template operator()<G>();
+        sm0_step.template operator()<G>();
         __builtin_amdgcn_sched_barrier(0);
       };
       [&]<int... G>(std::integer_sequence<int, G...>) __attribute__((always_inline)) {
@@ -413,74 +497,12 @@ __device__ __forceinline__ void decode_worker(const DecodeParams& p, char (*lds_
         if (lvalid) next_pid = ld_uniform(p.block_table + (size_t)lb * p.max_pages + lpage);
       }
 
-      // ---- softmax weights (base 2), elementwise against the row reference ----
-      // Lane (col, grp4) holds, for score row rt, key key0 + 16kt + 4*grp4 + i
-      // in s[kt][rt][i]; keys a row may not see get weight 0.
-      // Masking is needed only on a page that holds keys some row may not
-      // see (the sequence's last page, or causal rows); the test is uniform.
-      const bool mask = key0 + 32 > n_vis_min;
-      float x[2][2][4];
+      // Key tile 1's softmax.
+      sm_load(1);
+      sm_check(1);
 #pragma unroll
-      for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) x[rt][kt][i] = s[kt][rt][i];
-      if (mask) {
-#pragma unroll
-        for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-          for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const int key = key0 + 16 * kt + 4 * grp4 + i;
-              x[rt][kt][i] = key < n_vis[rt] ? x[rt][kt][i] : kNegInf;
-            }
-      }
-      // Row maxima of this lane's 8 raw scores per row (scale > 0 keeps the order).
-      float xm[2];
-#pragma unroll
-      for (int rt = 0; rt < 2; ++rt) {
-        float r = kNegInf;
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) r = fmaxf(r, x[rt][kt][i]);
-        xm[rt] = r * p.scale_log2;
-      }
-      if (!kRedo && cpage == seg_page0) {
-        // First page of the segment: each row's reference is its maximum
-        // over the page's 64 keys, from both key halves.
-#pragma unroll
-        for (int rt = 0; rt < 2; ++rt) {
-          const float r = row_max4(xm[rt]);
-          if (grp4 == 0) sh.x[kh][32 * rh + 16 * rt + col] = r;
-          m_ref[rt] = r;
-        }
-        __syncthreads();
-#pragma unroll
-        for (int rt = 0; rt < 2; ++rt) m_ref[rt] = fmaxf(m_ref[rt], sh.x[kh ^ 1][32 * rh + 16 * rt + col]);
-      }
-#pragma unroll
-      for (int rt = 0; rt < 2; ++rt) {
-        // A row with no reference yet that sees a key here, or a score far
-        // above the reference, voids the segment's result for this pass.
-        overflow |= xm[rt] > m_ref[rt] + kOverflowThreshold;
-        m_seen[rt] = fmaxf(m_seen[rt], xm[rt]);
-        const float mu = m_ref[rt] == kNegInf ? 0.f : m_ref[rt];
-        float w[2][4];
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            w[kt][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[rt][kt][i], p.scale_log2, -mu));
-            l_run[rt] += w[kt][i];
-          }
-        // Slot 8*grp4 + 4kt + i of this row's k-step kh = key 16kt + 4*grp4 + i.
-        const u32x4 pv = u32x4{pack_bf16x2(w[0][0], w[0][1]), pack_bf16x2(w[0][2], w[0][3]),
-                               pack_bf16x2(w[1][0], w[1][1]), pack_bf16x2(w[1][2], w[1][3])};
-        *(__attribute__((address_space(3))) u32x4*)(pw + (uint32_t)(rt * 16 * kPRowBytes)) = pv;
-      }
+      for (int e = 0; e < 4; ++e) sm_exp(1, e >> 1, 2 * (e & 1));
+      sm_write(1);
       __syncthreads();            // P of all 64 rows is in LDS
 
       // ---- outputs: O^T += V^T P^T, 8 column tiles x 4 row tiles per k-step ----
