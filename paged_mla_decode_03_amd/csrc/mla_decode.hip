@@ -52,6 +52,7 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) const bf16x8 lds_bf16x8;
@@ -437,8 +438,8 @@ __device__ __forceinline__ void decode_worker(const DecodeParams& p, char (*lds_
       auto sm_write = [&](int kt) __attribute__((always_inline)) {
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt)
-          *(__attribute__((address_space(3))) uint2*)(pw + (uint32_t)(rt * 16 * kPRowBytes + kt * 8)) =
-              uint2{pk[kt][rt][0], pk[kt][rt][1]};
+          *(__attribute__((address_space(3))) u32x2*)(pw + (uint32_t)(rt * 16 * kPRowBytes + kt * 8)) =
+              u32x2{pk[kt][rt][0], pk[kt][rt][1]};
       };
       // First page of the segment: each row's reference is its maximum over
       // key tile 0 of both key halves (32 of the page's keys, key 0 among
