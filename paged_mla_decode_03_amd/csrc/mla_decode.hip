@@ -441,21 +441,22 @@ __device__ __forceinline__ void decode_worker(const DecodeParams& p, char (*lds_
           *(__attribute__((address_space(3))) u32x2*)(pw + (uint32_t)(rt * 16 * kPRowBytes + kt * 8)) =
               u32x2{pk[kt][rt][0], pk[kt][rt][1]};
       };
-      // First page of the segment: each row's reference is its maximum over
-      // key tile 0 of both key halves (32 of the page's keys, key 0 among
-      // them, so every row that sees the page has a finite reference).
+      // First page of the segment (the reference is still unset): each
+      // row's reference is its maximum over the page's 64 keys, from both
+      // key halves, so a sequence that fits in one page has its largest
+      // weight exactly 1.  On the other pages key tile 0's softmax runs
+      // between the key-tile-1 MFMAs.
+      const bool first = !kRedo && cpage == seg_page0;
       auto first_page_reference = [&]() __attribute__((always_inline)) {
-        if (!kRedo && cpage == seg_page0) {
 #pragma unroll
-          for (int rt = 0; rt < 2; ++rt) {
-            const float r = row_max4(xm[0][rt]);
-            if (grp4 == 0) sh.x[kh][32 * rh + 16 * rt + col] = r;
-            m_ref[rt] = r;
-          }
-          __syncthreads();
-#pragma unroll
-          for (int rt = 0; rt < 2; ++rt) m_ref[rt] = fmaxf(m_ref[rt], sh.x[kh ^ 1][32 * rh + 16 * rt + col]);
+        for (int rt = 0; rt < 2; ++rt) {
+          const float r = row_max4(fmaxf(xm[0][rt], xm[1][rt]));
+          if (grp4 == 0) sh.x[kh][32 * rh + 16 * rt + col] = r;
+          m_ref[rt] = r;
         }
+        __syncthreads();
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt) m_ref[rt] = fmaxf(m_ref[rt], sh.x[kh ^ 1][32 * rh + 16 * rt + col]);
       };
 
 #pragma unroll
@@ -470,12 +471,13 @@ __device__ __forceinline__ void decode_worker(const DecodeParams& p, char (*lds_
       auto sm0_step = [&]<int G>() __attribute__((always_inline)) {
         if constexpr (G == kQk / 2 - 1) {
           sm_load(0);
-          first_page_reference();
         } else if constexpr (G >= kQk / 2 + 1 && (G - kQk / 2 - 1) % 3 == 0 && (G - kQk / 2 - 1) / 3 < 6) {
           constexpr int st = (G - kQk / 2 - 1) / 3;
-          if constexpr (st == 0) sm_check(0);
-          else if constexpr (st <= 4) sm_exp(0, (st - 1) >> 1, 2 * ((st - 1) & 1));
-          else sm_write(0);
+          if (!first) {
+            if constexpr (st == 0) sm_check(0);
+            else if constexpr (st <= 4) sm_exp(0, (st - 1) >> 1, 2 * ((st - 1) & 1));
+            else sm_write(0);
+          }
         }
       };
       auto qk_step = [&]<int G>() __attribute__((always_inline)) {
@@ -498,8 +500,15 @@ __device__ __forceinline__ void decode_worker(const DecodeParams& p, char (*lds_
         if (lvalid) next_pid = ld_uniform(p.block_table + (size_t)lb * p.max_pages + lpage);
       }
 
-      // Key tile 1's softmax.
+      // Key tile 1's softmax (and, on the segment's first page, tile 0's).
       sm_load(1);
+      if (first) {
+        first_page_reference();
+        sm_check(0);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sm_exp(0, e >> 1, 2 * (e & 1));
+        sm_write(0);
+      }
       sm_check(1);
 #pragma unroll
       for (int e = 0; e < 4; ++e) sm_exp(1, e >> 1, 2 * (e & 1));
