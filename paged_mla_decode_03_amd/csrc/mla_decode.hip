@@ -385,8 +385,9 @@ __device__ __forceinline__ void decode_worker(const DecodeParams& p, char (*lds_
       constexpr int kQk = 2 * kKs * 2;           // 72 score MFMAs
       constexpr int kPv = 2 * 8 * 4;             // 64 output MFMAs
       constexpr int kKAhead = 4;
+      constexpr int kDmaStart = 0;               // DMA d follows MFMA kDmaStart + d * kDmaEvery
       constexpr int kDmaEvery = 5;
-      static_assert(kDmaEvery * (kLdsDmaPerWave - 1) < kQk + kPv, "every DMA inside the streams");
+      static_assert(kDmaStart + kDmaEvery * (kLdsDmaPerWave - 1) < kQk + kPv, "every DMA inside the streams");
       f32x4 s[2][2];
       bf16x8 kf[2 * kKs];
 
@@ -463,8 +464,8 @@ __device__ __forceinline__ void decode_worker(const DecodeParams& p, char (*lds_
       for (int r = 0; r < kKAhead; ++r) kf[r] = read_k(r / kKs, r % kKs);
       __builtin_amdgcn_sched_barrier(0);
       auto dma_step = [&]<int G>() __attribute__((always_inline)) {
-        if constexpr (G % kDmaEvery == 0 && G / kDmaEvery < kLdsDmaPerWave) {
-          if (dma) stage_tile(dma_rsrc, lane_src_off, row_stride_bytes, dma_dst, wave, G / kDmaEvery);
+        if constexpr (G >= kDmaStart && (G - kDmaStart) % kDmaEvery == 0 && (G - kDmaStart) / kDmaEvery < kLdsDmaPerWave) {
+          if (dma) stage_tile(dma_rsrc, lane_src_off, row_stride_bytes, dma_dst, wave, (G - kDmaStart) / kDmaEvery);
         }
       };
       // After score MFMA g (key tile 1): the stages of key tile 0's softmax.
