@@ -185,21 +185,21 @@ __device__ inline bool next_page(const int32_t* meta, const int32_t* seqlens, in
 
 // LDS of one decode workgroup besides the two page buffers: the softmax
 // weights P of the current page in the output MFMA's operand order, and one
-// float per (key half, row) for the row statistics the two key halves swap.
+// float per row for the row sums the output waves need.
 struct DecodeShared {
   char p[kPBytes];
-  float x[2][kRowsPerBlock];
+  float x[kRowsPerBlock];
 };
 
 // One worker's pages for latent head g and row block rb: every segment in the
 // worker's range [meta[0], meta[1]) .. [meta[2], meta[3]).
 //
-// Roles of the four waves.  Scores: wave w takes query rows 32*(w>>1) ..+31
-// (its Q, 32 x 576 bf16, sits in VGPRs) against keys 32*(w&1) ..+31 of each
-// page, so every K fragment it reads feeds two MFMAs.  Outputs: wave w owns
-// output columns 128w ..+127 for all 64 rows (O^T, 128 x 64 fp32, in 32
-// MFMA accumulators), reading P of all rows from LDS and V columns
-// 128w ..+127 only.  Per page the LDS reads are K 144 KB + V 64 KB + P 32 KB.
+// Roles of the four waves.  Scores and softmax: wave w takes query rows
+// 16w ..+15 (its Q, 16 x 576 bf16, sits in VGPRs) against all 64 keys of
+// each page, so a row's maximum and sum never leave its wave.  Outputs:
+// wave w owns output columns 128w ..+127 for all 64 rows (O^T, 128 x 64
+// fp32, in 32 MFMA accumulators), reading P of all rows from LDS and V
+// columns 128w ..+127 only.
 //
 // kSingleHead: h_kv == 1, so a page's rows are contiguous 1152-byte rows and
 // every stride is a compile-time constant.
@@ -215,8 +215,6 @@ __device__ __forceinline__ void decode_worker(const DecodeParams& p, char (*lds_
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
-  const int rh = wave >> 1;       // score rows 32rh .. 32rh+31
-  const int kh = wave & 1;        // score keys 32kh .. 32kh+31 of each page
   const int grp4 = lane >> 4;     // which 4-key / 8-wide k slice of an MFMA fragment
   const int col = lane & 15;      // row (or output column) within an MFMA tile
 
@@ -234,8 +232,21 @@ __device__ __forceinline__ void decode_worker(const DecodeParams& p, char (*lds_
   const char* kv_head = (const char*)p.kv + (size_t)g * kRowBytes;
   const uint32_t lane_src_off = (lane >> 3) * row_stride_bytes + ((lane & 7) ^ (lane >> 3)) * 16;
 
-  // The rows this lane serves.  Scores / softmax: rows 32rh + 16rt + col,
-  // rt = 0, 1.  Outputs: rows 16rt4 + col, rt4 = 0..3.
+  // Page-independent per-lane LDS offsets; a fragment read adds the page
+  // buffer's base and a compile-time offset below 64 KB.
+  //   K: row col (+16 per key tile), 16-byte chunk 4*par + grp4 (+8 per 2 k-steps).
+  //   V: row lane/4 (+16 per read), columns 128*wave + 16*m4 + 4*(lane%4) (+64 per 4 tiles).
+  //   P: row 16*wave + col (write) or col (read, +16 per row tile), chunk grp4 (+4 per k-step).
+  uint32_t kb_off[2], vb_off[4];
+#pragma unroll
+  for (int par = 0; par < 2; ++par) kb_off[par] = lds_tile_offset(col, 4 * par + grp4);
+#pragma unroll
+  for (int m4 = 0; m4 < 4; ++m4)
+    vb_off[m4] = wave * (2 * 1024) + lds_tile_offset(lane >> 2, 2 * m4 + ((lane & 3) >> 1)) + 8 * (lane & 1);
+  const uint32_t pw = lds_p + (16 * wave + col) * kPRowBytes + grp4 * 16;
+  const uint32_t pr = lds_p + col * kPRowBytes + grp4 * 16;
+
+  // Query row r of the block: its token and head.
   auto row_tok = [&](int r) __attribute__((always_inline)) {
     const int qrow = rb * kRowsPerBlock + r;
     return qrow < p.rows ? qrow / p.group : 0;
@@ -244,6 +255,7 @@ __device__ __forceinline__ void decode_worker(const DecodeParams& p, char (*lds_
     const int qrow = rb * kRowsPerBlock + r;
     return qrow < p.rows ? g * p.group + (qrow - (qrow / p.group) * p.group) : 0;
   };
+  const int srow = 16 * wave + col;    // this lane's score row
 
   // First page in flight before anything else; the id of the page after it
   // is read now, one page ahead of its DMAs.
@@ -266,35 +278,25 @@ __device__ __forceinline__ void decode_worker(const DecodeParams& p, char (*lds_
     const int slot = s0 + (b == meta_b0 ? ld_uniform(meta + 4) : 0);
     const int seg_page0 = cpage;
 
-    // Q fragments of the two score row tiles: lane (col, grp4) holds row
-    // 32rh + 16rt + col, dims 32*ks + 8*grp4 .. +7.
-    bf16x8 qf[2][kDqk / 32];
-    int n_vis[2];              // keys each of this lane's score rows may see
-    // Fewest keys any row of the block sees (causal rows: the block's first token).
-    const int n_vis_min = p.causal ? L - p.s_q + row_tok(0) + 1 : L;
-#pragma unroll
-    for (int rt = 0; rt < 2; ++rt) {
-      const int r = 32 * rh + 16 * rt + col;
-      const bool ok = rb * kRowsPerBlock + r < p.rows;
-      const int tok = row_tok(r);
-      n_vis[rt] = p.causal ? L - p.s_q + tok + 1 : L;
-      const uint16_t* qp = p.q + ((size_t)(b * p.s_q + tok) * p.h_q + row_head(r)) * kDqk + grp4 * 8;
+    // Q fragments of the score row: lane (col, grp4) holds dims 32*ks + 8*grp4 .. +7.
+    bf16x8 qf[kDqk / 32];
+    {
+      const bool ok = rb * kRowsPerBlock + srow < p.rows;
+      const uint16_t* qp = p.q + ((size_t)(b * p.s_q + row_tok(srow)) * p.h_q + row_head(srow)) * kDqk + grp4 * 8;
 #pragma unroll
       for (int ks = 0; ks < kDqk / 32; ++ks) {
         u32x4 v = ok ? *(const u32x4*)(qp + ks * 32) : u32x4{0, 0, 0, 0};
-        qf[rt][ks] = __builtin_bit_cast(bf16x8, v);
+        qf[ks] = __builtin_bit_cast(bf16x8, v);
       }
     }
-    float m_ref[2], m_seen[2], l_run[2];   // per score row, log2 units / this lane's share
-#pragma unroll
-    for (int rt = 0; rt < 2; ++rt) {
-      m_ref[rt] = kNegInf;
-      if constexpr (kRedo)
-        m_ref[rt] = p.redo_m[(size_t)redo_item * kRowsPerBlock + 32 * rh + 16 * rt + col];
-      m_seen[rt] = kNegInf;
-      l_run[rt] = 0.f;
-    }
-    int overflow = 0;          // a score rose more than kOverflowThreshold above its reference
+    const int n_vis = p.causal ? L - p.s_q + row_tok(srow) + 1 : L;   // keys the score row may see
+    // Fewest keys any row of the block sees (causal rows: the block's first token).
+    const int n_vis_min = p.causal ? L - p.s_q + row_tok(0) + 1 : L;
+    float m_ref = kNegInf;      // the score row's reference point (log2 units)
+    if constexpr (kRedo) m_ref = p.redo_m[(size_t)redo_item * kRowsPerBlock + srow];
+    float m_seen = kNegInf;     // largest score this lane has seen
+    float l_run = 0.f;          // this lane's share of sum_j 2^(s_j - m_ref)
+    int overflow = 0;           // a score rose more than kOverflowThreshold above the reference
 
     // Output tiles, zeroed from an MFMA so that they are born in the
     // accumulation registers.
@@ -328,34 +330,13 @@ __device__ __forceinline__ void decode_worker(const DecodeParams& p, char (*lds_
       const __amdgpu_buffer_rsrc_t dma_rsrc = page_resource(kv_head + (size_t)next_pid * page_stride_bytes, page_span);
       const uint32_t dma_dst = lds_base + ((it + 1) & 1) * kPageBytes;
 
-      // Per-lane LDS bases of this page's fragment reads; every read is one
-      // of them plus a compile-time offset below 64 KB.  They are formed
-      // here from the lane id rather than kept live across the loop, and the
-      // empty asm statements stop the compiler from hoisting them or turning
-      // base + offset into an OR that the DS immediate offset cannot absorb.
-      int ln = lane;
-      asm volatile("" : "+v"(ln));
       const uint32_t page_base = (uint32_t)(uintptr_t)buf;
-      uint32_t kb[2], vb[4], pw, pr;
+      uint32_t kb[2], vb[4];
 #pragma unroll
-      for (int par = 0; par < 2; ++par) {
-        // K row 32kh + (ln & 15) (+16 per key tile), chunk 4*par + (ln >> 4) (+8 per 2 k-steps)
-        kb[par] = page_base + kh * (4 * 9 * 1024) + lds_tile_offset(ln & 15, 4 * par + (ln >> 4));
-        asm volatile("" : "+v"(kb[par]));
-      }
+      for (int par = 0; par < 2; ++par) kb[par] = page_base + kb_off[par];
 #pragma unroll
-      for (int m4 = 0; m4 < 4; ++m4) {
-        // V row (ln >> 2) (+16 per read), columns 128*wave + 16*m4 + 4*(ln & 3) (+64 per 4 tiles)
-        vb[m4] = page_base + wave * (2 * 1024) + lds_tile_offset(ln >> 2, 2 * m4 + ((ln & 3) >> 1)) + 8 * (ln & 1);
-        asm volatile("" : "+v"(vb[m4]));
-      }
-      // P: row r at r * kPRowBytes; 16-byte chunk 4*kk + slot/8 of that row.
-      pw = lds_p + (32 * rh + (ln & 15)) * kPRowBytes + (4 * kh + (ln >> 4)) * 16;
-      pr = lds_p + (ln & 15) * kPRowBytes + (ln >> 4) * 16;
-      asm volatile("" : "+v"(pw));
-      asm volatile("" : "+v"(pr));
-
-      const int key0 = cpage * kPage + 32 * kh;
+      for (int m4 = 0; m4 < 4; ++m4) vb[m4] = page_base + vb_off[m4];
+      const int key0 = cpage * kPage;
 
       auto read_k = [&](int kt, int ks) __attribute__((always_inline)) {
         return *(lds_bf16x8*)(kb[ks & 1] + (uint32_t)((2 * kt * 9 + (ks >> 1)) * 1024));
@@ -377,89 +358,19 @@ __device__ __forceinline__ void decode_worker(const DecodeParams& p, char (*lds_
         return *(lds_bf16x8*)(pr + (uint32_t)(t * 16 * kPRowBytes + kk * 64));
       };
 
-      // ---- scores: S^T = K Q^T for key tiles kt = 0, 1 and row tiles rt = 0, 1 ----
-      // 72 MFMAs in issue order (kt, ks, rt); every K fragment feeds the two
-      // row tiles; reads run kKAhead fragments ahead; one DMA of the next
-      // page after every kDmaEvery-th MFMA of the page (scores and outputs).
+      // ---- scores: S^T = K Q^T for key tiles kt = 0..3 (16 keys each) ----
+      // 72 MFMAs in issue order (kt, ks), K fragments kKAhead reads ahead;
+      // one DMA of the next page after MFMA kDmaStart + d * kDmaEvery of the
+      // page (scores and outputs).
       constexpr int kKs = kDqk / 32;             // 18
-      constexpr int kQk = 2 * kKs * 2;           // 72 score MFMAs
+      constexpr int kQk = 4 * kKs;               // 72 score MFMAs
       constexpr int kPv = 2 * 8 * 4;             // 64 output MFMAs
-      constexpr int kKAhead = 4;
+      constexpr int kKAhead = 8;
       constexpr int kDmaStart = 0;               // DMA d follows MFMA kDmaStart + d * kDmaEvery
-      constexpr int kDmaEvery = 5;
+      constexpr int kDmaEvery = 4;
       static_assert(kDmaStart + kDmaEvery * (kLdsDmaPerWave - 1) < kQk + kPv, "every DMA inside the streams");
-      f32x4 s[2][2];
-      bf16x8 kf[2 * kKs];
-
-      // ---- softmax weights (base 2), elementwise against the row reference ----
-      // Lane (col, grp4) holds, for score row rt, key key0 + 16kt + 4*grp4 + i
-      // in s[kt][rt][i]; keys a row may not see get weight 0.  The work of key
-      // tile 0 runs in short stages between the key-tile-1 MFMAs; tile 1's
-      // runs after the stream.  Masking is needed only on a page that holds
-      // keys some row may not see (the sequence's last page, or causal rows).
-      const bool mask = key0 + 32 > n_vis_min;
-      float x[2][2][4], xm[2][2], mu[2];
-      uint32_t pk[2][2][2];
-      auto sm_load = [&](int kt) __attribute__((always_inline)) {
-#pragma unroll
-        for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) x[kt][rt][i] = s[kt][rt][i];
-        if (mask) {
-#pragma unroll
-          for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const int key = key0 + 16 * kt + 4 * grp4 + i;
-              x[kt][rt][i] = key < n_vis[rt] ? x[kt][rt][i] : kNegInf;
-            }
-        }
-        // Row maxima of this lane's 4 raw scores per row (the scale is > 0).
-#pragma unroll
-        for (int rt = 0; rt < 2; ++rt)
-          xm[kt][rt] = fmaxf(fmaxf(x[kt][rt][0], x[kt][rt][1]), fmaxf(x[kt][rt][2], x[kt][rt][3])) * p.scale_log2;
-      };
-      auto sm_check = [&](int kt) __attribute__((always_inline)) {
-#pragma unroll
-        for (int rt = 0; rt < 2; ++rt) {
-          // A row with no reference yet that sees a key here, or a score far
-          // above the reference, voids the segment's result for this pass.
-          overflow |= xm[kt][rt] > m_ref[rt] + kOverflowThreshold;
-          m_seen[rt] = fmaxf(m_seen[rt], xm[kt][rt]);
-          mu[rt] = m_ref[rt] == kNegInf ? 0.f : m_ref[rt];
-        }
-      };
-      auto sm_exp = [&](int kt, int rt, int i0) __attribute__((always_inline)) {
-        const float w0 = __builtin_amdgcn_exp2f(__builtin_fmaf(x[kt][rt][i0], p.scale_log2, -mu[rt]));
-        const float w1 = __builtin_amdgcn_exp2f(__builtin_fmaf(x[kt][rt][i0 + 1], p.scale_log2, -mu[rt]));
-        l_run[rt] += w0 + w1;
-        pk[kt][rt][i0 >> 1] = pack_bf16x2(w0, w1);
-      };
-      // Slots 8*grp4 + 4kt + i of row 32rh + 16rt + col, k-step kh, hold key 16kt + 4*grp4 + i.
-      auto sm_write = [&](int kt) __attribute__((always_inline)) {
-#pragma unroll
-        for (int rt = 0; rt < 2; ++rt)
-          *(__attribute__((address_space(3))) u32x2*)(pw + (uint32_t)(rt * 16 * kPRowBytes + kt * 8)) =
-              u32x2{pk[kt][rt][0], pk[kt][rt][1]};
-      };
-      // First page of the segment (the reference is still unset): each
-      // row's reference is its maximum over the page's 64 keys, from both
-      // key halves, so a sequence that fits in one page has its largest
-      // weight exactly 1.  On the other pages key tile 0's softmax runs
-      // between the key-tile-1 MFMAs.
-      const bool first = !kRedo && cpage == seg_page0;
-      auto first_page_reference = [&]() __attribute__((always_inline)) {
-#pragma unroll
-        for (int rt = 0; rt < 2; ++rt) {
-          const float r = row_max4(fmaxf(xm[0][rt], xm[1][rt]));
-          if (grp4 == 0) sh.x[kh][32 * rh + 16 * rt + col] = r;
-          m_ref[rt] = r;
-        }
-        __syncthreads();
-#pragma unroll
-        for (int rt = 0; rt < 2; ++rt) m_ref[rt] = fmaxf(m_ref[rt], sh.x[kh ^ 1][32 * rh + 16 * rt + col]);
-      };
-
+      f32x4 s[4];
+      bf16x8 kf[kQk];
 #pragma unroll
       for (int r = 0; r < kKAhead; ++r) kf[r] = read_k(r / kKs, r % kKs);
       __builtin_amdgcn_sched_barrier(0);
@@ -468,26 +379,12 @@ __device__ __forceinline__ void decode_worker(const DecodeParams& p, char (*lds_
           if (dma) stage_tile(dma_rsrc, lane_src_off, row_stride_bytes, dma_dst, wave, (G - kDmaStart) / kDmaEvery);
         }
       };
-      // After score MFMA g (key tile 1): the stages of key tile 0's softmax.
-      auto sm0_step = [&]<int G>() __attribute__((always_inline)) {
-        if constexpr (G == kQk / 2 - 1) {
-          sm_load(0);
-        } else if constexpr (G >= kQk / 2 + 1 && (G - kQk / 2 - 1) % 3 == 0 && (G - kQk / 2 - 1) / 3 < 6) {
-          constexpr int st = (G - kQk / 2 - 1) / 3;
-          if (!first) {
-            if constexpr (st == 0) sm_check(0);
-            else if constexpr (st <= 4) sm_exp(0, (st - 1) >> 1, 2 * ((st - 1) & 1));
-            else sm_write(0);
-          }
-        }
-      };
       auto qk_step = [&]<int G>() __attribute__((always_inline)) {
-        constexpr int r = G / 2, rt = G % 2, kt = r / kKs, ks = r % kKs;
-        const f32x4 c = ks == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : s[kt][rt];
-        s[kt][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[r], qf[rt][ks], c, 0, 0, 0);
-        if constexpr (rt == 1 && r + kKAhead < 2 * kKs) kf[r + kKAhead] = read_k((r + kKAhead) / kKs, (r + kKAhead) % kKs);
+        constexpr int kt = G / kKs, ks = G % kKs;
+        const f32x4 c = ks == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : s[kt];
+        s[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[G], qf[ks], c, 0, 0, 0);
+        if constexpr (G + kKAhead < kQk) kf[G + kKAhead] = read_k((G + kKAhead) / kKs, (G + kKAhead) % kKs);
         dma_step.template operator()<G>();
-        sm0_step.template operator()<G>();
         __builtin_amdgcn_sched_barrier(0);
       };
       [&]<int... G>(std::integer_sequence<int, G...>) __attribute__((always_inline)) {
@@ -501,25 +398,63 @@ __device__ __forceinline__ void decode_worker(const DecodeParams& p, char (*lds_
         if (lvalid) next_pid = ld_uniform(p.block_table + (size_t)lb * p.max_pages + lpage);
       }
 
-      // Key tile 1's softmax (and, on the segment's first page, tile 0's).
-      sm_load(1);
-      if (first) {
-        first_page_reference();
-        sm_check(0);
+      // ---- softmax weights (base 2) against the row reference ----
+      // Lane (col, grp4) holds, for the score row, key key0 + 16kt + 4*grp4 + i
+      // in s[kt][i].  Keys the row may not see get weight 0; masking is
+      // needed only on a page that holds such keys (the sequence's last page,
+      // or causal rows), a uniform test.
+      float x[4][4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) sm_exp(0, e >> 1, 2 * (e & 1));
-        sm_write(0);
+      for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) x[kt][i] = s[kt][i];
+      if (key0 + kPage > n_vis_min) {
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int key = key0 + 16 * kt + 4 * grp4 + i;
+            x[kt][i] = key < n_vis ? x[kt][i] : kNegInf;
+          }
       }
-      sm_check(1);
+      // This lane's maximum raw score (the scale is > 0), in log2 units.
+      float xm = kNegInf;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) sm_exp(1, e >> 1, 2 * (e & 1));
-      sm_write(1);
+      for (int kt = 0; kt < 4; ++kt)
+        xm = fmaxf(xm, fmaxf(fmaxf(x[kt][0], x[kt][1]), fmaxf(x[kt][2], x[kt][3])));
+      xm *= p.scale_log2;
+      if (!kRedo && cpage == seg_page0) {
+        // First page of the segment: the reference is the row's maximum over
+        // the page, so a sequence that fits in one page has its largest
+        // weight exactly 1.
+        m_ref = row_max4(xm);
+      }
+      // A row with no reference yet that sees a key here, or a score far
+      // above the reference, voids the segment's result for this pass.
+      overflow |= xm > m_ref + kOverflowThreshold;
+      m_seen = fmaxf(m_seen, xm);
+      const float mu = m_ref == kNegInf ? 0.f : m_ref;
+      uint32_t pk[4][2];
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const float w0 = __builtin_amdgcn_exp2f(__builtin_fmaf(x[kt][2 * h], p.scale_log2, -mu));
+          const float w1 = __builtin_amdgcn_exp2f(__builtin_fmaf(x[kt][2 * h + 1], p.scale_log2, -mu));
+          l_run += w0 + w1;
+          pk[kt][h] = pack_bf16x2(w0, w1);
+        }
+      // Slot 8*grp4 + 4*(kt&1) + i of k-step kk = kt>>1 holds key 16*(kt&1) + 4*grp4 + i.
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk)
+        *(__attribute__((address_space(3))) u32x4*)(pw + (uint32_t)(kk * 64)) =
+            u32x4{pk[2 * kk][0], pk[2 * kk][1], pk[2 * kk + 1][0], pk[2 * kk + 1][1]};
       __syncthreads();            // P of all 64 rows is in LDS
 
       // ---- outputs: O^T += V^T P^T, 8 column tiles x 4 row tiles per k-step ----
       // 64 MFMAs in issue order (kk, d, t); V fragments kVAhead ahead; the
       // four P fragments of a k-step read before its first MFMA.
-      constexpr int kVAhead = 2;
+      constexpr int kVAhead = 3;
       bf16x8 vf[2][8], pfr[2][4];
 #pragma unroll
       for (int t = 0; t < 4; ++t) pfr[0][t] = read_p(0, t);
@@ -547,75 +482,55 @@ __device__ __forceinline__ void decode_worker(const DecodeParams& p, char (*lds_
     }
 
     // ---------------- segment epilogue ----------------
-    // Every wave is past its last output MFMA before the exchanges below
-    // reuse sh.x; the page buffers are not touched here.
+    // Every wave is past its last output MFMA before sh.x is reused below;
+    // the page buffers are not touched here.
     const int ovf = __syncthreads_or(overflow);
     bool write_out = true;
     if constexpr (!kRedo) {
       // A segment where some row overflowed is recorded for the redo launch
-      // (with every row's maximum over both key halves) and leaves its
-      // outputs to it.  Every segment writes its flag, so stale flags never
-      // survive a call.
+      // (with every row's maximum) and leaves its outputs to it.  Every
+      // segment writes its flag, so stale flags never survive a call.
       const int item = (slot * p.h_kv + g) * p.row_blocks + rb;
       if (tid == 0) p.redo_flag[item] = ovf;
       if (ovf) {
-#pragma unroll
-        for (int rt = 0; rt < 2; ++rt) {
-          const float r = row_max4(m_seen[rt]);
-          if (grp4 == 0) sh.x[kh][32 * rh + 16 * rt + col] = r;
-        }
-        __syncthreads();
+        const float r = row_max4(m_seen);
         if (tid < kMetaInts) {
           const int rec[kMetaInts] = {b, seg_page0, b, cend, slot - s0, 0, 0, 0};
           p.redo_meta[(size_t)item * kMetaInts + tid] = rec[tid];
         }
-        if (tid < kRowsPerBlock)
-          p.redo_m[(size_t)item * kRowsPerBlock + tid] = fmaxf(sh.x[0][tid], sh.x[1][tid]);
-        __syncthreads();
+        if (grp4 == 0) p.redo_m[(size_t)item * kRowsPerBlock + srow] = r;
         write_out = false;
       }
     }
     if (write_out) {
-      // Row sums: each score wave's share over its key half, then both halves.
-#pragma unroll
-      for (int rt = 0; rt < 2; ++rt) {
-        const float l = row_sum4(l_run[rt]);
-        if (grp4 == 0) sh.x[kh][32 * rh + 16 * rt + col] = l;
-      }
-      __syncthreads();
-      // LSE of the score rows, written by the key-half-0 waves.
-      if (kh == 0 && grp4 == 0) {
-#pragma unroll
-        for (int rt = 0; rt < 2; ++rt) {
-          const int r = 32 * rh + 16 * rt + col;
-          const int qrow = rb * kRowsPerBlock + r;
-          const float l = sh.x[0][r] + sh.x[1][r];
-          const float lse_nat = l == 0.f ? kNegInf : (m_ref[rt] + __log2f(l)) * 0.69314718055994531f;
-          if (qrow < p.rows) {
-            if (nsplit == 1)
-              p.lse[((size_t)b * p.h_q + row_head(r)) * p.s_q + row_tok(r)] = lse_nat;
-            else
-              p.ws_lse[(size_t)(slot * p.h_kv + g) * p.rows + qrow] = lse_nat;
-          }
+      // Row sums, swapped through LDS for the output waves.
+      const float l_row = row_sum4(l_run);
+      if (grp4 == 0) {
+        sh.x[srow] = l_row;
+        const int qrow = rb * kRowsPerBlock + srow;
+        const float lse_nat = l_row == 0.f ? kNegInf : (m_ref + __log2f(l_row)) * 0.69314718055994531f;
+        if (qrow < p.rows) {
+          if (nsplit == 1)
+            p.lse[((size_t)b * p.h_q + row_head(srow)) * p.s_q + row_tok(srow)] = lse_nat;
+          else
+            p.ws_lse[(size_t)(slot * p.h_kv + g) * p.rows + qrow] = lse_nat;
         }
       }
+      __syncthreads();
       // O: lane (col, grp4) holds O[16t + col][128*wave + 16d + 4*grp4 + i] in acc[d][t][i].
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         const int r = 16 * t + col;
         const int qrow = rb * kRowsPerBlock + r;
-        const float l = sh.x[0][r] + sh.x[1][r];
+        const float l = sh.x[r];
         const float inv = l == 0.f ? 0.f : 1.f / l;
         if (qrow < p.rows) {
           if (nsplit == 1) {
             uint16_t* op = p.o + ((size_t)(b * p.s_q + row_tok(r)) * p.h_q + row_head(r)) * kDv + 128 * wave + 4 * grp4;
 #pragma unroll
-            for (int d = 0; d < 8; ++d) {
-              uint2 v;
-              v.x = pack_bf16x2(acc[d][t][0] * inv, acc[d][t][1] * inv);
-              v.y = pack_bf16x2(acc[d][t][2] * inv, acc[d][t][3] * inv);
-              *(uint2*)(op + 16 * d) = v;
-            }
+            for (int d = 0; d < 8; ++d)
+              *(u32x2*)(op + 16 * d) = u32x2{pack_bf16x2(acc[d][t][0] * inv, acc[d][t][1] * inv),
+                                             pack_bf16x2(acc[d][t][2] * inv, acc[d][t][3] * inv)};
           } else {
             float* wp = p.ws_o + ((size_t)(slot * p.h_kv + g) * p.rows + qrow) * kDv + 128 * wave + 4 * grp4;
 #pragma unroll
@@ -624,6 +539,8 @@ __device__ __forceinline__ void decode_worker(const DecodeParams& p, char (*lds_
         }
       }
     }
+    // The next segment's first page barrier orders these sh.x reads before
+    // that segment rewrites it.
 
     // Next segment: the sequence after this one in the worker's range.
     if (cb == meta_b1) break;
