@@ -1,9 +1,8 @@
 """Benchmark of one paged MLA decode step on one MI355X.
 
-A step is the whole hot path over one batch: the split-KV decode kernel, the
-redo launch (which recomputes overflowed splits and for these inputs only
-scans their flags) and the log-sum-exp combine (the scheduler metadata is
-computed once per batch of sequence lengths and timed separately).  Inputs are seeded synthetic bf16
+A step is the whole hot path over one batch: the split-KV decode kernel and
+the log-sum-exp combine (the scheduler metadata is computed once per batch of
+sequence lengths and timed separately).  Inputs are seeded synthetic bf16
 tensors resident in HBM before timing starts.  Successive steps alternate
 between independent KV pools whose total exceeds the 256 MB Infinity Cache,
 so every step streams its cache from HBM.
@@ -44,6 +43,9 @@ def parse():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=15.0)
+    ap.add_argument("--copy-mb", type=int, default=0,
+                    help="before the timed steps, run one plain device copy of this many MiB: the known-size "
+                         "kernel that scales the decode kernel's HBM counters in a rocprofv3 --pmc run")
     return ap.parse_args()
 
 
@@ -104,8 +106,8 @@ def main():
     import torch
 
     sys.path.insert(0, ROOT)
-    from paged_mla_decode_03_amd import (DecodeBuffers, get_mla_metadata, mla_combine_splits,
-                                         mla_decode_redo, mla_decode_splitkv)
+    from paged_mla_decode_03_amd import (DecodeBuffers, get_mla_metadata, mla_combine_splits, mla_decode_paged,
+                                         mla_decode_splitkv)
     from workloads import WORKLOADS, algorithmic_counts, make_inputs
 
     dev = torch.device("cuda", 0)
@@ -138,39 +140,56 @@ def main():
     W = meta.shape[0]
     buf = DecodeBuffers(q, pools[0], 512, W)
 
-    # The three launches of one step, each bracketed by events on the stream
-    # they run on (torch's current stream, which the binding launches on).
-    def step(i, evs=None):
+    # One step: mla_decode_paged, one call that launches the decode and the
+    # combine kernel on torch's current stream (which the binding launches on).
+    def step(i):
+        mla_decode_paged(q, pools[i % n_pools], bt, seqlens, 512, meta, ns, causal=w.causal, buffers=buf)
+
+    # The same two launches through their own entry points, each bracketed by
+    # events (used only outside the timed loop: an event between launches
+    # widens the gap).
+    def split_step(i, evs):
         kv = pools[i % n_pools]
-        if evs:
-            evs[0].record()
+        evs[0].record()
         mla_decode_splitkv(q, kv, bt, seqlens, 512, meta, ns, causal=w.causal, buffers=buf)
-        if evs:
-            evs[1].record()
-        mla_decode_redo(q, kv, bt, seqlens, 512, meta, ns, causal=w.causal, buffers=buf)
-        if evs:
-            evs[2].record()
+        evs[1].record()
         mla_combine_splits(ns, w.s_q, w.h_q, w.h_kv, 512, W, buf)
-        if evs:
-            evs[3].record()
+        evs[2].record()
 
     print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
+    if args.copy_mb > 0:
+        src = torch.empty(args.copy_mb << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    # The timed steps: launches only, between a synchronize and a pair of
+    # events on each side.
+    g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_start = time.perf_counter()
+    g0.record()
     for i in range(args.steps):
-        step(i, evs[i])
+        step(i)
+    g1.record()
     torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - t_start) * 1e3
-    decode_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
-    redo_ms = np.array([e[1].elapsed_time(e[2]) for e in evs])
-    combine_ms = np.array([e[2].elapsed_time(e[3]) for e in evs])
-    step_ms = np.array([e[0].elapsed_time(e[3]) for e in evs])
     ms_per_step = wall_ms / args.steps
+    event_ms_per_step = g0.elapsed_time(g1) / args.steps
+
+    # Per-launch split of a step, from separate steps with events between the
+    # launches (outside the timed loop).
+    n_split = min(args.steps, 10)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n_split)]
+    for i in range(n_split):
+        split_step(i, evs[i])
+    torch.cuda.synchronize()
+    decode_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
+    combine_ms = np.array([e[1].elapsed_time(e[2]) for e in evs])
 
     # The decode kernel alone, launched back to back between two events on
     # its stream: the average is the kernel's own duration plus one dispatch
@@ -184,9 +203,10 @@ def main():
     d1.record()
     torch.cuda.synchronize()
     decode_b2b_ms = d0.elapsed_time(d1) / n_dec
-    print(f"[bench] {args.steps} steps: {ms_per_step * 1e3:.1f} us/step (wall), decode kernel "
-          f"{decode_ms.mean() * 1e3:.1f} us in step ({decode_b2b_ms * 1e3:.1f} us back to back), redo scan "
-          f"{redo_ms.mean() * 1e3:.1f} us, combine {combine_ms.mean() * 1e3:.1f} us", file=sys.stderr, flush=True)
+    print(f"[bench] {args.steps} steps: {ms_per_step * 1e3:.1f} us/step (wall), "
+          f"{event_ms_per_step * 1e3:.1f} us/step (events), decode kernel "
+          f"{decode_ms.mean() * 1e3:.1f} us in step ({decode_b2b_ms * 1e3:.1f} us back to back), "
+          f"combine {combine_ms.mean() * 1e3:.1f} us", file=sys.stderr, flush=True)
 
     gbs = counts["total_bytes"] / (ms_per_step * 1e-3) / 1e9
     tflops = counts["flops"] / (ms_per_step * 1e-3) / 1e12
@@ -220,9 +240,8 @@ def main():
         "mfma_frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
         "decode_kernel_us": round(decode_b2b_ms * 1e3, 2),
         "decode_in_step_us": round(decode_ms.mean() * 1e3, 2),
-        "redo_kernel_us": round(redo_ms.mean() * 1e3, 2),
         "combine_kernel_us": round(combine_ms.mean() * 1e3, 2),
-        "step_event_us_p10_p50_p90": [round(float(np.percentile(step_ms, p)) * 1e3, 2) for p in (10, 50, 90)],
+        "step_event_us": round(event_ms_per_step * 1e3, 2),
         "metadata_us": round(metadata_us, 2),
         "algorithmic_bytes": counts["total_bytes"],
         "algorithmic_flops": counts["flops"],

@@ -94,12 +94,10 @@ int mla_get_metadata(const int32_t* cache_seqlens, int batch, int rows_per_kv, i
                      void* stream);
 
 /* Bytes of workspace mla_decode_paged needs.  With slots = num_workers +
- * batch, rows = s_q*h_q/h_kv and items = slots * h_kv * ceil(rows/64), the
- * workspace holds, each part rounded up to 256 bytes: fp32 split partials
- * O_s [slots][h_kv][rows][dv], fp32 lse_s [slots][h_kv][rows], then the
- * overflow records (int32 flags [items], int32 [items][8], fp32
- * [items][64]).  Returns 0 for invalid sizes.  Its contents need no
- * initialisation: every call writes what it later reads. */
+ * batch and rows = s_q*h_q/h_kv, the workspace holds, each part rounded up
+ * to 256 bytes: fp32 split partials O_s [slots][h_kv][rows][dv], then fp32
+ * lse_s [slots][h_kv][rows].  Returns 0 for invalid sizes.  Its contents
+ * need no initialisation: every call writes what it later reads. */
 size_t mla_workspace_bytes(int batch, int s_q, int h_q, int h_kv, int dv, int num_workers);
 
 /* Paged MLA decode: split-KV attention over the paged latent cache followed
@@ -119,10 +117,11 @@ size_t mla_workspace_bytes(int batch, int s_q, int h_q, int h_kv, int dv, int nu
  *   o              [dev] bf16 [batch][s_q][h_q][dv], 16-byte aligned
  *   lse            [dev] fp32 [batch][h_q][s_q], natural log, scale included
  *   workspace      [dev] >= mla_workspace_bytes(...) bytes, 256-byte aligned
- * Launches on `stream`: the decode kernel, a one-workgroup kernel that
- * recomputes any split whose scores rose more than 2^48 (log2 units) above
- * the reference the decode kernel took from the split's first 32 keys
- * (it finds none for ordinary inputs), and the combine kernel. */
+ * Launches on `stream`: the decode kernel, then the combine kernel.  Each
+ * workgroup of the decode kernel weighs keys against a per-row reference
+ * taken from the first page of its split; should a later score rise more
+ * than 48 (log2 units) above it, the workgroup runs that split again with
+ * each row's maximum as the reference (ordinary inputs never need this). */
 int mla_decode_paged(const void* q, const void* kvcache, const int32_t* block_table,
                      int max_pages_per_seq, int num_pages, const int32_t* cache_seqlens,
                      int batch, int s_q, int h_q, int h_kv, int d_qk, int dv,
@@ -132,10 +131,7 @@ int mla_decode_paged(const void* q, const void* kvcache, const int32_t* block_ta
 
 /* The first launch of mla_decode_paged alone: the split-KV decode kernel.
  * It writes o/lse of every sequence that has exactly one split and fp32
- * partials of the others into the workspace -- except splits it flags as
- * overflowed (a score more than 2^48, in base-2 weight units, above the
- * reference the kernel took from the split's first 32 keys), whose outputs
- * it leaves to mla_decode_redo.  Same arguments and checks as
+ * partials of the others into the workspace.  Same arguments and checks as
  * mla_decode_paged. */
 int mla_decode_splitkv(const void* q, const void* kvcache, const int32_t* block_table,
                        int max_pages_per_seq, int num_pages, const int32_t* cache_seqlens,
@@ -143,19 +139,6 @@ int mla_decode_splitkv(const void* q, const void* kvcache, const int32_t* block_
                        const int32_t* tile_scheduler_metadata, const int32_t* num_splits,
                        int num_workers, int causal, float softmax_scale, void* o, float* lse,
                        void* workspace, size_t workspace_bytes, void* stream);
-
-/* The second launch alone, to follow mla_decode_splitkv with the same
- * arguments on the same stream: one workgroup scans the split flags that
- * mla_decode_splitkv wrote into the workspace and recomputes every flagged
- * split, with each query row's reference set to its maximum score over the
- * split (recorded by the first launch), writing what mla_decode_splitkv
- * would have written.  With no flagged split it only reads the flags. */
-int mla_decode_redo(const void* q, const void* kvcache, const int32_t* block_table,
-                    int max_pages_per_seq, int num_pages, const int32_t* cache_seqlens,
-                    int batch, int s_q, int h_q, int h_kv, int d_qk, int dv,
-                    const int32_t* tile_scheduler_metadata, const int32_t* num_splits,
-                    int num_workers, int causal, float softmax_scale, void* o, float* lse,
-                    void* workspace, size_t workspace_bytes, void* stream);
 
 /* The last launch alone: the log-sum-exp merge.  For each sequence with
  * n_b = num_splits[b+1] - num_splits[b] partials: n_b = 0 writes O = 0 and

@@ -61,7 +61,7 @@ def _load():
     lib.mla_workspace_bytes.argtypes = [c_int, c_int, c_int, c_int, c_int, c_int]
     decode_args = [vp, vp, vp, c_int, c_int, vp, c_int, c_int, c_int, c_int, c_int, c_int,
                    vp, vp, c_int, c_int, c_float, vp, vp, vp, c_size_t, vp]
-    for name in ("mla_decode_paged", "mla_decode_splitkv", "mla_decode_redo"):
+    for name in ("mla_decode_paged", "mla_decode_splitkv"):
         f = getattr(lib, name)
         f.restype = c_int
         f.argtypes = decode_args
@@ -192,18 +192,6 @@ def mla_decode_splitkv(q, kvcache, block_table, cache_seqlens, dv, tile_schedule
     if buffers is None:
         buffers = DecodeBuffers(q, kvcache, dv, tile_scheduler_metadata.shape[0])
     _decode_call("mla_decode_splitkv", q, kvcache, block_table, cache_seqlens, dv, tile_scheduler_metadata,
-                 num_splits, causal, softmax_scale, buffers.o, buffers.lse, buffers.workspace)
-    return buffers
-
-
-def mla_decode_redo(q, kvcache, block_table, cache_seqlens, dv, tile_scheduler_metadata, num_splits,
-                    causal=False, softmax_scale=None, buffers: Optional[DecodeBuffers] = None):
-    """The redo launch alone (second launch of mla_decode_paged): recomputes the
-    splits mla_decode_splitkv flagged as overflowed; same arguments and buffers."""
-    _validate(q, kvcache, block_table, cache_seqlens, tile_scheduler_metadata, num_splits)
-    if buffers is None:
-        raise ValueError("mla_decode_redo needs the buffers mla_decode_splitkv wrote")
-    _decode_call("mla_decode_redo", q, kvcache, block_table, cache_seqlens, dv, tile_scheduler_metadata,
                  num_splits, causal, softmax_scale, buffers.o, buffers.lse, buffers.workspace)
     return buffers
 

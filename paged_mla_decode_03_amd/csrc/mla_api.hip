@@ -49,24 +49,18 @@ int check_shape(int batch, int s_q, int h_q, int h_kv, int dv, Shape* s) {
 }
 
 // Workspace layout (each part 256-byte aligned): split partials O [W+B][h_kv][R][512]
-// and LSE [W+B][h_kv][R] (fp32), then the redo records of the overflow path:
-// flags [items], one-segment worker rows [items][8], row maxima [items][64],
-// items = (W+B) * h_kv * row_blocks.
+// and LSE [W+B][h_kv][R] (fp32).
 struct WsLayout {
-  size_t lse, flag, meta, m, total;
+  size_t lse, total;
 };
 
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
 WsLayout ws_layout(const Shape& s, int num_workers) {
   const size_t slots = (size_t)num_workers + s.batch;
-  const size_t items = slots * s.h_kv * row_blocks_of(s.rows);
   WsLayout w;
   w.lse = align256(slots * s.h_kv * s.rows * MLA_D_V * 4);
-  w.flag = w.lse + align256(slots * s.h_kv * s.rows * 4);
-  w.meta = w.flag + align256(items * 4);
-  w.m = w.meta + align256(items * mla::kMetaInts * 4);
-  w.total = w.m + align256(items * mla::kRowsPerBlock * 4);
+  w.total = w.lse + align256(slots * s.h_kv * s.rows * 4);
   return w;
 }
 
@@ -109,9 +103,6 @@ mla::DecodeParams decode_params(const void* q, const void* kvcache, const int32_
   char* ws = (char*)workspace;
   p.ws_o = (float*)ws;
   p.ws_lse = (float*)(ws + w.lse);
-  p.redo_flag = (int32_t*)(ws + w.flag);
-  p.redo_meta = (int32_t*)(ws + w.meta);
-  p.redo_m = (float*)(ws + w.m);
   p.batch = s.batch;
   p.s_q = s.s_q;
   p.h_q = s.h_q;
@@ -134,14 +125,6 @@ int launch_decode(const mla::DecodeParams& p, hipStream_t stream) {
     hipLaunchKernelGGL(mla::mla_decode_kernel<true>, dim3(blocks), dim3(mla::kThreads), 0, stream, p);
   else
     hipLaunchKernelGGL(mla::mla_decode_kernel<false>, dim3(blocks), dim3(mla::kThreads), 0, stream, p);
-  return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_HIP;
-}
-
-int launch_redo(const mla::DecodeParams& p, hipStream_t stream) {
-  if (p.h_kv == 1)
-    hipLaunchKernelGGL(mla::mla_redo_kernel<true>, dim3(1), dim3(mla::kThreads), 0, stream, p);
-  else
-    hipLaunchKernelGGL(mla::mla_redo_kernel<false>, dim3(1), dim3(mla::kThreads), 0, stream, p);
   return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
 
@@ -234,21 +217,6 @@ int mla_decode_splitkv(const void* q, const void* kvcache, const int32_t* block_
   return launch_decode(p, (hipStream_t)stream);
 }
 
-int mla_decode_redo(const void* q, const void* kvcache, const int32_t* block_table, int max_pages_per_seq,
-                    int num_pages, const int32_t* cache_seqlens, int batch, int s_q, int h_q, int h_kv,
-                    int d_qk, int dv, const int32_t* meta, const int32_t* num_splits, int num_workers,
-                    int causal, float softmax_scale, void* o, float* lse, void* workspace,
-                    size_t workspace_bytes_given, void* stream) {
-  Shape s;
-  int st = check_decode(q, kvcache, block_table, max_pages_per_seq, num_pages, cache_seqlens, batch, s_q, h_q,
-                        h_kv, d_qk, dv, meta, num_splits, num_workers, causal, o, lse, workspace,
-                        workspace_bytes_given, &s);
-  if (st != MLA_OK) return st;
-  const mla::DecodeParams p = decode_params(q, kvcache, block_table, max_pages_per_seq, cache_seqlens, s, meta,
-                                            num_splits, num_workers, causal, softmax_scale, o, lse, workspace);
-  return launch_redo(p, (hipStream_t)stream);
-}
-
 int mla_combine_splits(const int32_t* num_splits, int batch, int s_q, int h_q, int h_kv, int dv,
                        int num_workers, void* o, float* lse, const void* workspace, size_t workspace_bytes_given,
                        void* stream) {
@@ -277,8 +245,6 @@ int mla_decode_paged(const void* q, const void* kvcache, const int32_t* block_ta
   const mla::DecodeParams p = decode_params(q, kvcache, block_table, max_pages_per_seq, cache_seqlens, s, meta,
                                             num_splits, num_workers, causal, softmax_scale, o, lse, workspace);
   st = launch_decode(p, (hipStream_t)stream);
-  if (st != MLA_OK) return st;
-  st = launch_redo(p, (hipStream_t)stream);
   if (st != MLA_OK) return st;
   return launch_combine(p, (hipStream_t)stream);
 }

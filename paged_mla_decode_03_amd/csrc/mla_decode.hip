@@ -12,32 +12,32 @@
 //     page range the scheduler gave its worker.  The workgroups that serve
 //     the other row blocks of the same head read the same pages; they are
 //     dispatched back to back on the same XCD so the second read hits L2.
-//   * Wave v owns query rows 16v..16v+15.  Its absorbed Q (16 x 576 bf16) sits
-//     in VGPRs as MFMA B fragments for the whole segment; its output
-//     O^T (512 x 16 fp32) sits in 32 v_mfma_f32_16x16x32_bf16 accumulators
-//     (128 accumulation registers).
-//   * A page is processed as two k-steps of 32 keys.  Per k-step: S^T = K Q^T
-//     for two 16-key tiles (A = K rows from LDS, B = Q), the softmax weights
-//     in the accumulator layout (each lane holds 4 keys of one query row),
-//     then O^T += V^T P^T (A = V columns read with the transposing
-//     ds_read_b64_tr_b16, B = P taken straight from the S^T accumulators).
+//   * Scores: wave v takes query rows 16v..16v+15 against all 64 keys of a
+//     page.  Its absorbed Q (16 x 576 bf16) sits in VGPRs as MFMA B
+//     fragments for the whole segment; S^T = K Q^T is 4 key tiles x 18
+//     k-steps of v_mfma_f32_16x16x32_bf16 with K fragments read from LDS.
+//   * Softmax in the score accumulators' layout (each lane holds 4 keys of
+//     one row, 16 per page), row maxima and sums with lane permutes; the
+//     bf16 weights P go to LDS.
+//   * Outputs: wave v owns output columns 128v..128v+127 for all 64 rows,
+//     O^T += V^T P^T (A = V columns read with the transposing
+//     ds_read_b64_tr_b16, B = P from LDS), 32 accumulators (128 registers)
+//     that only MFMAs touch.
 //   * Pages move HBM -> LDS with buffer_load_dwordx4 ... lds (no VGPR
 //     staging; the buffer resource bounds every read to the page), double
-//     buffered: page i+1 is in flight while page i is computed.  The page
-//     sits in LDS as 72 tiles of 1 KB (8 rows x 8 chunks of 16 bytes) with the
-//     16-byte chunks XOR-swizzled by row inside a tile.
+//     buffered: page i+1's 72 DMAs go out one by one between page i's MFMAs.
+//     The page sits in LDS as 72 tiles of 1 KB (8 rows x 8 chunks of 16
+//     bytes) with the 16-byte chunks XOR-swizzled by row inside a tile.
 //   * Softmax runs in base 2 with the scale folded into one multiply.  Each
 //     row keeps a reference point m (its maximum over the segment's first
-//     k-step) and accumulates unnormalised weights 2^(s - m) <= 2^48; that is
+//     page) and accumulates unnormalised weights 2^(s - m) <= 2^48; that is
 //     exact math, and bf16/fp32 have the range for it (sums stay below 2^65
 //     times the largest cached value for 2^17 keys).  The output tile is
-//     therefore never rescaled: only MFMAs touch it, which keeps it in the
-//     accumulation registers with no copies.  Should a later k-step exceed a
-//     row's reference by more than 48, the segment is void: the workgroup
-//     records it, with every row's maximum over the segment, and a second
-//     launch of one workgroup recomputes it with those maxima as references,
-//     where no weight exceeds 1.  For attention scores of any ordinary spread
-//     nothing is recorded and the second launch only scans the flags.
+//     therefore never rescaled.  Should a later page exceed a row's
+//     reference by more than 48, the pass is void and the workgroup runs the
+//     segment again with each row's maximum over the segment as its
+//     reference, where no weight exceeds 1.  For attention scores of any
+//     ordinary spread the second pass never runs.
 //   * Keys a query may not see (tail slots of the last page, causal future)
 //     get weight 0, and tail rows of the last page are zeroed in LDS so that
 //     whatever the cache holds there never reaches O.
@@ -104,12 +104,15 @@ __device__ inline __amdgpu_buffer_rsrc_t page_resource(const char* page_head, ui
 }
 
 // DMA number k (0 .. kLdsDmaPerWave-1) of this wave for one page: tile
-// j = 4k + wave, i.e. rows 8a..8a+7 x chunks 8b..8b+7 with j = 9a + b.
+// j = 18 * wave + k, i.e. rows 8a..8a+7 x chunks 8b..8b+7 with j = 9a + b,
+// so a = 2 * wave + k / 9 and b = k % 9.  Both addresses are a per-wave base
+// plus a compile-time offset (k is a constant in every call), which keeps the
+// 18 DMAs of a page from holding 36 scalar registers across the page loop.
 __device__ inline void stage_tile(__amdgpu_buffer_rsrc_t rsrc, uint32_t lane_off, int row_stride_bytes,
                                   uint32_t lds_dst, int wave, int k) {
-  const int j = k * kWaves + wave;            // tile index 9a + b, wave-uniform
-  const int a = j / 9, b = j - (j / 9) * 9;
-  const uint32_t m0 = lds_dst + j * 1024;
+  static_assert(kLdsDmaPerWave == 18, "two 8-row tile rows per wave");
+  const int a = 2 * wave + k / 9, b = k % 9;
+  const uint32_t m0 = lds_dst + (uint32_t)(wave * kLdsDmaPerWave * 1024) + (uint32_t)(k * 1024);
   const uint32_t soff = a * 8 * row_stride_bytes + b * 128;
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
                :
@@ -203,13 +206,13 @@ struct DecodeShared {
 //
 // kSingleHead: h_kv == 1, so a page's rows are contiguous 1152-byte rows and
 // every stride is a compile-time constant.
-// kRedo: the worker is one segment that overflowed in the first launch
-// (meta is its redo record); each row starts from the reference point
-// recorded for it, which is its maximum score over the segment.
-template <bool kSingleHead, bool kRedo>
+//
+// A segment whose scores rose too far above their reference (see the
+// softmax below) is run a second time by the same workgroup, with each row's
+// maximum over the segment as its reference.
+template <bool kSingleHead>
 __device__ __forceinline__ void decode_worker(const DecodeParams& p, char (*lds_page)[kPageBytes],
-                                              DecodeShared& sh, const int32_t* meta, int g, int rb,
-                                              int redo_item) {
+                                              DecodeShared& sh, const int32_t* meta, int g, int rb) {
   const uint32_t lds_base = (uint32_t)(uintptr_t)&lds_page[0][0];   // LDS byte address
   const uint32_t lds_p = (uint32_t)(uintptr_t)&sh.p[0];
   const int tid = threadIdx.x;
@@ -257,6 +260,22 @@ __device__ __forceinline__ void decode_worker(const DecodeParams& p, char (*lds_
   };
   const int srow = 16 * wave + col;    // this lane's score row
 
+  // Q fragments of the score row for sequence b: lane (col, grp4) holds dims
+  // 32*ks + 8*grp4 .. +7.
+  bf16x8 qf[kDqk / 32];
+  auto load_q = [&](int b) __attribute__((always_inline)) {
+    const bool ok = rb * kRowsPerBlock + srow < p.rows;
+    const uint16_t* qp = p.q + ((size_t)(b * p.s_q + row_tok(srow)) * p.h_q + row_head(srow)) * kDqk + grp4 * 8;
+#pragma unroll
+    for (int ks = 0; ks < kDqk / 32; ++ks) {
+      u32x4 v = ok ? *(const u32x4*)(qp + ks * 32) : u32x4{0, 0, 0, 0};
+      qf[ks] = __builtin_bit_cast(bf16x8, v);
+    }
+  };
+  // The first segment's Q needs only the worker's first sequence: its loads
+  // go out before the chain of table reads that locates the first page.
+  load_q(cb);
+
   // First page in flight before anything else; the id of the page after it
   // is read now, one page ahead of its DMAs.
   int next_pid = 0;
@@ -269,6 +288,7 @@ __device__ __forceinline__ void decode_worker(const DecodeParams& p, char (*lds_
   }
 
   int it = 0;
+  bool first_segment = true;
   while (true) {
     // ---------------- segment: pages [cpage, cend) of sequence cb ----------------
     const int b = cb;
@@ -277,232 +297,231 @@ __device__ __forceinline__ void decode_worker(const DecodeParams& p, char (*lds_
     const int nsplit = ld_uniform(p.num_splits + b + 1) - s0;
     const int slot = s0 + (b == meta_b0 ? ld_uniform(meta + 4) : 0);
     const int seg_page0 = cpage;
-
-    // Q fragments of the score row: lane (col, grp4) holds dims 32*ks + 8*grp4 .. +7.
-    bf16x8 qf[kDqk / 32];
-    {
-      const bool ok = rb * kRowsPerBlock + srow < p.rows;
-      const uint16_t* qp = p.q + ((size_t)(b * p.s_q + row_tok(srow)) * p.h_q + row_head(srow)) * kDqk + grp4 * 8;
-#pragma unroll
-      for (int ks = 0; ks < kDqk / 32; ++ks) {
-        u32x4 v = ok ? *(const u32x4*)(qp + ks * 32) : u32x4{0, 0, 0, 0};
-        qf[ks] = __builtin_bit_cast(bf16x8, v);
-      }
-    }
+    if (!first_segment) load_q(b);
+    first_segment = false;
     const int n_vis = p.causal ? L - p.s_q + row_tok(srow) + 1 : L;   // keys the score row may see
     // Fewest keys any row of the block sees (causal rows: the block's first token).
     const int n_vis_min = p.causal ? L - p.s_q + row_tok(0) + 1 : L;
     float m_ref = kNegInf;      // the score row's reference point (log2 units)
-    if constexpr (kRedo) m_ref = p.redo_m[(size_t)redo_item * kRowsPerBlock + srow];
-    float m_seen = kNegInf;     // largest score this lane has seen
-    float l_run = 0.f;          // this lane's share of sum_j 2^(s_j - m_ref)
-    int overflow = 0;           // a score rose more than kOverflowThreshold above the reference
-
-    // Output tiles, zeroed from an MFMA so that they are born in the
-    // accumulation registers.
+    bool second_pass = false;   // rerun with m_ref = the row's maximum over the segment
+    float m_seen, l_run;        // largest score this lane has seen; its share of sum_j 2^(s_j - m_ref)
+    int overflow;               // a score rose more than kOverflowThreshold above the reference
     f32x4 acc[8][4];
-    {
-      const bf16x8 zero8 = __builtin_bit_cast(bf16x8, u32x4{0, 0, 0, 0});
-      const f32x4 zero4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(zero8, zero8, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-#pragma unroll
-      for (int d = 0; d < 8; ++d)
-#pragma unroll
-        for (int t = 0; t < 4; ++t) acc[d][t] = zero4;
-    }
 
-    // The loop leaves at its bottom, so the tiles' loop-carried value has
-    // the next page's first MFMA as its only use and every MFMA can
-    // accumulate in place.
     while (true) {
-      // Page `it` has landed in every wave's share, the buffer of page it-1
-      // and the P buffer are free.
-      __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-      __syncthreads();
-      char* buf = lds_page[it & 1];
-      const int valid = min(kPage, L - cpage * kPage);
-      if (valid < kPage) {
-        zero_tail_rows(buf, valid, tid);
+      // ---------------- one pass over the segment's pages ----------------
+      m_seen = kNegInf;
+      l_run = 0.f;
+      overflow = 0;
+      // Output tiles, zeroed from an MFMA so that they are born in the
+      // accumulation registers.
+      {
+        const bf16x8 zero8 = __builtin_bit_cast(bf16x8, u32x4{0, 0, 0, 0});
+        const f32x4 zero4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(zero8, zero8, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+#pragma unroll
+        for (int d = 0; d < 8; ++d)
+#pragma unroll
+          for (int t = 0; t < 4; ++t) acc[d][t] = zero4;
+      }
+
+      // The loop leaves at its bottom, so the tiles' loop-carried value has
+      // the next page's first MFMA as its only use and every MFMA can
+      // accumulate in place.
+      while (true) {
+        // Page `it` has landed in every wave's share, the buffer of page it-1
+        // and the P buffer are free.
+        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
         __syncthreads();
-      }
-      // The next page's DMAs go out one by one inside this page's MFMA
-      // streams (below); its id was read a page ago.
-      const bool dma = lvalid;
-      const __amdgpu_buffer_rsrc_t dma_rsrc = page_resource(kv_head + (size_t)next_pid * page_stride_bytes, page_span);
-      const uint32_t dma_dst = lds_base + ((it + 1) & 1) * kPageBytes;
-
-      const uint32_t page_base = (uint32_t)(uintptr_t)buf;
-      uint32_t kb[2], vb[4];
-#pragma unroll
-      for (int par = 0; par < 2; ++par) kb[par] = page_base + kb_off[par];
-#pragma unroll
-      for (int m4 = 0; m4 < 4; ++m4) vb[m4] = page_base + vb_off[m4];
-      const int key0 = cpage * kPage;
-
-      auto read_k = [&](int kt, int ks) __attribute__((always_inline)) {
-        return *(lds_bf16x8*)(kb[ks & 1] + (uint32_t)((2 * kt * 9 + (ks >> 1)) * 1024));
-      };
-      // A operand of O^T += V^T P^T for output tile d of k-step kk: lane
-      // (n = col, grp4) gets V[key][128*wave + 16d + n] for keys 32kk +
-      // 4*grp4 + m and 32kk + 16 + 4*grp4 + m, from two transposing reads of
-      // 4 rows x 16 columns (lane l fetches row l/4, columns 4*(l%4)..+3).
-      auto read_v = [&](int kk, int d) __attribute__((always_inline)) {
-        const uint32_t o0 = (uint32_t)(((4 * kk + 0) * 9 + (d >> 2)) * 1024);
-        const uint32_t o1 = (uint32_t)(((4 * kk + 2) * 9 + (d >> 2)) * 1024);
-        const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vb[d & 3] + o0));
-        const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vb[d & 3] + o1));
-        return __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
-      };
-      // B operand for output row tile t of k-step kk: lane (col, grp4) gets
-      // P[16t + col][slots 8*grp4 .. +7 of k-step kk].
-      auto read_p = [&](int kk, int t) __attribute__((always_inline)) {
-        return *(lds_bf16x8*)(pr + (uint32_t)(t * 16 * kPRowBytes + kk * 64));
-      };
-
-      // ---- scores: S^T = K Q^T for key tiles kt = 0..3 (16 keys each) ----
-      // 72 MFMAs in issue order (kt, ks), K fragments kKAhead reads ahead;
-      // one DMA of the next page after MFMA kDmaStart + d * kDmaEvery of the
-      // page (scores and outputs).
-      constexpr int kKs = kDqk / 32;             // 18
-      constexpr int kQk = 4 * kKs;               // 72 score MFMAs
-      constexpr int kPv = 2 * 8 * 4;             // 64 output MFMAs
-      constexpr int kKAhead = 8;
-      constexpr int kDmaStart = 0;               // DMA d follows MFMA kDmaStart + d * kDmaEvery
-      constexpr int kDmaEvery = 4;
-      static_assert(kDmaStart + kDmaEvery * (kLdsDmaPerWave - 1) < kQk + kPv, "every DMA inside the streams");
-      f32x4 s[4];
-      bf16x8 kf[kQk];
-#pragma unroll
-      for (int r = 0; r < kKAhead; ++r) kf[r] = read_k(r / kKs, r % kKs);
-      __builtin_amdgcn_sched_barrier(0);
-      auto dma_step = [&]<int G>() __attribute__((always_inline)) {
-        if constexpr (G >= kDmaStart && (G - kDmaStart) % kDmaEvery == 0 && (G - kDmaStart) / kDmaEvery < kLdsDmaPerWave) {
-          if (dma) stage_tile(dma_rsrc, lane_src_off, row_stride_bytes, dma_dst, wave, (G - kDmaStart) / kDmaEvery);
+        char* buf = lds_page[it & 1];
+        const int valid = min(kPage, L - cpage * kPage);
+        if (valid < kPage) {
+          zero_tail_rows(buf, valid, tid);
+          __syncthreads();
         }
-      };
-      auto qk_step = [&]<int G>() __attribute__((always_inline)) {
-        constexpr int kt = G / kKs, ks = G % kKs;
-        const f32x4 c = ks == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : s[kt];
-        s[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[G], qf[ks], c, 0, 0, 0);
-        if constexpr (G + kKAhead < kQk) kf[G + kKAhead] = read_k((G + kKAhead) / kKs, (G + kKAhead) % kKs);
-        dma_step.template operator()<G>();
+        // The next page's DMAs go out one by one inside this page's MFMA
+        // streams (below); its id was read a page ago.
+        const bool dma = lvalid;
+        const __amdgpu_buffer_rsrc_t dma_rsrc = page_resource(kv_head + (size_t)next_pid * page_stride_bytes, page_span);
+        const uint32_t dma_dst = lds_base + ((it + 1) & 1) * kPageBytes;
+
+        const uint32_t page_base = (uint32_t)(uintptr_t)buf;
+        uint32_t kb[2], vb[4];
+#pragma unroll
+        for (int par = 0; par < 2; ++par) kb[par] = page_base + kb_off[par];
+#pragma unroll
+        for (int m4 = 0; m4 < 4; ++m4) vb[m4] = page_base + vb_off[m4];
+        const int key0 = cpage * kPage;
+
+        auto read_k = [&](int kt, int ks) __attribute__((always_inline)) {
+          return *(lds_bf16x8*)(kb[ks & 1] + (uint32_t)((2 * kt * 9 + (ks >> 1)) * 1024));
+        };
+        // A operand of O^T += V^T P^T for output tile d of k-step kk: lane
+        // (n = col, grp4) gets V[key][128*wave + 16d + n] for keys 32kk +
+        // 4*grp4 + m and 32kk + 16 + 4*grp4 + m, from two transposing reads of
+        // 4 rows x 16 columns (lane l fetches row l/4, columns 4*(l%4)..+3).
+        auto read_v = [&](int kk, int d) __attribute__((always_inline)) {
+          const uint32_t o0 = (uint32_t)(((4 * kk + 0) * 9 + (d >> 2)) * 1024);
+          const uint32_t o1 = (uint32_t)(((4 * kk + 2) * 9 + (d >> 2)) * 1024);
+          const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vb[d & 3] + o0));
+          const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vb[d & 3] + o1));
+          return __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
+        };
+        // B operand for output row tile t of k-step kk: lane (col, grp4) gets
+        // P[16t + col][slots 8*grp4 .. +7 of k-step kk].
+        auto read_p = [&](int kk, int t) __attribute__((always_inline)) {
+          return *(lds_bf16x8*)(pr + (uint32_t)(t * 16 * kPRowBytes + kk * 64));
+        };
+
+        // ---- scores: S^T = K Q^T for key tiles kt = 0..3 (16 keys each) ----
+        // 72 MFMAs in issue order (kt, ks), K fragments kKAhead reads ahead;
+        // one DMA of the next page after MFMA kDmaStart + d * kDmaEvery of the
+        // page (scores and outputs).
+        constexpr int kKs = kDqk / 32;             // 18
+        constexpr int kQk = 4 * kKs;               // 72 score MFMAs
+        constexpr int kPv = 2 * 8 * 4;             // 64 output MFMAs
+        constexpr int kKAhead = 8;
+        constexpr int kDmaStart = 0;               // DMA d follows MFMA kDmaStart + d * kDmaEvery
+        constexpr int kDmaEvery = 4;
+        static_assert(kDmaStart + kDmaEvery * (kLdsDmaPerWave - 1) < kQk + kPv, "every DMA inside the streams");
+        f32x4 s[4];
+        bf16x8 kf[kQk];
+#pragma unroll
+        for (int r = 0; r < kKAhead; ++r) kf[r] = read_k(r / kKs, r % kKs);
         __builtin_amdgcn_sched_barrier(0);
-      };
-      [&]<int... G>(std::integer_sequence<int, G...>) __attribute__((always_inline)) {
-        (qk_step.template operator()<G>(), ...);
-      }(std::make_integer_sequence<int, kQk>{});
+        auto dma_step = [&]<int G>() __attribute__((always_inline)) {
+          if constexpr (G >= kDmaStart && (G - kDmaStart) % kDmaEvery == 0 && (G - kDmaStart) / kDmaEvery < kLdsDmaPerWave) {
+            if (dma) stage_tile(dma_rsrc, lane_src_off, row_stride_bytes, dma_dst, wave, (G - kDmaStart) / kDmaEvery);
+          }
+        };
+        auto qk_step = [&]<int G>() __attribute__((always_inline)) {
+          constexpr int kt = G / kKs, ks = G % kKs;
+          const f32x4 c = ks == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : s[kt];
+          s[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[G], qf[ks], c, 0, 0, 0);
+          if constexpr (G + kKAhead < kQk) kf[G + kKAhead] = read_k((G + kKAhead) / kKs, (G + kKAhead) % kKs);
+          dma_step.template operator()<G>();
+          __builtin_amdgcn_sched_barrier(0);
+        };
+        [&]<int... G>(std::integer_sequence<int, G...>) __attribute__((always_inline)) {
+          (qk_step.template operator()<G>(), ...);
+        }(std::make_integer_sequence<int, kQk>{});
 
-      // The load cursor moves on and the id of the page after the next is
-      // read here, where waiting for the scalar load costs nothing.
-      if (lvalid) {
-        lvalid = next_page(meta, p.seqlens, lb, lpage, lend);
-        if (lvalid) next_pid = ld_uniform(p.block_table + (size_t)lb * p.max_pages + lpage);
-      }
+        // The load cursor moves on and the id of the page after the next is
+        // read here, where waiting for the scalar load costs nothing.
+        if (lvalid) {
+          lvalid = next_page(meta, p.seqlens, lb, lpage, lend);
+          if (lvalid) next_pid = ld_uniform(p.block_table + (size_t)lb * p.max_pages + lpage);
+        }
 
-      // ---- softmax weights (base 2) against the row reference ----
-      // Lane (col, grp4) holds, for the score row, key key0 + 16kt + 4*grp4 + i
-      // in s[kt][i].  Keys the row may not see get weight 0; masking is
-      // needed only on a page that holds such keys (the sequence's last page,
-      // or causal rows), a uniform test.
-      float x[4][4];
-#pragma unroll
-      for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) x[kt][i] = s[kt][i];
-      if (key0 + kPage > n_vis_min) {
+        // ---- softmax weights (base 2) against the row reference ----
+        // Lane (col, grp4) holds, for the score row, key key0 + 16kt + 4*grp4 + i
+        // in s[kt][i].  Keys the row may not see get weight 0; masking is
+        // needed only on a page that holds such keys (the sequence's last page,
+        // or causal rows), a uniform test.
+        float x[4][4];
 #pragma unroll
         for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int key = key0 + 16 * kt + 4 * grp4 + i;
-            x[kt][i] = key < n_vis ? x[kt][i] : kNegInf;
+          for (int i = 0; i < 4; ++i) x[kt][i] = s[kt][i];
+        if (key0 + kPage > n_vis_min) {
+#pragma unroll
+          for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int key = key0 + 16 * kt + 4 * grp4 + i;
+              x[kt][i] = key < n_vis ? x[kt][i] : kNegInf;
+            }
+        }
+        // This lane's maximum raw score (the scale is > 0), in log2 units.
+        float xm = kNegInf;
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt)
+          xm = fmaxf(xm, fmaxf(fmaxf(x[kt][0], x[kt][1]), fmaxf(x[kt][2], x[kt][3])));
+        xm *= p.scale_log2;
+        if (!second_pass && cpage == seg_page0) {
+          // First page of the segment: the reference is the row's maximum over
+          // the page, so a sequence that fits in one page has its largest
+          // weight exactly 1.
+          m_ref = row_max4(xm);
+        }
+        // A row with no reference yet that sees a key here, or a score far
+        // above the reference, voids the segment's result for this pass.
+        overflow |= xm > m_ref + kOverflowThreshold;
+        m_seen = fmaxf(m_seen, xm);
+        const float mu = m_ref == kNegInf ? 0.f : m_ref;
+        uint32_t pk[4][2];
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const float w0 = __builtin_amdgcn_exp2f(__builtin_fmaf(x[kt][2 * h], p.scale_log2, -mu));
+            const float w1 = __builtin_amdgcn_exp2f(__builtin_fmaf(x[kt][2 * h + 1], p.scale_log2, -mu));
+            l_run += w0 + w1;
+            pk[kt][h] = pack_bf16x2(w0, w1);
           }
-      }
-      // This lane's maximum raw score (the scale is > 0), in log2 units.
-      float xm = kNegInf;
+        // Slot 8*grp4 + 4*(kt&1) + i of k-step kk = kt>>1 holds key 16*(kt&1) + 4*grp4 + i.
 #pragma unroll
-      for (int kt = 0; kt < 4; ++kt)
-        xm = fmaxf(xm, fmaxf(fmaxf(x[kt][0], x[kt][1]), fmaxf(x[kt][2], x[kt][3])));
-      xm *= p.scale_log2;
-      if (!kRedo && cpage == seg_page0) {
-        // First page of the segment: the reference is the row's maximum over
-        // the page, so a sequence that fits in one page has its largest
-        // weight exactly 1.
-        m_ref = row_max4(xm);
-      }
-      // A row with no reference yet that sees a key here, or a score far
-      // above the reference, voids the segment's result for this pass.
-      overflow |= xm > m_ref + kOverflowThreshold;
-      m_seen = fmaxf(m_seen, xm);
-      const float mu = m_ref == kNegInf ? 0.f : m_ref;
-      uint32_t pk[4][2];
-#pragma unroll
-      for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const float w0 = __builtin_amdgcn_exp2f(__builtin_fmaf(x[kt][2 * h], p.scale_log2, -mu));
-          const float w1 = __builtin_amdgcn_exp2f(__builtin_fmaf(x[kt][2 * h + 1], p.scale_log2, -mu));
-          l_run += w0 + w1;
-          pk[kt][h] = pack_bf16x2(w0, w1);
-        }
-      // Slot 8*grp4 + 4*(kt&1) + i of k-step kk = kt>>1 holds key 16*(kt&1) + 4*grp4 + i.
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk)
-        *(__attribute__((address_space(3))) u32x4*)(pw + (uint32_t)(kk * 64)) =
-            u32x4{pk[2 * kk][0], pk[2 * kk][1], pk[2 * kk + 1][0], pk[2 * kk + 1][1]};
-      __syncthreads();            // P of all 64 rows is in LDS
+        for (int kk = 0; kk < 2; ++kk)
+          *(__attribute__((address_space(3))) u32x4*)(pw + (uint32_t)(kk * 64)) =
+              u32x4{pk[2 * kk][0], pk[2 * kk][1], pk[2 * kk + 1][0], pk[2 * kk + 1][1]};
+        __syncthreads();            // P of all 64 rows is in LDS
 
-      // ---- outputs: O^T += V^T P^T, 8 column tiles x 4 row tiles per k-step ----
-      // 64 MFMAs in issue order (kk, d, t); V fragments kVAhead ahead; the
-      // four P fragments of a k-step read before its first MFMA.
-      constexpr int kVAhead = 3;
-      bf16x8 vf[2][8], pfr[2][4];
+        // ---- outputs: O^T += V^T P^T, 8 column tiles x 4 row tiles per k-step ----
+        // 64 MFMAs in issue order (kk, d, t); V fragments kVAhead ahead; the
+        // four P fragments of a k-step read before its first MFMA.
+        constexpr int kVAhead = 3;
+        bf16x8 vf[2][8], pfr[2][4];
 #pragma unroll
-      for (int t = 0; t < 4; ++t) pfr[0][t] = read_p(0, t);
+        for (int t = 0; t < 4; ++t) pfr[0][t] = read_p(0, t);
 #pragma unroll
-      for (int d = 0; d < kVAhead; ++d) vf[0][d] = read_v(0, d);
-      __builtin_amdgcn_sched_barrier(0);
-      auto pv_step = [&]<int G>() __attribute__((always_inline)) {
-        constexpr int n = G - kQk, kk = n / 32, d = (n % 32) / 4, t = n % 4;
-        acc[d][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[kk][d], pfr[kk][t], acc[d][t], 0, 0, 0);
-        if constexpr (t == 3) {
-          constexpr int nv = kk * 8 + d + kVAhead;   // next V fragment to read
-          if constexpr (nv < 16) vf[nv / 8][nv % 8] = read_v(nv / 8, nv % 8);
-        }
-        if constexpr (kk == 0 && d == 5) pfr[1][t] = read_p(1, t);
-        dma_step.template operator()<G>();
+        for (int d = 0; d < kVAhead; ++d) vf[0][d] = read_v(0, d);
         __builtin_amdgcn_sched_barrier(0);
-      };
-      [&]<int... G>(std::integer_sequence<int, G...>) __attribute__((always_inline)) {
-        (pv_step.template operator()<G + kQk>(), ...);
-      }(std::make_integer_sequence<int, kPv>{});
+        auto pv_step = [&]<int G>() __attribute__((always_inline)) {
+          constexpr int n = G - kQk, kk = n / 32, d = (n % 32) / 4, t = n % 4;
+          acc[d][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[kk][d], pfr[kk][t], acc[d][t], 0, 0, 0);
+          if constexpr (t == 3) {
+            constexpr int nv = kk * 8 + d + kVAhead;   // next V fragment to read
+            if constexpr (nv < 16) vf[nv / 8][nv % 8] = read_v(nv / 8, nv % 8);
+          }
+          if constexpr (kk == 0 && d == 5) pfr[1][t] = read_p(1, t);
+          dma_step.template operator()<G>();
+          __builtin_amdgcn_sched_barrier(0);
+        };
+        [&]<int... G>(std::integer_sequence<int, G...>) __attribute__((always_inline)) {
+          (pv_step.template operator()<G + kQk>(), ...);
+        }(std::make_integer_sequence<int, kPv>{});
 
-      ++it;
-      if (cpage + 1 == cend) break;
-      ++cpage;
+        ++it;
+        if (cpage + 1 == cend) break;
+        ++cpage;
+      }
+
+      // Every wave is past its last output MFMA (sh.x below is free, and so is
+      // the buffer of the segment's last page).  A second pass cannot
+      // overflow (no score exceeds its row's maximum); it ends the loop anyway.
+      if (!__syncthreads_or(overflow) || second_pass) break;
+      // Some row of the block overflowed: the pass is void.  Run the segment
+      // again with every row's maximum over it as the reference, so that no
+      // weight exceeds 1.  The DMAs in flight (the worker's next page) are
+      // drained and the load pipeline restarts at the segment's first page.
+      m_ref = row_max4(m_seen);
+      second_pass = true;
+      __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+      __syncthreads();
+      lb = b;
+      lpage = seg_page0;
+      lend = cend;
+      cpage = seg_page0;
+      {
+        const int page_id = ld_uniform(p.block_table + (size_t)lb * p.max_pages + lpage);
+        lvalid = next_page(meta, p.seqlens, lb, lpage, lend);
+        stage_page(kv_head + (size_t)page_id * page_stride_bytes, page_span, lane_src_off, row_stride_bytes,
+                   lds_base + (it & 1) * kPageBytes, wave);
+        if (lvalid) next_pid = ld_uniform(p.block_table + (size_t)lb * p.max_pages + lpage);
+      }
     }
 
     // ---------------- segment epilogue ----------------
-    // Every wave is past its last output MFMA before sh.x is reused below;
-    // the page buffers are not touched here.
-    const int ovf = __syncthreads_or(overflow);
-    bool write_out = true;
-    if constexpr (!kRedo) {
-      // A segment where some row overflowed is recorded for the redo launch
-      // (with every row's maximum) and leaves its outputs to it.  Every
-      // segment writes its flag, so stale flags never survive a call.
-      const int item = (slot * p.h_kv + g) * p.row_blocks + rb;
-      if (tid == 0) p.redo_flag[item] = ovf;
-      if (ovf) {
-        const float r = row_max4(m_seen);
-        if (tid < kMetaInts) {
-          const int rec[kMetaInts] = {b, seg_page0, b, cend, slot - s0, 0, 0, 0};
-          p.redo_meta[(size_t)item * kMetaInts + tid] = rec[tid];
-        }
-        if (grp4 == 0) p.redo_m[(size_t)item * kRowsPerBlock + srow] = r;
-        write_out = false;
-      }
-    }
-    if (write_out) {
+    {
       // Row sums, swapped through LDS for the output waves.
       const float l_row = row_sum4(l_run);
       if (grp4 == 0) {
@@ -566,39 +585,10 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(DecodeParams p)
   if (grp >= p.num_workers * p.h_kv) return;
   const int worker = grp / p.h_kv;
   const int g = grp - worker * p.h_kv;
-  decode_worker<kSingleHead, false>(p, lds_page, sh, p.meta + (size_t)worker * kMetaInts, g, rb, -1);
-}
-
-// One workgroup redoes, one after another, the segments the decode launch
-// flagged (none for ordinary scores: the launch then only scans the flags).
-template <bool kSingleHead>
-__global__ __launch_bounds__(kThreads, 1) void mla_redo_kernel(DecodeParams p) {
-  __shared__ __attribute__((aligned(1024))) char lds_page[2][kPageBytes];
-  __shared__ __attribute__((aligned(16))) DecodeShared sh;
-  __shared__ int list[kRedoScan];
-  __shared__ int n_list;
-  const int tid = threadIdx.x;
-  const int total = p.num_splits[p.batch] * p.h_kv * p.row_blocks;
-  for (int base = 0; base < total; base += kRedoScan) {
-    if (tid == 0) n_list = 0;
-    __syncthreads();
-    for (int i = base + tid; i < min(total, base + kRedoScan); i += kThreads)
-      if (p.redo_flag[i]) list[atomicAdd(&n_list, 1)] = i;
-    __syncthreads();
-    const int n = n_list;
-    for (int e = 0; e < n; ++e) {
-      const int item = list[e];
-      const int rb = item % p.row_blocks;
-      const int g = (item / p.row_blocks) % p.h_kv;
-      decode_worker<kSingleHead, true>(p, lds_page, sh, p.redo_meta + (size_t)item * kMetaInts, g, rb, item);
-      __syncthreads();
-    }
-  }
+  decode_worker<kSingleHead>(p, lds_page, sh, p.meta + (size_t)worker * kMetaInts, g, rb);
 }
 
 template __global__ void mla_decode_kernel<true>(DecodeParams p);
 template __global__ void mla_decode_kernel<false>(DecodeParams p);
-template __global__ void mla_redo_kernel<true>(DecodeParams p);
-template __global__ void mla_redo_kernel<false>(DecodeParams p);
 
 }  // namespace mla

@@ -23,7 +23,6 @@ constexpr int kMetaInts = 8;
 constexpr int kMaxWorkers = 4096;
 constexpr int kSchedThreads = 256;
 constexpr int kCombineRowsPerBlock = 4;            // one wave per (sequence, head, query row)
-constexpr int kRedoScan = 256;                     // redo flags one scan step of the redo launch reads
 constexpr int kPRowBytes = 2 * kPage + 16;         // one row of softmax weights in LDS, padded against bank conflicts
 constexpr int kPBytes = kRowsPerBlock * kPRowBytes;
 
@@ -38,9 +37,6 @@ struct DecodeParams {
   float* lse;                   // [B][h_q][s_q]
   float* ws_o;                  // [W+B][h_kv][R][512]
   float* ws_lse;                // [W+B][h_kv][R]
-  int32_t* redo_flag;           // [W+B][h_kv][row_blocks]: segment overflowed (1) or not (0)
-  int32_t* redo_meta;           // [W+B][h_kv][row_blocks][8]: a flagged segment as a one-segment worker
-  float* redo_m;                // [W+B][h_kv][row_blocks][64]: its rows' maximum scores (log2 units)
   int batch, s_q, h_q, h_kv;
   int rows;                     // R = s_q * h_q / h_kv
   int group;                    // G = h_q / h_kv
@@ -71,8 +67,6 @@ struct SchedParams {
 
 template <bool kSingleHead>
 __global__ void mla_decode_kernel(DecodeParams p);
-template <bool kSingleHead>
-__global__ void mla_redo_kernel(DecodeParams p);
 __global__ void mla_combine_kernel(CombineParams p);
 __global__ void mla_sched_kernel(SchedParams p);
 

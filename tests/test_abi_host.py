@@ -29,7 +29,7 @@ def declared_functions():
 def test_header_declares_the_boundary():
     names = set(declared_functions())
     assert {"mla_get_metadata", "mla_decode_paged", "mla_num_workers", "mla_workspace_bytes",
-            "mla_status_string", "mla_decode_splitkv", "mla_decode_redo", "mla_combine_splits",
+            "mla_status_string", "mla_decode_splitkv", "mla_combine_splits",
             "mla_sched_fixed_overhead"} <= names
 
 
@@ -58,9 +58,7 @@ def test_workspace_bytes():
     got = lib.mla_workspace_bytes(64, 1, 128, 1, 512, 256)
     a256 = lambda x: (x + 255) // 256 * 256
     slots, rows = 256 + 64, 128
-    items = slots * 1 * 2                     # two row blocks of 64
-    assert got == (a256(slots * rows * 512 * 4) + a256(slots * rows * 4)
-                   + a256(items * 4) + a256(items * 8 * 4) + a256(items * 64 * 4))
+    assert got == a256(slots * rows * 512 * 4) + a256(slots * rows * 4)
     assert lib.mla_workspace_bytes(0, 1, 128, 1, 512, 256) == 0
     assert lib.mla_workspace_bytes(2, 1, 128, 3, 512, 256) == 0     # h_q % h_kv != 0
     assert lib.mla_workspace_bytes(2, 1, 128, 1, 256, 256) == 0     # dv != 512
@@ -91,7 +89,7 @@ def _decode(lib, entry="mla_decode_paged", **kw):
     (dict(ws_bytes=1024), -3),
     (dict(W=0), -4), (dict(W=5000), -4),
 ])
-@pytest.mark.parametrize("entry", ["mla_decode_paged", "mla_decode_splitkv", "mla_decode_redo"])
+@pytest.mark.parametrize("entry", ["mla_decode_paged", "mla_decode_splitkv"])
 def test_decode_rejects_invalid_arguments(kw, status, entry):
     assert _decode(_lib(), entry, **kw) == status
 

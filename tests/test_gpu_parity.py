@@ -73,9 +73,9 @@ def test_softmax_scale_argument():
 
 @pytest.mark.parametrize("W", [1, 3])
 def test_reference_point_overflow(W):
-    """Scores on later pages rise far above the first 32 keys of the split
-    (more than 2^48 in the kernel's base-2 weights): the decode launch must
-    flag the split and the redo launch recompute it, unsplit (W=1) and split
+    """Scores on later pages rise far above the split's first page (more
+    than 2^48 in the kernel's base-2 weights): the workgroup must run the
+    split a second time with each row's maximum as reference, unsplit (W=1) and split
     (W=3) alike.  Only the k^R columns are scaled, so V stays N(0, 1)."""
     inp = _custom(2, 1, 64, 1, False, [64 * 6 + 5, 64 * 3], seed=9)
     kv = inp.kvcache.float()
