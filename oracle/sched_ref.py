@@ -9,12 +9,15 @@ s_q*h_q//h_kv, h_kv)`` returns ``tile_scheduler_metadata, num_splits``
 split-KV kernel runs the pieces and a combine kernel merges them
 (deepseek.csdn.net article, section 4.2(1)) with dynamic load balancing over
 variable-length sequences (section 4.2(2)).  They give no rule.  This is the
-build's own rule ("rule v0"), written as plain loops:
+build's own rule ("rule v1"), written as plain loops:
 
 * n_b = ceil(L_b / 64) pages for sequence b.
-* A cost line holds, for each sequence in order, F overhead units followed by
-  its n_b page units.  T = sum_b (F + n_b) and the quota is
-  Q = max(1, ceil(T / W)) for W workers.
+* A cost line holds, for each sequence in order, H = floor(F / 2) overhead
+  units (its query load), its n_b page units, then F - H overhead units (its
+  output write).  T = sum_b (F + n_b) and the quota is Q = max(1, ceil(T / W))
+  for W workers.  Splitting F around the pages charges each of two workers
+  that share a sequence one of the two fixed costs, both of which every
+  split pays.
 * Worker w owns cost units [w*Q, (w+1)*Q).  Its segments are the
   intersections of that range with each sequence's page units; overhead-only
   intersections give no segment.
@@ -44,15 +47,16 @@ def num_workers_ref(n_cu: int, rows_per_kv: int, h_kv: int) -> int:
     return max(1, n_cu // (h_kv * row_blocks))
 
 
-def split_rule_v0(cache_seqlens, num_workers: int, fixed_overhead: int = FIXED_OVERHEAD_PAGES):
+def split_rule(cache_seqlens, num_workers: int, fixed_overhead: int = FIXED_OVERHEAD_PAGES):
     """Returns (tile_scheduler_metadata int32 [W][8], num_splits int32 [B+1])."""
     L = [int(x) for x in np.asarray(cache_seqlens).reshape(-1)]
     B, W, F = len(L), int(num_workers), int(fixed_overhead)
+    H = F // 2          # overhead units before a sequence's pages; F - H follow them
     n = [(x + PAGE_SIZE - 1) // PAGE_SIZE for x in L]
     start = []          # first page unit of each sequence on the cost line
     pos = 0
     for b in range(B):
-        start.append(pos + F)
+        start.append(pos + H)
         pos += F + n[b]
     T = pos
     Q = max(1, -(-T // W))

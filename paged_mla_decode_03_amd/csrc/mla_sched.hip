@@ -6,13 +6,16 @@
 // deepseek.csdn.net article, section 4.2(2).  The split rule itself is this
 // library's own:
 //
-//   n_b pages = ceil(L_b / 64).  On one cost line each sequence takes F
-//   overhead units (its query load and output write) followed by n_b page
-//   units; T = sum_b (F + n_b), quota Q = max(1, ceil(T / W)).  Worker w owns
-//   units [w*Q, (w+1)*Q) and processes the pages that fall in that range.
+//   n_b pages = ceil(L_b / 64).  On one cost line each sequence takes
+//   H = floor(F/2) overhead units (its query load), its n_b page units, then
+//   F - H overhead units (its output write); T = sum_b (F + n_b), quota
+//   Q = max(1, ceil(T / W)).  Worker w owns units [w*Q, (w+1)*Q) and
+//   processes the pages that fall in that range.  With the overhead on both
+//   sides of the pages, two workers that share a sequence are each charged
+//   one of the fixed costs that every split pays.
 //
-// Sequence b's pages start at unit s_b + F (s_b = exclusive prefix sum of the
-// costs), so the workers meeting them are wf = (s_b+F)/Q .. wl = (s_b+F+n_b-1)/Q,
+// Sequence b's pages start at unit s_b + H (s_b = exclusive prefix sum of the
+// costs), so the workers meeting them are wf = (s_b+H)/Q .. wl = (s_b+H+n_b-1)/Q,
 // and b has wl - wf + 1 splits.  A worker's first segment is the sequence with
 // the smallest b that meets it, its last the largest; min/max over b are
 // found with LDS atomics, which makes the result independent of thread order.
@@ -51,7 +54,7 @@ __global__ __launch_bounds__(kSchedThreads) void mla_sched_kernel(SchedParams p)
   __shared__ int first_seq[kMaxWorkers];
   __shared__ int last_seq[kMaxWorkers];
   const int tid = threadIdx.x;
-  const int B = p.batch, W = p.num_workers, F = p.fixed_overhead;
+  const int B = p.batch, W = p.num_workers, F = p.fixed_overhead, H = F / 2;
 
   for (int w = tid; w < W; w += kSchedThreads) {
     first_seq[w] = 0x7fffffff;
@@ -76,7 +79,7 @@ __global__ __launch_bounds__(kSchedThreads) void mla_sched_kernel(SchedParams p)
     const int n = b < B ? pages_of(p.seqlens[b]) : 0;
     long long chunk_cost, chunk_splits;
     const long long s_b = start_carry + block_exclusive_scan(b < B ? (long long)F + n : 0, scan_tmp, chunk_cost);
-    const long long first_unit = s_b + F;
+    const long long first_unit = s_b + H;
     long long wf = 0, wl = -1;
     if (n > 0) {
       wf = first_unit / Q;
@@ -111,7 +114,7 @@ __global__ __launch_bounds__(kSchedThreads) void mla_sched_kernel(SchedParams p)
     const long long s_b = start_carry + block_exclusive_scan(b < B ? (long long)F + n : 0, scan_tmp, chunk_cost);
     start_carry += chunk_cost;
     if (n == 0) continue;
-    const long long first_unit = s_b + F;
+    const long long first_unit = s_b + H;
     const long long wf = first_unit / Q, wl = (first_unit + n - 1) / Q;
     for (long long w = wf; w <= wl; ++w) {
       int32_t* row = p.meta + (size_t)w * kMetaInts;

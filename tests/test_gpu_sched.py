@@ -4,7 +4,7 @@ import numpy as np
 import pytest
 import torch
 
-from oracle.sched_ref import split_rule_v0
+from oracle.sched_ref import split_rule
 from paged_mla_decode_03_amd import fixed_overhead_pages, get_mla_metadata, num_workers
 from workloads import WORKLOADS, draw_seqlens
 
@@ -17,7 +17,7 @@ def _check(seqlens, rows, h_kv, W=None):
     W = W or num_workers(rows, h_kv)
     meta, ns = get_mla_metadata(L, rows, h_kv, W)
     torch.cuda.synchronize()
-    ref_meta, ref_ns = split_rule_v0(seqlens, W, fixed_overhead_pages())
+    ref_meta, ref_ns = split_rule(seqlens, W, fixed_overhead_pages())
     np.testing.assert_array_equal(meta.cpu().numpy(), ref_meta)
     np.testing.assert_array_equal(ns.cpu().numpy(), ref_ns)
 

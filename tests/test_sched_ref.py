@@ -11,8 +11,7 @@ quota, split slots are dense and unique.
 import numpy as np
 import pytest
 
-from oracle.sched_ref import (FIXED_OVERHEAD_PAGES, PAGE_SIZE, num_workers_ref, segments_of,
-                              split_rule_v0)
+from oracle.sched_ref import FIXED_OVERHEAD_PAGES, PAGE_SIZE, num_workers_ref, segments_of, split_rule
 
 
 def simulate(seqlens, W, F):
@@ -20,8 +19,9 @@ def simulate(seqlens, W, F):
     [(b, page_lo, page_hi)] and per-sequence split counts."""
     units = []
     for b, L in enumerate(seqlens):
-        units += [None] * F
+        units += [None] * (F // 2)
         units += [(b, p) for p in range((L + PAGE_SIZE - 1) // PAGE_SIZE)]
+        units += [None] * (F - F // 2)
     T = len(units)
     Q = max(1, -(-T // W))
     segs = [[] for _ in range(W)]
@@ -53,9 +53,9 @@ CASES = [
 
 
 @pytest.mark.parametrize("seqlens,W", CASES)
-@pytest.mark.parametrize("F", [0, FIXED_OVERHEAD_PAGES, 5])
+@pytest.mark.parametrize("F", [0, 1, FIXED_OVERHEAD_PAGES, 5])
 def test_rule_matches_unit_simulation(seqlens, W, F):
-    meta, ns = split_rule_v0(seqlens, W, F)
+    meta, ns = split_rule(seqlens, W, F)
     segs, counts, Q = simulate(seqlens, W, F)
     assert meta.shape == (W, 8) and meta.dtype == np.int32
     assert ns.shape == (len(seqlens) + 1,) and ns.dtype == np.int32
@@ -82,11 +82,21 @@ def test_rule_matches_unit_simulation(seqlens, W, F):
 
 def test_uniform_workload_is_balanced():
     # 64 x 64 pages over 256 workers with no overhead: 16 pages each, 4 splits each.
-    meta, ns = split_rule_v0([4096] * 64, 256, 0)
+    meta, ns = split_rule([4096] * 64, 256, 0)
     assert list(np.diff(ns)) == [4] * 64
     for w in range(256):
         (b, lo, hi, slot), = segments_of(meta[w], [4096] * 64, ns)
         assert hi - lo == 16
+
+
+def test_two_workers_sharing_a_sequence_get_equal_pages():
+    # 64 x 64 pages over 128 workers: every sequence is split in two, and each
+    # half pays one of the sequence's two fixed costs, so all workers get 32.
+    meta, ns = split_rule([4096] * 64, 128, FIXED_OVERHEAD_PAGES)
+    assert list(np.diff(ns)) == [2] * 64
+    for w in range(128):
+        (b, lo, hi, slot), = segments_of(meta[w], [4096] * 64, ns)
+        assert hi - lo == 32
 
 
 def test_num_workers():
