@@ -61,10 +61,14 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 constexpr float kOverflowThreshold = 48.0f;   // log2 units: weights stay <= 2^48
 constexpr float kNegInf = -__builtin_huge_valf();
 constexpr uint32_t kBufferConfig = 0x00020000;   // buffer resource word 3 (raw, no swizzle)
-// s_waitcnt immediate for vmcnt(0) alone (expcnt and lgkmcnt at their maxima).
-// Issued through the builtin, the compiler knows every vector memory
-// operation -- its own and the page DMAs -- is complete after it.
+// s_waitcnt immediate for vmcnt(0) alone (expcnt and lgkmcnt at their maxima),
+// for waits on the kernel's own vector loads: issued through the builtin, the
+// compiler knows they are complete after it.
 constexpr int kWaitVmcnt0 = 0x0F70;
+
+// Wait for the page DMAs, which the compiler does not see: in inline
+// assembly, so that no pass can judge it redundant and drop it.
+__device__ inline void wait_dma_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 __device__ inline int pages_of(int seqlen) { return (seqlen + kPage - 1) / kPage; }
 
@@ -155,6 +159,11 @@ __device__ inline float xor32_pair(float x, bool max_op) {
   return max_op ? fmaxf(a, b) : a + b;
 }
 __device__ inline float row_max4(float x) { return xor32_pair(xor16_pair(x, true), true); }
+
+// Larger of two scores.  NaN-propagating maximum (v_maximum3_f32): unlike
+// fmaxf it needs no quieting of its inputs first.  Scores are never NaN
+// (slots past a sequence's end are zeroed in LDS before use).
+__device__ inline float max2(float a, float b) { return __builtin_elementwise_maximum(a, b); }
 __device__ inline float row_sum4(float x) { return xor32_pair(xor16_pair(x, false), false); }
 
 // Two floats to two bf16 (round to nearest even) in one v_cvt_pk_bf16_f32.
@@ -169,8 +178,10 @@ __device__ inline int segment_end(const int32_t* meta, const int32_t* seqlens, i
   return b == ld_uniform(meta + 2) ? ld_uniform(meta + 3) : pages_of(ld_uniform(seqlens + b));
 }
 
-// Advance (b, page, end) to the worker's next page; returns false past the end.
-__device__ inline bool next_page(const int32_t* meta, const int32_t* seqlens, int& b, int& page, int& end) {
+// Advance (b, page, end) to the worker's next page; returns false past the
+// end.  p0 is the first page of the cursor's segment (0 on entering a new
+// sequence).
+__device__ inline bool next_page(const int32_t* meta, const int32_t* seqlens, int& b, int& page, int& end, int& p0) {
   if (++page < end) return true;
   for (int nb = b + 1; nb <= ld_uniform(meta + 2); ++nb) {
     const int e = segment_end(meta, seqlens, nb);
@@ -178,10 +189,25 @@ __device__ inline bool next_page(const int32_t* meta, const int32_t* seqlens, in
       b = nb;
       page = 0;
       end = e;
+      p0 = 0;
       return true;
     }
   }
   return false;
+}
+
+// Page that step `page` of segment [p0, end) processes.  The two row blocks
+// of a head read the same pages, and each page's fetch takes its full memory
+// latency while its twin in the other block is still in flight.  So odd row
+// blocks swap the pages after the first in pairs (p0, p0+2, p0+1, p0+4,
+// p0+3, ...): every other page a block fetches is the one its twin fetched a
+// page earlier, an L2 hit, and the two blocks together keep two pages in
+// flight.  The first page, whose maxima set the softmax references, stays
+// first in both blocks.  The result does not otherwise depend on the order.
+__device__ inline int page_in_order(int page, int p0, int end, bool swap) {
+  const int j = page - p0;
+  const int jj = ((j - 1) ^ 1) + 1;
+  return swap && j >= 1 && p0 + jj < end ? p0 + jj : page;
 }
 
 }  // namespace
@@ -226,7 +252,8 @@ __device__ __forceinline__ void decode_worker(const DecodeParams& p, char (*lds_
   // Compute cursor (cb, cpage, cend) and load cursor (lb, lpage, lend).
   int cb = meta_b0, cpage = ld_uniform(meta + 1), cend = segment_end(meta, p.seqlens, cb);
   if (cpage >= cend) return;
-  int lb = cb, lpage = cpage, lend = cend;
+  int lb = cb, lpage = cpage, lend = cend, lp0 = cpage;
+  const bool swap = rb & 1;
   bool lvalid = true;
 
   const int row_stride_bytes = kSingleHead ? kRowBytes : p.h_kv * kRowBytes;   // bytes between tokens
@@ -272,23 +299,18 @@ __device__ __forceinline__ void decode_worker(const DecodeParams& p, char (*lds_
       qf[ks] = __builtin_bit_cast(bf16x8, v);
     }
   };
-  // The first segment's Q needs only the worker's first sequence: its loads
-  // go out before the chain of table reads that locates the first page.
-  load_q(cb);
-
   // First page in flight before anything else; the id of the page after it
   // is read now, one page ahead of its DMAs.
   int next_pid = 0;
   {
-    const int page_id = ld_uniform(p.block_table + (size_t)lb * p.max_pages + lpage);
-    lvalid = next_page(meta, p.seqlens, lb, lpage, lend);
+    const int page_id = ld_uniform(p.block_table + (size_t)lb * p.max_pages + page_in_order(lpage, lp0, lend, swap));
+    lvalid = next_page(meta, p.seqlens, lb, lpage, lend, lp0);
     stage_page(kv_head + (size_t)page_id * page_stride_bytes, page_span, lane_src_off, row_stride_bytes,
                lds_base, wave);
-    if (lvalid) next_pid = ld_uniform(p.block_table + (size_t)lb * p.max_pages + lpage);
+    if (lvalid) next_pid = ld_uniform(p.block_table + (size_t)lb * p.max_pages + page_in_order(lpage, lp0, lend, swap));
   }
 
   int it = 0;
-  bool first_segment = true;
   while (true) {
     // ---------------- segment: pages [cpage, cend) of sequence cb ----------------
     const int b = cb;
@@ -297,8 +319,10 @@ __device__ __forceinline__ void decode_worker(const DecodeParams& p, char (*lds_
     const int nsplit = ld_uniform(p.num_splits + b + 1) - s0;
     const int slot = s0 + (b == meta_b0 ? ld_uniform(meta + 4) : 0);
     const int seg_page0 = cpage;
-    if (!first_segment) load_q(b);
-    first_segment = false;
+    load_q(b);
+    // Q is waited for here, once per segment, so that no wait inside the page
+    // loop is left to count Q's loads (it would wait for the page DMAs too).
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     const int n_vis = p.causal ? L - p.s_q + row_tok(srow) + 1 : L;   // keys the score row may see
     // Fewest keys any row of the block sees (causal rows: the block's first token).
     const int n_vis_min = p.causal ? L - p.s_q + row_tok(0) + 1 : L;
@@ -330,10 +354,11 @@ __device__ __forceinline__ void decode_worker(const DecodeParams& p, char (*lds_
       while (true) {
         // Page `it` has landed in every wave's share, the buffer of page it-1
         // and the P buffer are free.
-        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+        wait_dma_all();
         __syncthreads();
         char* buf = lds_page[it & 1];
-        const int valid = min(kPage, L - cpage * kPage);
+        const int ppage = page_in_order(cpage, seg_page0, cend, swap);   // the page this step processes
+        const int valid = min(kPage, L - ppage * kPage);
         if (valid < kPage) {
           zero_tail_rows(buf, valid, tid);
           __syncthreads();
@@ -350,7 +375,7 @@ __device__ __forceinline__ void decode_worker(const DecodeParams& p, char (*lds_
         for (int par = 0; par < 2; ++par) kb[par] = page_base + kb_off[par];
 #pragma unroll
         for (int m4 = 0; m4 < 4; ++m4) vb[m4] = page_base + vb_off[m4];
-        const int key0 = cpage * kPage;
+        const int key0 = ppage * kPage;
 
         auto read_k = [&](int kt, int ks) __attribute__((always_inline)) {
           return *(lds_bf16x8*)(kb[ks & 1] + (uint32_t)((2 * kt * 9 + (ks >> 1)) * 1024));
@@ -408,8 +433,8 @@ __device__ __forceinline__ void decode_worker(const DecodeParams& p, char (*lds_
         // The load cursor moves on and the id of the page after the next is
         // read here, where waiting for the scalar load costs nothing.
         if (lvalid) {
-          lvalid = next_page(meta, p.seqlens, lb, lpage, lend);
-          if (lvalid) next_pid = ld_uniform(p.block_table + (size_t)lb * p.max_pages + lpage);
+          lvalid = next_page(meta, p.seqlens, lb, lpage, lend, lp0);
+          if (lvalid) next_pid = ld_uniform(p.block_table + (size_t)lb * p.max_pages + page_in_order(lpage, lp0, lend, swap));
         }
 
         // ---- softmax weights (base 2) against the row reference ----
@@ -435,7 +460,7 @@ __device__ __forceinline__ void decode_worker(const DecodeParams& p, char (*lds_
         float xm = kNegInf;
 #pragma unroll
         for (int kt = 0; kt < 4; ++kt)
-          xm = fmaxf(xm, fmaxf(fmaxf(x[kt][0], x[kt][1]), fmaxf(x[kt][2], x[kt][3])));
+          xm = max2(xm, max2(max2(x[kt][0], x[kt][1]), max2(x[kt][2], x[kt][3])));
         xm *= p.scale_log2;
         if (!second_pass && cpage == seg_page0) {
           // First page of the segment: the reference is the row's maximum over
@@ -446,7 +471,7 @@ __device__ __forceinline__ void decode_worker(const DecodeParams& p, char (*lds_
         // A row with no reference yet that sees a key here, or a score far
         // above the reference, voids the segment's result for this pass.
         overflow |= xm > m_ref + kOverflowThreshold;
-        m_seen = fmaxf(m_seen, xm);
+        m_seen = max2(m_seen, xm);
         const float mu = m_ref == kNegInf ? 0.f : m_ref;
         uint32_t pk[4][2];
 #pragma unroll
@@ -505,18 +530,19 @@ __device__ __forceinline__ void decode_worker(const DecodeParams& p, char (*lds_
       // drained and the load pipeline restarts at the segment's first page.
       m_ref = row_max4(m_seen);
       second_pass = true;
-      __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+      wait_dma_all();
       __syncthreads();
       lb = b;
       lpage = seg_page0;
       lend = cend;
+      lp0 = seg_page0;
       cpage = seg_page0;
       {
-        const int page_id = ld_uniform(p.block_table + (size_t)lb * p.max_pages + lpage);
-        lvalid = next_page(meta, p.seqlens, lb, lpage, lend);
+        const int page_id = ld_uniform(p.block_table + (size_t)lb * p.max_pages + page_in_order(lpage, lp0, lend, swap));
+        lvalid = next_page(meta, p.seqlens, lb, lpage, lend, lp0);
         stage_page(kv_head + (size_t)page_id * page_stride_bytes, page_span, lane_src_off, row_stride_bytes,
                    lds_base + (it & 1) * kPageBytes, wave);
-        if (lvalid) next_pid = ld_uniform(p.block_table + (size_t)lb * p.max_pages + lpage);
+        if (lvalid) next_pid = ld_uniform(p.block_table + (size_t)lb * p.max_pages + page_in_order(lpage, lp0, lend, swap));
       }
     }
 
@@ -563,8 +589,8 @@ __device__ __forceinline__ void decode_worker(const DecodeParams& p, char (*lds_
 
     // Next segment: the sequence after this one in the worker's range.
     if (cb == meta_b1) break;
-    int nb = cb, np = cpage, ne = cend;
-    if (!next_page(meta, p.seqlens, nb, np, ne)) break;
+    int nb = cb, np = cpage, ne = cend, n0 = seg_page0;
+    if (!next_page(meta, p.seqlens, nb, np, ne, n0)) break;
     cb = nb;
     cpage = np;
     cend = ne;
