@@ -8,21 +8,24 @@
 // block_table, a split-KV forward kernel, then a combine kernel).
 //
 // Work decomposition (MI355X-native):
-//   * One workgroup = 4 waves = 64 query rows of one latent head, over the
-//     page range the scheduler gave its worker.  The workgroups that serve
-//     the other row blocks of the same head read the same pages; they are
-//     dispatched back to back on the same XCD so the second read hits L2.
-//   * Scores: wave v takes query rows 16v..16v+15 against all 64 keys of a
-//     page.  Its absorbed Q (16 x 576 bf16) sits in VGPRs as MFMA B
-//     fragments for the whole segment; S^T = K Q^T is 4 key tiles x 18
-//     k-steps of v_mfma_f32_16x16x32_bf16 with K fragments read from LDS.
+//   * One workgroup = 8 waves (two per SIMD) = 64 query rows of one latent
+//     head, over the page range the scheduler gave its worker.  The
+//     workgroups that serve the other row blocks of the same head read the
+//     same pages; they are dispatched back to back on the same XCD so the
+//     second read hits L2.
+//   * Scores: wave v takes score row tile v % 4 (16 query rows) against key
+//     half v / 4 (32 keys) of a page.  Its absorbed Q (16 x 576 bf16) sits in
+//     VGPRs as MFMA B fragments for the whole segment; S^T = K Q^T is 2 key
+//     tiles x 18 k-steps of v_mfma_f32_16x16x32_bf16 with K fragments read
+//     from LDS.
 //   * Softmax in the score accumulators' layout (each lane holds 4 keys of
-//     one row, 16 per page), row maxima and sums with lane permutes; the
-//     bf16 weights P go to LDS.
-//   * Outputs: wave v owns output columns 128v..128v+127 for all 64 rows,
+//     one row per tile), row maxima and sums with lane permutes and, across
+//     the two key halves, through LDS; the bf16 weights P go to LDS.
+//   * Outputs: wave v owns output columns 64v..64v+63 for all 64 rows,
 //     O^T += V^T P^T (A = V columns read with the transposing
-//     ds_read_b64_tr_b16, B = P from LDS), 32 accumulators (128 registers)
-//     that only MFMAs touch.
+//     ds_read_b64_tr_b16, B = P from LDS), 16 accumulators (64 registers)
+//     that only MFMAs touch.  With two waves per SIMD, one wave's softmax,
+//     LDS waits and DMA issue overlap the other's MFMAs.
 //   * Pages move HBM -> LDS with buffer_load_dwordx4 ... lds (no VGPR
 //     staging; the buffer resource bounds every read to the page), double
 //     buffered: page i+1's 72 DMAs go out one by one between page i's MFMAs.
@@ -108,16 +111,14 @@ __device__ inline __amdgpu_buffer_rsrc_t page_resource(const char* page_head, ui
 }
 
 // DMA number k (0 .. kLdsDmaPerWave-1) of this wave for one page: tile
-// j = 18 * wave + k, i.e. rows 8a..8a+7 x chunks 8b..8b+7 with j = 9a + b,
-// so a = 2 * wave + k / 9 and b = k % 9.  Both addresses are a per-wave base
-// plus a compile-time offset (k is a constant in every call), which keeps the
-// 18 DMAs of a page from holding 36 scalar registers across the page loop.
+// j = 9 * wave + k, i.e. rows 8*wave..+7 x chunks 8k..8k+7.  Both addresses
+// are a per-wave base plus a compile-time offset (k is a constant in every
+// call), so the page's DMAs hold no scalar registers across the page loop.
 __device__ inline void stage_tile(__amdgpu_buffer_rsrc_t rsrc, uint32_t lane_off, int row_stride_bytes,
                                   uint32_t lds_dst, int wave, int k) {
-  static_assert(kLdsDmaPerWave == 18, "two 8-row tile rows per wave");
-  const int a = 2 * wave + k / 9, b = k % 9;
+  static_assert(kLdsDmaPerWave == 9, "one 8-row tile row per wave");
   const uint32_t m0 = lds_dst + (uint32_t)(wave * kLdsDmaPerWave * 1024) + (uint32_t)(k * 1024);
-  const uint32_t soff = a * 8 * row_stride_bytes + b * 128;
+  const uint32_t soff = wave * 8 * row_stride_bytes + k * 128;
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
                :
                : "s"(m0), "v"(lane_off), "s"(rsrc), "s"(soff)
@@ -217,18 +218,18 @@ __device__ inline int page_in_order(int page, int p0, int end, bool swap) {
 // float per row for the row sums the output waves need.
 struct DecodeShared {
   char p[kPBytes];
-  float x[kRowsPerBlock];
+  float x[2][kRowsPerBlock];    // per-row values of the two key halves (maxima, sums)
 };
 
 // One worker's pages for latent head g and row block rb: every segment in the
 // worker's range [meta[0], meta[1]) .. [meta[2], meta[3]).
 //
-// Roles of the four waves.  Scores and softmax: wave w takes query rows
-// 16w ..+15 (its Q, 16 x 576 bf16, sits in VGPRs) against all 64 keys of
-// each page, so a row's maximum and sum never leave its wave.  Outputs:
-// wave w owns output columns 128w ..+127 for all 64 rows (O^T, 128 x 64
-// fp32, in 32 MFMA accumulators), reading P of all rows from LDS and V
-// columns 128w ..+127 only.
+// Roles of the eight waves.  Scores and softmax: wave w takes query rows
+// 16*(w%4) ..+15 (its Q, 16 x 576 bf16, sits in VGPRs) against keys
+// 32*(w/4) ..+31 of each page; a row's maximum (first page) and sum combine
+// the two halves through LDS.  Outputs: wave w owns output columns
+// 64w ..+63 for all 64 rows (O^T, 64 x 64 fp32, in 16 MFMA accumulators),
+// reading P of all rows from LDS and V columns 64w ..+63 only.
 //
 // kSingleHead: h_kv == 1, so a page's rows are contiguous 1152-byte rows and
 // every stride is a compile-time constant.
@@ -246,6 +247,8 @@ __device__ __forceinline__ void decode_worker(const DecodeParams& p, char (*lds_
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
   const int grp4 = lane >> 4;     // which 4-key / 8-wide k slice of an MFMA fragment
   const int col = lane & 15;      // row (or output column) within an MFMA tile
+  const int rt = wave & 3;        // score row tile of this wave
+  const int kh = wave >> 2;       // key half (32 keys of each page) of this wave's scores
 
   const int meta_b0 = ld_uniform(meta + 0), meta_b1 = ld_uniform(meta + 2);
   if (meta_b1 < meta_b0) return;                       // worker without pages
@@ -265,15 +268,15 @@ __device__ __forceinline__ void decode_worker(const DecodeParams& p, char (*lds_
   // Page-independent per-lane LDS offsets; a fragment read adds the page
   // buffer's base and a compile-time offset below 64 KB.
   //   K: row col (+16 per key tile), 16-byte chunk 4*par + grp4 (+8 per 2 k-steps).
-  //   V: row lane/4 (+16 per read), columns 128*wave + 16*m4 + 4*(lane%4) (+64 per 4 tiles).
-  //   P: row 16*wave + col (write) or col (read, +16 per row tile), chunk grp4 (+4 per k-step).
+  //   V: row lane/4 (+16 per read), columns 64*wave + 16*d + 4*(lane%4).
+  //   P: row 16*rt + col (write) or col (read, +16 per row tile), chunk grp4 (+4 per k-step).
   uint32_t kb_off[2], vb_off[4];
 #pragma unroll
   for (int par = 0; par < 2; ++par) kb_off[par] = lds_tile_offset(col, 4 * par + grp4);
 #pragma unroll
-  for (int m4 = 0; m4 < 4; ++m4)
-    vb_off[m4] = wave * (2 * 1024) + lds_tile_offset(lane >> 2, 2 * m4 + ((lane & 3) >> 1)) + 8 * (lane & 1);
-  const uint32_t pw = lds_p + (16 * wave + col) * kPRowBytes + grp4 * 16;
+  for (int d = 0; d < 4; ++d)
+    vb_off[d] = wave * 1024 + lds_tile_offset(lane >> 2, 2 * d + ((lane & 3) >> 1)) + 8 * (lane & 1);
+  const uint32_t pw = lds_p + (16 * rt + col) * kPRowBytes + grp4 * 16;
   const uint32_t pr = lds_p + col * kPRowBytes + grp4 * 16;
 
   // Query row r of the block: its token and head.
@@ -285,7 +288,7 @@ __device__ __forceinline__ void decode_worker(const DecodeParams& p, char (*lds_
     const int qrow = rb * kRowsPerBlock + r;
     return qrow < p.rows ? g * p.group + (qrow - (qrow / p.group) * p.group) : 0;
   };
-  const int srow = 16 * wave + col;    // this lane's score row
+  const int srow = 16 * rt + col;      // this lane's score row
 
   // Q fragments of the score row for sequence b: lane (col, grp4) holds dims
   // 32*ks + 8*grp4 .. +7.
@@ -330,7 +333,7 @@ __device__ __forceinline__ void decode_worker(const DecodeParams& p, char (*lds_
     bool second_pass = false;   // rerun with m_ref = the row's maximum over the segment
     float m_seen, l_run;        // largest score this lane has seen; its share of sum_j 2^(s_j - m_ref)
     int overflow;               // a score rose more than kOverflowThreshold above the reference
-    f32x4 acc[8][4];
+    f32x4 acc[4][4];
 
     while (true) {
       // ---------------- one pass over the segment's pages ----------------
@@ -343,7 +346,7 @@ __device__ __forceinline__ void decode_worker(const DecodeParams& p, char (*lds_
         const bf16x8 zero8 = __builtin_bit_cast(bf16x8, u32x4{0, 0, 0, 0});
         const f32x4 zero4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(zero8, zero8, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
 #pragma unroll
-        for (int d = 0; d < 8; ++d)
+        for (int d = 0; d < 4; ++d)
 #pragma unroll
           for (int t = 0; t < 4; ++t) acc[d][t] = zero4;
       }
@@ -381,14 +384,14 @@ __device__ __forceinline__ void decode_worker(const DecodeParams& p, char (*lds_
           return *(lds_bf16x8*)(kb[ks & 1] + (uint32_t)((2 * kt * 9 + (ks >> 1)) * 1024));
         };
         // A operand of O^T += V^T P^T for output tile d of k-step kk: lane
-        // (n = col, grp4) gets V[key][128*wave + 16d + n] for keys 32kk +
+        // (n = col, grp4) gets V[key][64*wave + 16d + n] for keys 32kk +
         // 4*grp4 + m and 32kk + 16 + 4*grp4 + m, from two transposing reads of
         // 4 rows x 16 columns (lane l fetches row l/4, columns 4*(l%4)..+3).
         auto read_v = [&](int kk, int d) __attribute__((always_inline)) {
-          const uint32_t o0 = (uint32_t)(((4 * kk + 0) * 9 + (d >> 2)) * 1024);
-          const uint32_t o1 = (uint32_t)(((4 * kk + 2) * 9 + (d >> 2)) * 1024);
-          const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vb[d & 3] + o0));
-          const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vb[d & 3] + o1));
+          const uint32_t o0 = (uint32_t)((4 * kk + 0) * 9 * 1024);
+          const uint32_t o1 = (uint32_t)((4 * kk + 2) * 9 * 1024);
+          const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vb[d] + o0));
+          const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vb[d] + o1));
           return __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
         };
         // B operand for output row tile t of k-step kk: lane (col, grp4) gets
@@ -397,21 +400,23 @@ __device__ __forceinline__ void decode_worker(const DecodeParams& p, char (*lds_
           return *(lds_bf16x8*)(pr + (uint32_t)(t * 16 * kPRowBytes + kk * 64));
         };
 
-        // ---- scores: S^T = K Q^T for key tiles kt = 0..3 (16 keys each) ----
-        // 72 MFMAs in issue order (kt, ks), K fragments kKAhead reads ahead;
+        // ---- scores: S^T = K Q^T for key tiles 2kh, 2kh+1 (16 keys each) ----
+        // 36 MFMAs, K fragments kKAhead reads ahead;
         // one DMA of the next page after MFMA kDmaStart + d * kDmaEvery of the
         // page (scores and outputs).
         constexpr int kKs = kDqk / 32;             // 18
-        constexpr int kQk = 4 * kKs;               // 72 score MFMAs
-        constexpr int kPv = 2 * 8 * 4;             // 64 output MFMAs
+        constexpr int kQk = 2 * kKs;               // 36 score MFMAs: 2 key tiles x 18 k-steps
+        constexpr int kPv = 2 * 4 * 4;             // 32 output MFMAs: 2 k-steps x 4 column tiles x 4 row tiles
         constexpr int kKAhead = 8;
         constexpr int kDmaStart = 0;               // DMA d follows MFMA kDmaStart + d * kDmaEvery
         constexpr int kDmaEvery = 4;
         static_assert(kDmaStart + kDmaEvery * (kLdsDmaPerWave - 1) < kQk + kPv, "every DMA inside the streams");
-        f32x4 s[4];
+        f32x4 s[2];
         bf16x8 kf[kQk];
+        // Score MFMA G covers key tile 2*kh + G % 2 at k-step G / 2: the two
+        // tiles' accumulation chains alternate.
 #pragma unroll
-        for (int r = 0; r < kKAhead; ++r) kf[r] = read_k(r / kKs, r % kKs);
+        for (int r = 0; r < kKAhead; ++r) kf[r] = read_k(2 * kh + r % 2, r / 2);
         __builtin_amdgcn_sched_barrier(0);
         auto dma_step = [&]<int G>() __attribute__((always_inline)) {
           if constexpr (G >= kDmaStart && (G - kDmaStart) % kDmaEvery == 0 && (G - kDmaStart) / kDmaEvery < kLdsDmaPerWave) {
@@ -419,10 +424,10 @@ __device__ __forceinline__ void decode_worker(const DecodeParams& p, char (*lds_
           }
         };
         auto qk_step = [&]<int G>() __attribute__((always_inline)) {
-          constexpr int kt = G / kKs, ks = G % kKs;
-          const f32x4 c = ks == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : s[kt];
-          s[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[G], qf[ks], c, 0, 0, 0);
-          if constexpr (G + kKAhead < kQk) kf[G + kKAhead] = read_k((G + kKAhead) / kKs, (G + kKAhead) % kKs);
+          constexpr int i = G % 2, ks = G / 2;
+          const f32x4 c = ks == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : s[i];
+          s[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[G], qf[ks], c, 0, 0, 0);
+          if constexpr (G + kKAhead < kQk) kf[G + kKAhead] = read_k(2 * kh + (G + kKAhead) % 2, (G + kKAhead) / 2);
           dma_step.template operator()<G>();
           __builtin_amdgcn_sched_barrier(0);
         };
@@ -438,76 +443,75 @@ __device__ __forceinline__ void decode_worker(const DecodeParams& p, char (*lds_
         }
 
         // ---- softmax weights (base 2) against the row reference ----
-        // Lane (col, grp4) holds, for the score row, key key0 + 16kt + 4*grp4 + i
-        // in s[kt][i].  Keys the row may not see get weight 0; masking is
-        // needed only on a page that holds such keys (the sequence's last page,
-        // or causal rows), a uniform test.
-        float x[4][4];
+        // Lane (col, grp4) holds, for the score row, key key0 + 16*(2kh+i) +
+        // 4*grp4 + e in s[i][e].  Keys the row may not see get weight 0;
+        // masking is needed only on a page that holds such keys (the
+        // sequence's last page, or causal rows), a uniform test.
+        float x[2][4];
 #pragma unroll
-        for (int kt = 0; kt < 4; ++kt)
+        for (int i = 0; i < 2; ++i)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) x[kt][i] = s[kt][i];
+          for (int e = 0; e < 4; ++e) x[i][e] = s[i][e];
         if (key0 + kPage > n_vis_min) {
 #pragma unroll
-          for (int kt = 0; kt < 4; ++kt)
+          for (int i = 0; i < 2; ++i)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const int key = key0 + 16 * kt + 4 * grp4 + i;
-              x[kt][i] = key < n_vis ? x[kt][i] : kNegInf;
+            for (int e = 0; e < 4; ++e) {
+              const int key = key0 + 16 * (2 * kh + i) + 4 * grp4 + e;
+              x[i][e] = key < n_vis ? x[i][e] : kNegInf;
             }
         }
         // This lane's maximum raw score (the scale is > 0), in log2 units.
-        float xm = kNegInf;
-#pragma unroll
-        for (int kt = 0; kt < 4; ++kt)
-          xm = max2(xm, max2(max2(x[kt][0], x[kt][1]), max2(x[kt][2], x[kt][3])));
+        float xm = max2(max2(max2(x[0][0], x[0][1]), max2(x[0][2], x[0][3])),
+                        max2(max2(x[1][0], x[1][1]), max2(x[1][2], x[1][3])));
         xm *= p.scale_log2;
         if (!second_pass && cpage == seg_page0) {
           // First page of the segment: the reference is the row's maximum over
-          // the page, so a sequence that fits in one page has its largest
-          // weight exactly 1.
-          m_ref = row_max4(xm);
+          // the page (both key halves, swapped through LDS), so a sequence
+          // that fits in one page has its largest weight exactly 1.
+          const float hmax = row_max4(xm);
+          if (grp4 == 0) sh.x[kh][srow] = hmax;
+          __syncthreads();
+          m_ref = max2(sh.x[0][srow], sh.x[1][srow]);
         }
         // A row with no reference yet that sees a key here, or a score far
         // above the reference, voids the segment's result for this pass.
         overflow |= xm > m_ref + kOverflowThreshold;
         m_seen = max2(m_seen, xm);
         const float mu = m_ref == kNegInf ? 0.f : m_ref;
-        uint32_t pk[4][2];
+        uint32_t pk[2][2];
 #pragma unroll
-        for (int kt = 0; kt < 4; ++kt)
+        for (int i = 0; i < 2; ++i)
 #pragma unroll
           for (int h = 0; h < 2; ++h) {
-            const float w0 = __builtin_amdgcn_exp2f(__builtin_fmaf(x[kt][2 * h], p.scale_log2, -mu));
-            const float w1 = __builtin_amdgcn_exp2f(__builtin_fmaf(x[kt][2 * h + 1], p.scale_log2, -mu));
+            const float w0 = __builtin_amdgcn_exp2f(__builtin_fmaf(x[i][2 * h], p.scale_log2, -mu));
+            const float w1 = __builtin_amdgcn_exp2f(__builtin_fmaf(x[i][2 * h + 1], p.scale_log2, -mu));
             l_run += w0 + w1;
-            pk[kt][h] = pack_bf16x2(w0, w1);
+            pk[i][h] = pack_bf16x2(w0, w1);
           }
-        // Slot 8*grp4 + 4*(kt&1) + i of k-step kk = kt>>1 holds key 16*(kt&1) + 4*grp4 + i.
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk)
-          *(__attribute__((address_space(3))) u32x4*)(pw + (uint32_t)(kk * 64)) =
-              u32x4{pk[2 * kk][0], pk[2 * kk][1], pk[2 * kk + 1][0], pk[2 * kk + 1][1]};
+        // Slot 8*grp4 + 4*i + e of k-step kk = kh holds key 32kh + 16i + 4*grp4 + e.
+        *(__attribute__((address_space(3))) u32x4*)(pw + (uint32_t)(kh * 64)) =
+            u32x4{pk[0][0], pk[0][1], pk[1][0], pk[1][1]};
         __syncthreads();            // P of all 64 rows is in LDS
 
-        // ---- outputs: O^T += V^T P^T, 8 column tiles x 4 row tiles per k-step ----
-        // 64 MFMAs in issue order (kk, d, t); V fragments kVAhead ahead; the
+        // ---- outputs: O^T += V^T P^T, 4 column tiles x 4 row tiles per k-step ----
+        // 32 MFMAs in issue order (kk, d, t); V fragments kVAhead ahead; the
         // four P fragments of a k-step read before its first MFMA.
         constexpr int kVAhead = 3;
-        bf16x8 vf[2][8], pfr[2][4];
+        bf16x8 vf[2][4], pfr[2][4];
 #pragma unroll
         for (int t = 0; t < 4; ++t) pfr[0][t] = read_p(0, t);
 #pragma unroll
         for (int d = 0; d < kVAhead; ++d) vf[0][d] = read_v(0, d);
         __builtin_amdgcn_sched_barrier(0);
         auto pv_step = [&]<int G>() __attribute__((always_inline)) {
-          constexpr int n = G - kQk, kk = n / 32, d = (n % 32) / 4, t = n % 4;
+          constexpr int n = G - kQk, kk = n / 16, d = (n % 16) / 4, t = n % 4;
           acc[d][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[kk][d], pfr[kk][t], acc[d][t], 0, 0, 0);
           if constexpr (t == 3) {
-            constexpr int nv = kk * 8 + d + kVAhead;   // next V fragment to read
-            if constexpr (nv < 16) vf[nv / 8][nv % 8] = read_v(nv / 8, nv % 8);
+            constexpr int nv = kk * 4 + d + kVAhead;   // next V fragment to read
+            if constexpr (nv < 8) vf[nv / 4][nv % 4] = read_v(nv / 4, nv % 4);
           }
-          if constexpr (kk == 0 && d == 5) pfr[1][t] = read_p(1, t);
+          if constexpr (kk == 0 && d == 1) pfr[1][t] = read_p(1, t);
           dma_step.template operator()<G>();
           __builtin_amdgcn_sched_barrier(0);
         };
@@ -528,7 +532,12 @@ __device__ __forceinline__ void decode_worker(const DecodeParams& p, char (*lds_
       // again with every row's maximum over it as the reference, so that no
       // weight exceeds 1.  The DMAs in flight (the worker's next page) are
       // drained and the load pipeline restarts at the segment's first page.
-      m_ref = row_max4(m_seen);
+      {
+        const float hmax = row_max4(m_seen);
+        if (grp4 == 0) sh.x[kh][srow] = hmax;
+        __syncthreads();
+        m_ref = max2(sh.x[0][srow], sh.x[1][srow]);
+      }
       second_pass = true;
       wait_dma_all();
       __syncthreads();
@@ -548,10 +557,12 @@ __device__ __forceinline__ void decode_worker(const DecodeParams& p, char (*lds_
 
     // ---------------- segment epilogue ----------------
     {
-      // Row sums, swapped through LDS for the output waves.
-      const float l_row = row_sum4(l_run);
-      if (grp4 == 0) {
-        sh.x[srow] = l_row;
+      // Row sums: each key half's share, swapped through LDS.
+      const float l_half = row_sum4(l_run);
+      if (grp4 == 0) sh.x[kh][srow] = l_half;
+      __syncthreads();
+      if (kh == 0 && grp4 == 0) {
+        const float l_row = sh.x[0][srow] + sh.x[1][srow];
         const int qrow = rb * kRowsPerBlock + srow;
         const float lse_nat = l_row == 0.f ? kNegInf : (m_ref + __log2f(l_row)) * 0.69314718055994531f;
         if (qrow < p.rows) {
@@ -561,25 +572,24 @@ __device__ __forceinline__ void decode_worker(const DecodeParams& p, char (*lds_
             p.ws_lse[(size_t)(slot * p.h_kv + g) * p.rows + qrow] = lse_nat;
         }
       }
-      __syncthreads();
-      // O: lane (col, grp4) holds O[16t + col][128*wave + 16d + 4*grp4 + i] in acc[d][t][i].
+      // O: lane (col, grp4) holds O[16t + col][64*wave + 16d + 4*grp4 + i] in acc[d][t][i].
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         const int r = 16 * t + col;
         const int qrow = rb * kRowsPerBlock + r;
-        const float l = sh.x[r];
+        const float l = sh.x[0][r] + sh.x[1][r];
         const float inv = l == 0.f ? 0.f : 1.f / l;
         if (qrow < p.rows) {
           if (nsplit == 1) {
-            uint16_t* op = p.o + ((size_t)(b * p.s_q + row_tok(r)) * p.h_q + row_head(r)) * kDv + 128 * wave + 4 * grp4;
+            uint16_t* op = p.o + ((size_t)(b * p.s_q + row_tok(r)) * p.h_q + row_head(r)) * kDv + 64 * wave + 4 * grp4;
 #pragma unroll
-            for (int d = 0; d < 8; ++d)
+            for (int d = 0; d < 4; ++d)
               *(u32x2*)(op + 16 * d) = u32x2{pack_bf16x2(acc[d][t][0] * inv, acc[d][t][1] * inv),
                                              pack_bf16x2(acc[d][t][2] * inv, acc[d][t][3] * inv)};
           } else {
-            float* wp = p.ws_o + ((size_t)(slot * p.h_kv + g) * p.rows + qrow) * kDv + 128 * wave + 4 * grp4;
+            float* wp = p.ws_o + ((size_t)(slot * p.h_kv + g) * p.rows + qrow) * kDv + 64 * wave + 4 * grp4;
 #pragma unroll
-            for (int d = 0; d < 8; ++d) *(f32x4*)(wp + 16 * d) = acc[d][t] * inv;
+            for (int d = 0; d < 4; ++d) *(f32x4*)(wp + 16 * d) = acc[d][t] * inv;
           }
         }
       }

@@ -10,14 +10,13 @@ constexpr int kPage = 64;                          // tokens per cache page
 constexpr int kDqk = 576;                          // latent row: c^KV (512) + k^R (64)
 constexpr int kDv = 512;                           // value width = c^KV
 constexpr int kRowsPerBlock = 64;                  // query rows one decode workgroup serves
-constexpr int kWaves = 4;                          // 64-lane waves per decode workgroup
+constexpr int kWaves = 8;                          // 64-lane waves per decode workgroup (2 per SIMD)
 constexpr int kThreads = kWaves * 64;
-constexpr int kRowsPerWave = kRowsPerBlock / kWaves;   // 16 = one MFMA 16x16 tile
 constexpr int kRowBytes = kDqk * 2;                // 1152 bytes of bf16
 constexpr int kChunksPerRow = kRowBytes / 16;      // 72 chunks of 16 bytes
 constexpr int kPageBytes = kPage * kRowBytes;      // 73728 bytes staged in LDS per page
 constexpr int kPageChunks = kPage * kChunksPerRow; // 4608
-constexpr int kLdsDmaPerWave = kPageChunks / 64 / kWaves;  // 18 wave-wide 16-byte DMA loads
+constexpr int kLdsDmaPerWave = kPageChunks / 64 / kWaves;  // 9 wave-wide 16-byte DMA loads
 constexpr int kNumXcd = 8;                         // MI355X: 8 XCDs, round-robin block dispatch
 constexpr int kMetaInts = 8;
 constexpr int kMaxWorkers = 4096;
