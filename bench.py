@@ -176,6 +176,7 @@ def main():
     for i in range(args.steps):
         step(i)
     g1.record()
+    launch_ms = (time.perf_counter() - t_start) * 1e3      # host time to issue the steps
     torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - t_start) * 1e3
     ms_per_step = wall_ms / args.steps
@@ -204,7 +205,7 @@ def main():
     torch.cuda.synchronize()
     decode_b2b_ms = d0.elapsed_time(d1) / n_dec
     print(f"[bench] {args.steps} steps: {ms_per_step * 1e3:.1f} us/step (wall), "
-          f"{event_ms_per_step * 1e3:.1f} us/step (events), decode kernel "
+          f"{event_ms_per_step * 1e3:.1f} us/step (events), host issue {launch_ms / args.steps * 1e3:.1f} us/step, decode kernel "
           f"{decode_ms.mean() * 1e3:.1f} us in step ({decode_b2b_ms * 1e3:.1f} us back to back), "
           f"combine {combine_ms.mean() * 1e3:.1f} us", file=sys.stderr, flush=True)
 

@@ -56,9 +56,13 @@ __global__ __launch_bounds__(kCombineRowsPerBlock * 64) void mla_combine_kernel(
   const int head = g * p.group + (row - tok * p.group);
   uint16_t* op = p.o + ((size_t)(b * p.s_q + tok) * p.h_q + head) * kDv + lane * 8;
   float* lp = p.lse + ((size_t)b * p.h_q + head) * p.s_q + tok;
+  // lse_s of split s sits at lse0[s * stride]; its O_s row at o0 + s * stride * kDv.
+  const size_t stride = (size_t)p.h_kv * p.rows;
+  const float* lse0 = p.ws_lse + (size_t)(s0 * p.h_kv + g) * p.rows + row;
+  const float* o0 = p.ws_o + ((size_t)(s0 * p.h_kv + g) * p.rows + row) * kDv + lane * 8;
 
   float M = -__builtin_huge_valf();
-  for (int i = lane; i < n; i += 64) M = fmaxf(M, p.ws_lse[(size_t)((s0 + i) * p.h_kv + g) * p.rows + row]);
+  for (int i = lane; i < n; i += 64) M = fmaxf(M, lse0[(size_t)i * stride]);
   M = wave_reduce_max(M);
   if (n == 0 || M == -__builtin_huge_valf()) {
     *(uint4*)op = uint4{0, 0, 0, 0};
@@ -66,17 +70,52 @@ __global__ __launch_bounds__(kCombineRowsPerBlock * 64) void mla_combine_kernel(
     return;
   }
   float z = 0.f;
-  for (int i = lane; i < n; i += 64) z += expf(p.ws_lse[(size_t)((s0 + i) * p.h_kv + g) * p.rows + row] - M);
+  for (int i = lane; i < n; i += 64) z += expf(lse0[(size_t)i * stride] - M);
   z = wave_reduce_sum(z);
   const float lse = M + logf(z);
 
+  // Splits in slot order, four (then two) at a time so that their loads are
+  // in flight together; each lane reads 32 bytes of each split's row.
   f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
-  for (int i = 0; i < n; ++i) {
-    const size_t base = (size_t)((s0 + i) * p.h_kv + g) * p.rows + row;
-    const float w = expf(p.ws_lse[base] - lse);
-    const f32x4* src = (const f32x4*)(p.ws_o + base * kDv + lane * 8);
-    a0 += w * src[0];
-    a1 += w * src[1];
+  int i = 0;
+  for (; i + 4 <= n; i += 4) {
+    f32x4 v[4][2];
+    float w[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const f32x4* src = (const f32x4*)(o0 + (size_t)(i + k) * stride * kDv);
+      v[k][0] = *(src);
+      v[k][1] = *(src + 1);
+      w[k] = expf(lse0[(size_t)(i + k) * stride] - lse);
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      a0 += w[k] * v[k][0];
+      a1 += w[k] * v[k][1];
+    }
+  }
+  if (i + 2 <= n) {
+    f32x4 v[2][2];
+    float w[2];
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const f32x4* src = (const f32x4*)(o0 + (size_t)(i + k) * stride * kDv);
+      v[k][0] = *(src);
+      v[k][1] = *(src + 1);
+      w[k] = expf(lse0[(size_t)(i + k) * stride] - lse);
+    }
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      a0 += w[k] * v[k][0];
+      a1 += w[k] * v[k][1];
+    }
+    i += 2;
+  }
+  if (i < n) {
+    const f32x4* src = (const f32x4*)(o0 + (size_t)i * stride * kDv);
+    const float w = expf(lse0[(size_t)i * stride] - lse);
+    a0 += w * *(src);
+    a1 += w * *(src + 1);
   }
   uint4 v;
   v.x = pack_bf16x2(a0[0], a0[1]);
