@@ -197,18 +197,22 @@ __device__ inline bool next_page(const int32_t* meta, const int32_t* seqlens, in
   return false;
 }
 
-// Page that step `page` of segment [p0, end) processes.  The two row blocks
-// of a head read the same pages, and each page's fetch takes its full memory
-// latency while its twin in the other block is still in flight.  So odd row
-// blocks swap the pages after the first in pairs (p0, p0+2, p0+1, p0+4,
-// p0+3, ...): every other page a block fetches is the one its twin fetched a
-// page earlier, an L2 hit, and the two blocks together keep two pages in
-// flight.  The first page, whose maxima set the softmax references, stays
-// first in both blocks.  The result does not otherwise depend on the order.
-__device__ inline int page_in_order(int page, int p0, int end, bool swap) {
-  const int j = page - p0;
-  const int jj = ((j - 1) ^ 1) + 1;
-  return swap && j >= 1 && p0 + jj < end ? p0 + jj : page;
+// Page that step `page` of segment [p0, end) processes, in row block rb of
+// nrb.  The row blocks of a head read the same pages, and a page's fetch
+// takes its full memory latency while its twins in the other blocks are in
+// flight for the same page.  So after the segment's first page (whose maxima
+// set the softmax references, first in every block), pages go in groups of
+// nrb, and block rb takes a group's pages rotated by rb: at each group step
+// every block fetches a different page, and a page is fetched from memory by
+// one block and found in L2 by the others.  A last, partial group keeps its
+// order.  The result does not otherwise depend on the order.
+__device__ inline int page_in_order(int page, int p0, int end, int rb, int nrb) {
+  const int j = page - p0 - 1;
+  if (j < 0 || nrb == 1) return page;
+  const int base = p0 + 1 + (j / nrb) * nrb;
+  if (base + nrb > end) return page;
+  const int r = j - (j / nrb) * nrb + rb;
+  return base + (r >= nrb ? r - nrb : r);
 }
 
 }  // namespace
@@ -256,7 +260,7 @@ __device__ __forceinline__ void decode_worker(const DecodeParams& p, char (*lds_
   int cb = meta_b0, cpage = ld_uniform(meta + 1), cend = segment_end(meta, p.seqlens, cb);
   if (cpage >= cend) return;
   int lb = cb, lpage = cpage, lend = cend, lp0 = cpage;
-  const bool swap = rb & 1;
+  const int nrb = p.row_blocks;
   bool lvalid = true;
 
   const int row_stride_bytes = kSingleHead ? kRowBytes : p.h_kv * kRowBytes;   // bytes between tokens
@@ -306,11 +310,11 @@ __device__ __forceinline__ void decode_worker(const DecodeParams& p, char (*lds_
   // is read now, one page ahead of its DMAs.
   int next_pid = 0;
   {
-    const int page_id = ld_uniform(p.block_table + (size_t)lb * p.max_pages + page_in_order(lpage, lp0, lend, swap));
+    const int page_id = ld_uniform(p.block_table + (size_t)lb * p.max_pages + page_in_order(lpage, lp0, lend, rb, nrb));
     lvalid = next_page(meta, p.seqlens, lb, lpage, lend, lp0);
     stage_page(kv_head + (size_t)page_id * page_stride_bytes, page_span, lane_src_off, row_stride_bytes,
                lds_base, wave);
-    if (lvalid) next_pid = ld_uniform(p.block_table + (size_t)lb * p.max_pages + page_in_order(lpage, lp0, lend, swap));
+    if (lvalid) next_pid = ld_uniform(p.block_table + (size_t)lb * p.max_pages + page_in_order(lpage, lp0, lend, rb, nrb));
   }
 
   int it = 0;
@@ -360,7 +364,7 @@ __device__ __forceinline__ void decode_worker(const DecodeParams& p, char (*lds_
         wait_dma_all();
         __syncthreads();
         char* buf = lds_page[it & 1];
-        const int ppage = page_in_order(cpage, seg_page0, cend, swap);   // the page this step processes
+        const int ppage = page_in_order(cpage, seg_page0, cend, rb, nrb);   // the page this step processes
         const int valid = min(kPage, L - ppage * kPage);
         if (valid < kPage) {
           zero_tail_rows(buf, valid, tid);
@@ -439,7 +443,7 @@ __device__ __forceinline__ void decode_worker(const DecodeParams& p, char (*lds_
         // read here, where waiting for the scalar load costs nothing.
         if (lvalid) {
           lvalid = next_page(meta, p.seqlens, lb, lpage, lend, lp0);
-          if (lvalid) next_pid = ld_uniform(p.block_table + (size_t)lb * p.max_pages + page_in_order(lpage, lp0, lend, swap));
+          if (lvalid) next_pid = ld_uniform(p.block_table + (size_t)lb * p.max_pages + page_in_order(lpage, lp0, lend, rb, nrb));
         }
 
         // ---- softmax weights (base 2) against the row reference ----
@@ -547,11 +551,11 @@ __device__ __forceinline__ void decode_worker(const DecodeParams& p, char (*lds_
       lp0 = seg_page0;
       cpage = seg_page0;
       {
-        const int page_id = ld_uniform(p.block_table + (size_t)lb * p.max_pages + page_in_order(lpage, lp0, lend, swap));
+        const int page_id = ld_uniform(p.block_table + (size_t)lb * p.max_pages + page_in_order(lpage, lp0, lend, rb, nrb));
         lvalid = next_page(meta, p.seqlens, lb, lpage, lend, lp0);
         stage_page(kv_head + (size_t)page_id * page_stride_bytes, page_span, lane_src_off, row_stride_bytes,
                    lds_base + (it & 1) * kPageBytes, wave);
-        if (lvalid) next_pid = ld_uniform(p.block_table + (size_t)lb * p.max_pages + page_in_order(lpage, lp0, lend, swap));
+        if (lvalid) next_pid = ld_uniform(p.block_table + (size_t)lb * p.max_pages + page_in_order(lpage, lp0, lend, rb, nrb));
       }
     }
 

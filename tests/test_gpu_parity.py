@@ -37,7 +37,8 @@ SHAPES = [
     (1, 128, 1, False, [1, 63, 64, 65, 200, 1000]),
     (1, 64, 1, False, [130, 7, 777]),              # half-empty row block
     (1, 96, 1, False, [300, 2]),
-    (1, 200, 1, False, [129, 64]),                 # two row blocks, ragged second
+    (1, 200, 1, False, [129, 64]),                 # four row blocks, ragged last
+    (3, 64, 1, True, [700, 33, 1200]),             # causal, three row blocks (rotated page groups)
     (2, 128, 1, True, [1, 2, 3, 64, 65, 513]),     # causal s_q = 2, 256 rows
     (3, 16, 1, True, [1, 2, 5, 70]),               # rows that see nothing
     (1, 128, 2, False, [100, 257]),                # two latent heads
