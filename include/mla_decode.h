@@ -140,6 +140,20 @@ int mla_decode_splitkv(const void* q, const void* kvcache, const int32_t* block_
                        int num_workers, int causal, float softmax_scale, void* o, float* lse,
                        void* workspace, size_t workspace_bytes, void* stream);
 
+/* mla_decode_splitkv with its kernel timed: start_event and stop_event are
+ * HIP events (hipEvent_t, created by the caller, not null) that the kernel
+ * dispatch itself records when the decode kernel starts and when it ends, so
+ * that the time between them is the kernel's own, without the dispatch gap
+ * or end-of-launch cache write-back that events recorded on the stream
+ * around the launch also span.  For measurement; same checks otherwise. */
+int mla_decode_splitkv_timed(const void* q, const void* kvcache, const int32_t* block_table,
+                             int max_pages_per_seq, int num_pages, const int32_t* cache_seqlens,
+                             int batch, int s_q, int h_q, int h_kv, int d_qk, int dv,
+                             const int32_t* tile_scheduler_metadata, const int32_t* num_splits,
+                             int num_workers, int causal, float softmax_scale, void* o, float* lse,
+                             void* workspace, size_t workspace_bytes, void* stream,
+                             void* start_event, void* stop_event);
+
 /* The last launch alone: the log-sum-exp merge.  For each sequence with
  * n_b = num_splits[b+1] - num_splits[b] partials: n_b = 0 writes O = 0 and
  * LSE = -inf, n_b = 1 leaves what the decode kernel wrote, n_b > 1 writes

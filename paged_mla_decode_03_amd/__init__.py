@@ -4,9 +4,9 @@ The work runs in ``libmla_decode.so`` (hand-written HIP kernels behind a C ABI,
 ``include/mla_decode.h``); ``binding`` marshals torch tensors into it.
 """
 from .binding import (DecodeBuffers, MlaError, fixed_overhead_pages, get_mla_metadata, library,
-                      mla_combine_splits, mla_decode_paged, mla_decode_splitkv,
+                      mla_combine_splits, mla_decode_paged, mla_decode_splitkv, mla_decode_splitkv_timed,
                       num_workers, workspace_bytes)
 
 __all__ = ["DecodeBuffers", "MlaError", "fixed_overhead_pages", "get_mla_metadata", "library",
-           "mla_combine_splits", "mla_decode_paged", "mla_decode_splitkv", "num_workers",
+           "mla_combine_splits", "mla_decode_paged", "mla_decode_splitkv", "mla_decode_splitkv_timed", "num_workers",
            "workspace_bytes"]

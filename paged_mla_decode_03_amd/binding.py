@@ -65,6 +65,8 @@ def _load():
         f = getattr(lib, name)
         f.restype = c_int
         f.argtypes = decode_args
+    lib.mla_decode_splitkv_timed.restype = c_int
+    lib.mla_decode_splitkv_timed.argtypes = decode_args + [vp, vp]
     lib.mla_combine_splits.restype = c_int
     lib.mla_combine_splits.argtypes = [vp, c_int, c_int, c_int, c_int, c_int, c_int, vp, vp, vp, c_size_t, vp]
     _lib = lib
@@ -127,7 +129,7 @@ def workspace_bytes(batch: int, s_q: int, h_q: int, h_kv: int, dv: int, W: int) 
 
 
 def _decode_call(entry: str, q, kvcache, block_table, cache_seqlens, dv, tile_scheduler_metadata, num_splits,
-                 causal, softmax_scale, o, lse, workspace):
+                 causal, softmax_scale, o, lse, workspace, *extra):
     device = q.device
     B, s_q, h_q, d_qk = q.shape
     P, page, h_kv, d2 = kvcache.shape
@@ -137,7 +139,7 @@ def _decode_call(entry: str, q, kvcache, block_table, cache_seqlens, dv, tile_sc
         q.data_ptr(), kvcache.data_ptr(), block_table.data_ptr(), block_table.shape[1], P,
         cache_seqlens.data_ptr(), B, s_q, h_q, h_kv, d_qk, dv, tile_scheduler_metadata.data_ptr(),
         num_splits.data_ptr(), W, int(bool(causal)), float(softmax_scale or 0.0), o.data_ptr(), lse.data_ptr(),
-        workspace.data_ptr(), workspace.numel(), stream))
+        workspace.data_ptr(), workspace.numel(), stream, *extra))
 
 
 class DecodeBuffers:
@@ -193,6 +195,24 @@ def mla_decode_splitkv(q, kvcache, block_table, cache_seqlens, dv, tile_schedule
         buffers = DecodeBuffers(q, kvcache, dv, tile_scheduler_metadata.shape[0])
     _decode_call("mla_decode_splitkv", q, kvcache, block_table, cache_seqlens, dv, tile_scheduler_metadata,
                  num_splits, causal, softmax_scale, buffers.o, buffers.lse, buffers.workspace)
+    return buffers
+
+
+def mla_decode_splitkv_timed(q, kvcache, block_table, cache_seqlens, dv, tile_scheduler_metadata, num_splits,
+                             start: torch.cuda.Event, stop: torch.cuda.Event, causal=False, softmax_scale=None,
+                             buffers: Optional[DecodeBuffers] = None):
+    """mla_decode_splitkv with the kernel's own start and end recorded into
+    two timing events by the dispatch (start.elapsed_time(stop) after
+    stop.synchronize())."""
+    _validate(q, kvcache, block_table, cache_seqlens, tile_scheduler_metadata, num_splits)
+    if buffers is None:
+        buffers = DecodeBuffers(q, kvcache, dv, tile_scheduler_metadata.shape[0])
+    for e in (start, stop):
+        if not e.cuda_event:     # torch creates the HIP event on its first record
+            e.record()
+    _decode_call("mla_decode_splitkv_timed", q, kvcache, block_table, cache_seqlens, dv, tile_scheduler_metadata,
+                 num_splits, causal, softmax_scale, buffers.o, buffers.lse, buffers.workspace,
+                 start.cuda_event, stop.cuda_event)
     return buffers
 
 

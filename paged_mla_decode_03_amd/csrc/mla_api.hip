@@ -4,6 +4,8 @@
 #include <math.h>
 #include <mutex>
 
+#include <hip/hip_ext.h>
+
 #include "../../include/mla_decode.h"
 #include "mla_kernels.h"
 
@@ -118,13 +120,22 @@ mla::DecodeParams decode_params(const void* q, const void* kvcache, const int32_
   return p;
 }
 
-int launch_decode(const mla::DecodeParams& p, hipStream_t stream) {
+// With start/stop events, the dispatch itself records them when the kernel
+// starts and ends (hipExtLaunchKernelGGL).
+int launch_decode(const mla::DecodeParams& p, hipStream_t stream, hipEvent_t start = nullptr,
+                  hipEvent_t stop = nullptr) {
   const int groups = p.num_workers * p.h_kv;
   const int blocks = (groups + mla::kNumXcd - 1) / mla::kNumXcd * mla::kNumXcd * p.row_blocks;
-  if (p.h_kv == 1)
+  if (start || stop) {
+    if (p.h_kv == 1)
+      hipExtLaunchKernelGGL(mla::mla_decode_kernel<true>, dim3(blocks), dim3(mla::kThreads), 0, stream, start, stop, 0, p);
+    else
+      hipExtLaunchKernelGGL(mla::mla_decode_kernel<false>, dim3(blocks), dim3(mla::kThreads), 0, stream, start, stop, 0, p);
+  } else if (p.h_kv == 1) {
     hipLaunchKernelGGL(mla::mla_decode_kernel<true>, dim3(blocks), dim3(mla::kThreads), 0, stream, p);
-  else
+  } else {
     hipLaunchKernelGGL(mla::mla_decode_kernel<false>, dim3(blocks), dim3(mla::kThreads), 0, stream, p);
+  }
   return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
 
@@ -215,6 +226,22 @@ int mla_decode_splitkv(const void* q, const void* kvcache, const int32_t* block_
   const mla::DecodeParams p = decode_params(q, kvcache, block_table, max_pages_per_seq, cache_seqlens, s, meta,
                                             num_splits, num_workers, causal, softmax_scale, o, lse, workspace);
   return launch_decode(p, (hipStream_t)stream);
+}
+
+int mla_decode_splitkv_timed(const void* q, const void* kvcache, const int32_t* block_table, int max_pages_per_seq,
+                             int num_pages, const int32_t* cache_seqlens, int batch, int s_q, int h_q, int h_kv,
+                             int d_qk, int dv, const int32_t* meta, const int32_t* num_splits, int num_workers,
+                             int causal, float softmax_scale, void* o, float* lse, void* workspace,
+                             size_t workspace_bytes_given, void* stream, void* start_event, void* stop_event) {
+  Shape s;
+  int st = check_decode(q, kvcache, block_table, max_pages_per_seq, num_pages, cache_seqlens, batch, s_q, h_q,
+                        h_kv, d_qk, dv, meta, num_splits, num_workers, causal, o, lse, workspace,
+                        workspace_bytes_given, &s);
+  if (st != MLA_OK) return st;
+  if (!start_event || !stop_event) return MLA_ERR_INVALID_ARG;
+  const mla::DecodeParams p = decode_params(q, kvcache, block_table, max_pages_per_seq, cache_seqlens, s, meta,
+                                            num_splits, num_workers, causal, softmax_scale, o, lse, workspace);
+  return launch_decode(p, (hipStream_t)stream, (hipEvent_t)start_event, (hipEvent_t)stop_event);
 }
 
 int mla_combine_splits(const int32_t* num_splits, int batch, int s_q, int h_q, int h_kv, int dv,

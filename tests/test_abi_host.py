@@ -29,7 +29,7 @@ def declared_functions():
 def test_header_declares_the_boundary():
     names = set(declared_functions())
     assert {"mla_get_metadata", "mla_decode_paged", "mla_num_workers", "mla_workspace_bytes",
-            "mla_status_string", "mla_decode_splitkv", "mla_combine_splits",
+            "mla_status_string", "mla_decode_splitkv", "mla_decode_splitkv_timed", "mla_combine_splits",
             "mla_sched_fixed_overhead"} <= names
 
 
@@ -92,6 +92,20 @@ def _decode(lib, entry="mla_decode_paged", **kw):
 @pytest.mark.parametrize("entry", ["mla_decode_paged", "mla_decode_splitkv"])
 def test_decode_rejects_invalid_arguments(kw, status, entry):
     assert _decode(_lib(), entry, **kw) == status
+
+
+def test_timed_decode_rejects_invalid_arguments():
+    lib = _lib()
+    args = dict(q=FAKE, kv=FAKE, bt=FAKE, max_pages=4, num_pages=8, seqlens=FAKE, batch=2, s_q=1, h_q=16,
+                h_kv=1, d_qk=576, dv=512, meta=FAKE, ns=FAKE, W=256, causal=0, scale=0.0, o=FAKE, lse=FAKE,
+                ws=FAKE, ws_bytes=1 << 30, stream=None)
+    # the same checks as mla_decode_splitkv, then both events are required
+    assert lib.mla_decode_splitkv_timed(*args.values(), FAKE, None) == -1
+    assert lib.mla_decode_splitkv_timed(*args.values(), None, FAKE) == -1
+    args.update(q=None)
+    assert lib.mla_decode_splitkv_timed(*args.values(), FAKE, FAKE) == -1
+    args.update(q=FAKE, ws_bytes=1024)
+    assert lib.mla_decode_splitkv_timed(*args.values(), FAKE, FAKE) == -3
 
 
 def test_metadata_and_combine_reject_invalid_arguments():

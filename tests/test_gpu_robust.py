@@ -99,3 +99,23 @@ def test_zero_length_sequences_write_zero_and_neg_inf():
     assert np.isneginf(lse[0]).all() and np.isneginf(lse[2]).all()
     O, LSE = oracle(inp)
     compare(o, lse, O, LSE, label="zero-length")
+
+
+def test_timed_decode_matches_untimed_and_times_the_kernel():
+    """mla_decode_splitkv_timed runs the same kernel (bitwise the same
+    outputs) and its dispatch-recorded events bracket a positive duration."""
+    from paged_mla_decode_03_amd import mla_decode_splitkv, mla_decode_splitkv_timed
+    inp = _custom(1, 128, False, [70, 1300, 5], 4)
+    q, kv, bt, L = to_dev(inp)
+    meta, ns = get_mla_metadata(L, 128, 1, 17)
+    a = DecodeBuffers(q, kv, 512, 17)
+    b = DecodeBuffers(q, kv, 512, 17)
+    mla_decode_splitkv(q, kv, bt, L, 512, meta, ns, buffers=a)
+    mla_combine_splits(ns, 1, 128, 1, 512, 17, a)
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    mla_decode_splitkv_timed(q, kv, bt, L, 512, meta, ns, start, stop, buffers=b)
+    mla_combine_splits(ns, 1, 128, 1, 512, 17, b)
+    stop.synchronize()
+    ms = start.elapsed_time(stop)
+    assert 0 < ms < 1000, ms
+    assert torch.equal(a.o, b.o) and torch.equal(a.lse, b.lse)
