@@ -51,10 +51,16 @@ def parse():
 
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
-    for name in ("mla_decode.hip", "mla_kernels.h"):
+    for name in ("mla_decode.hip", "mla_decode_wide.hip", "mla_decode_common.h", "mla_kernels.h"):
         with open(os.path.join(ROOT, "paged_mla_decode_03_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
+
+
+def decode_kernel_name(w) -> str:
+    """The decode kernel a workload runs: 128-row workgroups above 128 query
+    rows per latent head, else 64-row ones."""
+    return "mla_decode_wide_kernel" if w.s_q * w.h_q // w.h_kv > 128 else "mla_decode_kernel"
 
 
 def measured_traffic(workload: str):
@@ -274,7 +280,7 @@ def main():
         "metadata_us": round(metadata_us, 2),
         "algorithmic_bytes": counts["total_bytes"],
         "algorithmic_flops": counts["flops"],
-        "roofline": {"kernel": "mla_decode_kernel", "bound": bound, "achieved": round(achieved, 2),
+        "roofline": {"kernel": decode_kernel_name(w), "bound": bound, "achieved": round(achieved, 2),
                      "peak": peak, "unit": unit, "frac": round(achieved / peak, 4),
                      "traffic": traffic,
                      "per_launch": {"bytes": counts["total_bytes"], "flops": counts["flops"]}},

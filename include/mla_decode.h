@@ -59,15 +59,18 @@ extern "C" {
 #define MLA_D_QK 576
 #define MLA_D_V 512
 #define MLA_METADATA_INTS 8       /* ints per worker row of tile_scheduler_metadata */
-#define MLA_ROWS_PER_BLOCK 64     /* query rows one workgroup serves */
+#define MLA_ROWS_PER_BLOCK 64     /* query rows one workgroup serves when rows_per_kv <= 128 ... */
+#define MLA_ROWS_PER_WIDE_BLOCK 128  /* ... and when rows_per_kv > 128 */
 #define MLA_MAX_WORKERS 4096
 
 /* Text for a status code (static storage, never NULL). */
 const char* mla_status_string(int status);
 
 /* Number of scheduler workers W for a launch on `device` (-1 = current
- * device): W = max(1, CUs / (h_kv * ceil(rows_per_kv / 64))), capped at
- * MLA_MAX_WORKERS.  rows_per_kv = s_q * h_q / h_kv.  Host-only; reads the
+ * device): W = max(1, CUs / (h_kv * ceil(rows_per_kv / rb))), capped at
+ * MLA_MAX_WORKERS, where rows_per_kv = s_q * h_q / h_kv and rb, the query
+ * rows of one workgroup, is 64 for rows_per_kv <= 128 and 128 above (one
+ * workgroup per CU either way).  Host-only; reads the
  * device's compute-unit count once and caches it. */
 int mla_num_workers(int device, int rows_per_kv, int h_kv, int* num_workers);
 

@@ -29,8 +29,8 @@ build's own rule ("rule v1"), written as plain loops:
   segment gets (0, 0, -1, 0, 0, 0, 0, 0).  Only a worker's first segment can
   start inside a sequence, so its later segments have ordinal 0.
 
-W = max(1, N_CU // (h_kv * ceil(R / 64))) for R = s_q*h_q/h_kv query rows per
-latent head, with 64 query rows per workgroup.
+W = max(1, N_CU // (h_kv * ceil(R / rb))) for R = s_q*h_q/h_kv query rows per
+latent head, with rb = 64 query rows per workgroup for R <= 128 and 128 above.
 """
 from __future__ import annotations
 
@@ -38,12 +38,14 @@ import numpy as np
 
 PAGE_SIZE = 64
 FIXED_OVERHEAD_PAGES = 2   # F: cost of one sequence's q load and output, in page units
-ROWS_PER_BLOCK = 64
+ROWS_PER_BLOCK = 64          # query rows per workgroup for R <= 128 ...
+ROWS_PER_WIDE_BLOCK = 128    # ... and for R > 128
 METADATA_INTS = 8
 
 
 def num_workers_ref(n_cu: int, rows_per_kv: int, h_kv: int) -> int:
-    row_blocks = (rows_per_kv + ROWS_PER_BLOCK - 1) // ROWS_PER_BLOCK
+    rb = ROWS_PER_BLOCK if rows_per_kv <= ROWS_PER_WIDE_BLOCK else ROWS_PER_WIDE_BLOCK
+    row_blocks = (rows_per_kv + rb - 1) // rb
     return max(1, n_cu // (h_kv * row_blocks))
 
 

@@ -34,7 +34,12 @@ int cu_count(int device, int* out) {
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
-int row_blocks_of(int rows) { return (rows + mla::kRowsPerBlock - 1) / mla::kRowsPerBlock; }
+// Row blocks per head: 64-row workgroups for heads of up to 128 query rows,
+// 128-row workgroups above that.
+int row_blocks_of(int rows) {
+  const int per = mla::rows_per_block(rows);
+  return (rows + per - 1) / per;
+}
 
 struct Shape {
   int batch, s_q, h_q, h_kv, rows, group;
@@ -122,19 +127,28 @@ mla::DecodeParams decode_params(const void* q, const void* kvcache, const int32_
 
 // With start/stop events, the dispatch itself records them when the kernel
 // starts and ends (hipExtLaunchKernelGGL).
+template <typename Kernel>
+void launch_one(Kernel kernel, int blocks, int threads, const mla::DecodeParams& p, hipStream_t stream,
+                hipEvent_t start, hipEvent_t stop) {
+  if (start || stop)
+    hipExtLaunchKernelGGL(kernel, dim3(blocks), dim3(threads), 0, stream, start, stop, 0, p);
+  else
+    hipLaunchKernelGGL(kernel, dim3(blocks), dim3(threads), 0, stream, p);
+}
+
 int launch_decode(const mla::DecodeParams& p, hipStream_t stream, hipEvent_t start = nullptr,
                   hipEvent_t stop = nullptr) {
   const int groups = p.num_workers * p.h_kv;
   const int blocks = (groups + mla::kNumXcd - 1) / mla::kNumXcd * mla::kNumXcd * p.row_blocks;
-  if (start || stop) {
+  if (mla::rows_per_block(p.rows) == mla::kWideRows) {
     if (p.h_kv == 1)
-      hipExtLaunchKernelGGL(mla::mla_decode_kernel<true>, dim3(blocks), dim3(mla::kThreads), 0, stream, start, stop, 0, p);
+      launch_one(mla::mla_decode_wide_kernel<true>, blocks, mla::kWideThreads, p, stream, start, stop);
     else
-      hipExtLaunchKernelGGL(mla::mla_decode_kernel<false>, dim3(blocks), dim3(mla::kThreads), 0, stream, start, stop, 0, p);
+      launch_one(mla::mla_decode_wide_kernel<false>, blocks, mla::kWideThreads, p, stream, start, stop);
   } else if (p.h_kv == 1) {
-    hipLaunchKernelGGL(mla::mla_decode_kernel<true>, dim3(blocks), dim3(mla::kThreads), 0, stream, p);
+    launch_one(mla::mla_decode_kernel<true>, blocks, mla::kThreads, p, stream, start, stop);
   } else {
-    hipLaunchKernelGGL(mla::mla_decode_kernel<false>, dim3(blocks), dim3(mla::kThreads), 0, stream, p);
+    launch_one(mla::mla_decode_kernel<false>, blocks, mla::kThreads, p, stream, start, stop);
   }
   return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }

@@ -1,0 +1,181 @@
+// Device helpers shared by the two decode kernels (64-row and 128-row
+// workgroups): LDS page layout and DMA staging, lane permutes for row
+// reductions, and the worker's page cursor.
+#pragma once
+
+#include "mla_kernels.h"
+
+namespace mla {
+namespace dev {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) const bf16x8 lds_bf16x8;
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+constexpr float kOverflowThreshold = 48.0f;   // log2 units: weights stay <= 2^48
+constexpr float kNegInf = -__builtin_huge_valf();
+constexpr uint32_t kBufferConfig = 0x00020000;   // buffer resource word 3 (raw, no swizzle)
+// s_waitcnt immediate for vmcnt(0) alone (expcnt and lgkmcnt at their maxima),
+// for waits on the kernel's own vector loads: issued through the builtin, the
+// compiler knows they are complete after it.
+constexpr int kWaitVmcnt0 = 0x0F70;
+
+// Wait for the page DMAs, which the compiler does not see: in inline
+// assembly, so that no pass can judge it redundant and drop it.
+__device__ inline void wait_dma_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+__device__ inline int pages_of(int seqlen) { return (seqlen + kPage - 1) / kPage; }
+
+// Read-only table entry at a wave-uniform address, through the constant
+// address space: a scalar load, counted by lgkmcnt.  Keeping the kernel's own
+// table reads off vmcnt means waiting for them never waits for page DMAs.
+__device__ inline int32_t ld_uniform(const int32_t* ptr) {
+  return *(const __attribute__((address_space(4))) int32_t*)ptr;
+}
+
+// LDS layout of a staged page: 72 tiles of 1 KB, tile (a, b) = rows 8a..8a+7 x
+// 16-byte chunks 8b..8b+7 at byte (9a + b) * 1024; inside a tile, chunk c of
+// row r sits at slot 8 * (r % 8) + ((c % 8) ^ (r % 8)).  The XOR spreads the
+// rows a fragment read touches over distinct banks, and one wave-wide
+// 16-byte DMA fills exactly one tile.
+__device__ inline int lds_tile_offset(int r, int c) {
+  return ((r >> 3) * 9 + (c >> 3)) * 1024 + ((r & 7) * 8 + ((c & 7) ^ (r & 7))) * 16;
+}
+
+// Stage one page of one latent head into LDS with 72 wave-wide DMAs, spread
+// evenly over the waves, either at once (stage_page) or one at a time
+// (stage_tile) among the previous page's MFMAs.  Lane u of the DMA for tile
+// (a, b) fetches row 8a + u/8, chunk 8b + ((u%8) ^ (u/8)): a per-lane byte
+// offset (lane_off) plus a wave-uniform one, relative to a buffer resource
+// that spans exactly this page's 64 rows.
+// All 64 rows are fetched; rows past the sequence end are zeroed afterwards by
+// zero_tail_rows().
+//
+// The DMAs are issued from inline assembly (buffer_load_dwordx4 ... lds, with
+// M0 holding the tile's LDS address), as composable_kernel does for gfx950:
+// the compiler then does not know they write LDS and does not make the reads
+// of the other buffer wait for them.  The kernel waits for them itself
+// (s_waitcnt vmcnt(0) at the top of each page step) before any wave reads
+// the buffer, and issues no vector load of its own between a DMA and that
+// wait.  They write no registers.
+__device__ inline __amdgpu_buffer_rsrc_t page_resource(const char* page_head, uint32_t page_bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc((void*)page_head, (short)0, (int)page_bytes, (int)kBufferConfig);
+}
+
+// DMA number k (0 .. kPerWave-1) of this wave for one page, when each of the
+// workgroup's waves issues kPerWave of the page's 72: tile j = kPerWave *
+// wave + k, i.e. tile row j / 9 (rows 8*(j/9) ..+7) x tile column j % 9
+// (chunks 8*(j%9) ..+7).  Both addresses are a per-wave base plus a
+// compile-time offset (k is a constant in every call), so the page's DMAs
+// hold no scalar registers across the page loop.
+template <int kPerWave>
+__device__ inline void stage_tile(__amdgpu_buffer_rsrc_t rsrc, uint32_t lane_off, int row_stride_bytes,
+                                  uint32_t lds_dst, int wave, int k) {
+  static_assert(kPerWave % 9 == 0 && (kPageBytes / 1024) % kPerWave == 0, "whole tile rows per wave");
+  const uint32_t m0 = lds_dst + (uint32_t)(wave * kPerWave * 1024) + (uint32_t)(k * 1024);
+  const uint32_t soff = (wave * (kPerWave / 9) + k / 9) * 8 * row_stride_bytes + (k % 9) * 128;
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               :
+               : "s"(m0), "v"(lane_off), "s"(rsrc), "s"(soff)
+               : "memory", "m0");
+}
+
+template <int kPerWave>
+__device__ inline void stage_page(const char* page_head, uint32_t page_bytes, uint32_t lane_off,
+                                  int row_stride_bytes, uint32_t lds_dst, int wave) {
+  const __amdgpu_buffer_rsrc_t rsrc = page_resource(page_head, page_bytes);
+#pragma unroll
+  for (int k = 0; k < kPerWave; ++k) stage_tile<kPerWave>(rsrc, lane_off, row_stride_bytes, lds_dst, wave, k);
+}
+
+// Zero rows [valid, 64) of a staged page (its cache slots lie past the
+// sequence end and may hold anything, NaN included); kThreadsIn threads.
+template <int kThreadsIn>
+__device__ inline void zero_tail_rows(char* page, int valid, int tid) {
+  for (int i = valid * kChunksPerRow + tid; i < kPageChunks; i += kThreadsIn) {
+    const int r = i / kChunksPerRow;
+    const int c = i - r * kChunksPerRow;
+    *(u32x4*)(page + lds_tile_offset(r, c)) = u32x4{0, 0, 0, 0};
+  }
+}
+
+// The 4 lanes l, l^16, l^32, l^48 hold the same query row.  With both
+// operands equal to x, v_permlane16_swap leaves {x[l], x[l^16]} in lane l's
+// pair of results and v_permlane32_swap {x[l], x[l^32]}; a symmetric
+// reduction of the pair is the xor-shuffle step, without an LDS round trip
+// (which would also wait for the fragment reads in flight).
+__device__ inline float xor16_pair(float x, bool max_op) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(uint32_t, x), __builtin_bit_cast(uint32_t, x),
+                                                  false, false);
+  const float a = __builtin_bit_cast(float, (uint32_t)r[0]), b = __builtin_bit_cast(float, (uint32_t)r[1]);
+  return max_op ? fmaxf(a, b) : a + b;
+}
+__device__ inline float xor32_pair(float x, bool max_op) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x), __builtin_bit_cast(uint32_t, x),
+                                                  false, false);
+  const float a = __builtin_bit_cast(float, (uint32_t)r[0]), b = __builtin_bit_cast(float, (uint32_t)r[1]);
+  return max_op ? fmaxf(a, b) : a + b;
+}
+__device__ inline float row_max4(float x) { return xor32_pair(xor16_pair(x, true), true); }
+
+// Larger of two scores.  NaN-propagating maximum (v_maximum3_f32): unlike
+// fmaxf it needs no quieting of its inputs first.  Scores are never NaN
+// (slots past a sequence's end are zeroed in LDS before use).
+__device__ inline float max2(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+__device__ inline float row_sum4(float x) { return xor32_pair(xor16_pair(x, false), false); }
+
+// Two floats to two bf16 (round to nearest even) in one v_cvt_pk_bf16_f32.
+__device__ inline uint32_t pack_bf16x2(float a, float b) {
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){a, b}, bf16x2));
+}
+
+// End page of sequence b's part of this worker's range.
+__device__ inline int segment_end(const int32_t* meta, const int32_t* seqlens, int b) {
+  return b == ld_uniform(meta + 2) ? ld_uniform(meta + 3) : pages_of(ld_uniform(seqlens + b));
+}
+
+// Advance (b, page, end) to the worker's next page; returns false past the
+// end.  p0 is the first page of the cursor's segment (0 on entering a new
+// sequence).
+__device__ inline bool next_page(const int32_t* meta, const int32_t* seqlens, int& b, int& page, int& end, int& p0) {
+  if (++page < end) return true;
+  for (int nb = b + 1; nb <= ld_uniform(meta + 2); ++nb) {
+    const int e = segment_end(meta, seqlens, nb);
+    if (e > 0) {
+      b = nb;
+      page = 0;
+      end = e;
+      p0 = 0;
+      return true;
+    }
+  }
+  return false;
+}
+
+// Page that step `page` of segment [p0, end) processes, in row block rb of
+// nrb.  The row blocks of a head read the same pages, and a page's fetch
+// takes its full memory latency while its twins in the other blocks are in
+// flight for the same page.  So after the segment's first page (whose maxima
+// set the softmax references, first in every block), pages go in groups of
+// nrb, and block rb takes a group's pages rotated by rb: at each group step
+// every block fetches a different page, and a page is fetched from memory by
+// one block and found in L2 by the others.  A last, partial group keeps its
+// order.  The result does not otherwise depend on the order.
+__device__ inline int page_in_order(int page, int p0, int end, int rb, int nrb) {
+  const int j = page - p0 - 1;
+  if (j < 0 || nrb == 1) return page;
+  const int base = p0 + 1 + (j / nrb) * nrb;
+  if (base + nrb > end) return page;
+  const int r = j - (j / nrb) * nrb + rb;
+  return base + (r >= nrb ? r - nrb : r);
+}
+
+}  // namespace dev
+}  // namespace mla

@@ -25,6 +25,20 @@ constexpr int kCombineRowsPerBlock = 4;            // one wave per (sequence, he
 constexpr int kPRowBytes = 2 * kPage + 16;         // one row of softmax weights in LDS, padded against bank conflicts
 constexpr int kPBytes = kRowsPerBlock * kPRowBytes;
 
+// Wide decode workgroup: 128 query rows of a head, 4 waves (one per SIMD, 512
+// registers each), used when a head has more than 128 query rows.  Its two
+// page buffers and the softmax weights fill the 160 KB of LDS exactly.
+constexpr int kWideRows = 128;
+constexpr int kWideWaves = 4;
+constexpr int kWideThreads = kWideWaves * 64;
+constexpr int kWideDmaPerWave = kPageChunks / 64 / kWideWaves;   // 18
+constexpr int kWidePRowBytes = 2 * kPage;                        // unpadded; 16-byte units XOR-swizzled
+constexpr int kWidePBytes = kWideRows * kWidePRowBytes;          // 16 KB
+static_assert(2 * kPageBytes + kWidePBytes == 160 * 1024, "wide workgroup LDS");
+
+// Query rows one decode workgroup serves for a head with R query rows.
+__host__ __device__ constexpr int rows_per_block(int rows) { return rows > kWideRows ? kWideRows : kRowsPerBlock; }
+
 struct DecodeParams {
   const uint16_t* q;            // bf16 [B][s_q][h_q][576]
   const uint16_t* kv;           // bf16 [P][64][h_kv][576]
@@ -41,7 +55,7 @@ struct DecodeParams {
   int group;                    // G = h_q / h_kv
   int max_pages;
   int num_workers;
-  int row_blocks;               // ceil(R / 64)
+  int row_blocks;               // ceil(R / rows_per_block(R))
   int causal;
   float scale_log2;             // softmax scale * log2(e)
 };
@@ -66,6 +80,8 @@ struct SchedParams {
 
 template <bool kSingleHead>
 __global__ void mla_decode_kernel(DecodeParams p);
+template <bool kSingleHead>
+__global__ void mla_decode_wide_kernel(DecodeParams p);
 __global__ void mla_combine_kernel(CombineParams p);
 __global__ void mla_sched_kernel(SchedParams p);
 

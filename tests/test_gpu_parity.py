@@ -33,15 +33,22 @@ def _custom(batch, s_q, h_q, h_kv, causal, seqlens, seed=0, **kw):
 
 
 SHAPES = [
-    # (s_q, h_q, h_kv, causal, seqlens): several tiles, ragged tails, row blocks
-    (1, 128, 1, False, [1, 63, 64, 65, 200, 1000]),
-    (1, 64, 1, False, [130, 7, 777]),              # half-empty row block
-    (1, 96, 1, False, [300, 2]),
-    (1, 200, 1, False, [129, 64]),                 # four row blocks, ragged last
-    (3, 64, 1, True, [700, 33, 1200]),             # causal, three row blocks (rotated page groups)
+    # (s_q, h_q, h_kv, causal, seqlens): several tiles, ragged tails, row blocks.
+    # Heads of up to 128 query rows run in 64-row workgroups, larger ones in
+    # 128-row workgroups.
+    (1, 128, 1, False, [1, 63, 64, 65, 200, 1000]),   # two 64-row blocks
+    (1, 64, 1, False, [130, 7, 777]),              # one 64-row block
+    (1, 48, 1, False, [5, 300]),                   # 64-row block, 16 rows empty
+    (1, 96, 1, False, [300, 2]),                   # two 64-row blocks, the second half empty
+    (1, 200, 1, False, [129, 64]),                 # two 128-row blocks, ragged last
+    (3, 64, 1, True, [700, 33, 1200]),             # causal, 192 rows: two 128-row blocks, the second half empty
     (2, 128, 1, True, [1, 2, 3, 64, 65, 513]),     # causal s_q = 2, 256 rows
+    (3, 128, 1, True, [300, 64, 129]),             # causal, three 128-row blocks (rotated page groups)
+    (2, 64, 1, True, [90, 700, 3]),                # causal, 128 rows: two 64-row blocks (rotated page pairs)
     (3, 16, 1, True, [1, 2, 5, 70]),               # rows that see nothing
     (1, 128, 2, False, [100, 257]),                # two latent heads
+    (2, 128, 2, True, [70, 200]),                  # two latent heads of 128 rows
+    (3, 128, 2, True, [70, 200]),                  # two latent heads of 192 rows
     (2, 32, 4, True, [66, 9]),
     (1, 16, 1, False, [0, 37, 0, 130]),            # empty sequences
 ]
@@ -72,13 +79,15 @@ def test_softmax_scale_argument():
     compare(o, lse, O, LSE, ulp_aware=True, label="scale 0.02")
 
 
+@pytest.mark.parametrize("h_q", [64, 256])
 @pytest.mark.parametrize("W", [1, 3])
-def test_reference_point_overflow(W):
+def test_reference_point_overflow(W, h_q):
     """Scores on later pages rise far above the split's first page (more
     than 2^48 in the kernel's base-2 weights): the workgroup must run the
     split a second time with each row's maximum as reference, unsplit (W=1) and split
-    (W=3) alike.  Only the k^R columns are scaled, so V stays N(0, 1)."""
-    inp = _custom(2, 1, 64, 1, False, [64 * 6 + 5, 64 * 3], seed=9)
+    (W=3) alike, in 64-row and 128-row workgroups.  Only the k^R columns are
+    scaled, so V stays N(0, 1)."""
+    inp = _custom(2, 1, h_q, 1, False, [64 * 6 + 5, 64 * 3], seed=9)
     kv = inp.kvcache.float()
     bt = inp.block_table.numpy()
     for b in range(2):
@@ -90,7 +99,7 @@ def test_reference_point_overflow(W):
     # the rise the kernel sees, in log2 units: far beyond its 48 threshold
     assert (LSE.max() - 0.0) / np.log(2) > 48
     o, lse, _, _ = run_gpu(inp, num_workers=W)
-    compare(o, lse, O, LSE, ulp_aware=True, label=f"overflow W={W}")
+    compare(o, lse, O, LSE, ulp_aware=True, label=f"overflow W={W} h_q={h_q}")
 
 
 # --------------------------------------------------------------------------

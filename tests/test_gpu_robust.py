@@ -18,11 +18,13 @@ def _custom(s_q, h_q, causal, seqlens, seed, **kw):
     return make_inputs(w, seed, seqlens=seqlens, **kw)
 
 
+@pytest.mark.parametrize("h_q", [32, 128])
 @pytest.mark.parametrize("causal", [False, True])
-def test_poisoned_unused_slots_change_nothing(causal):
+def test_poisoned_unused_slots_change_nothing(causal, h_q):
+    """64-row (2 x 32 rows) and 128-row (2 x 128 rows) workgroups alike."""
     lens = [37, 130, 64, 1]
-    clean = _custom(2, 128, causal, lens, 3, extra_pages=3)
-    dirty = _custom(2, 128, causal, lens, 3, extra_pages=3, poison=True)
+    clean = _custom(2, h_q, causal, lens, 3, extra_pages=3)
+    dirty = _custom(2, h_q, causal, lens, 3, extra_pages=3, poison=True)
     assert torch.isnan(dirty.kvcache.float()).any()
     a = run_gpu(clean)
     b = run_gpu(dirty)

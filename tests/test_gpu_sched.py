@@ -44,5 +44,6 @@ def test_edge_metadata_bit_exact(seqlens, W):
 def test_num_workers_uses_all_cus():
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     assert num_workers(64, 1) == cus
-    assert num_workers(128, 1) == cus // 2
-    assert num_workers(256, 1) == cus // 4
+    assert num_workers(128, 1) == cus // 2      # two 64-row blocks
+    assert num_workers(256, 1) == cus // 2      # two 128-row blocks
+    assert num_workers(320, 1) == cus // 3

@@ -100,9 +100,13 @@ def test_two_workers_sharing_a_sequence_get_equal_pages():
 
 
 def test_num_workers():
-    assert num_workers_ref(256, 128, 1) == 128
-    assert num_workers_ref(256, 256, 1) == 64
+    assert num_workers_ref(256, 128, 1) == 128   # two 64-row blocks per head
+    assert num_workers_ref(256, 129, 1) == 128   # two 128-row blocks
+    assert num_workers_ref(256, 256, 1) == 128   # two 128-row blocks
+    assert num_workers_ref(256, 384, 1) == 85    # three 128-row blocks
+    assert num_workers_ref(256, 64, 1) == 256    # one 64-row block
+    assert num_workers_ref(256, 65, 1) == 128    # two 64-row blocks
     assert num_workers_ref(256, 16, 1) == 256
     assert num_workers_ref(256, 64, 2) == 128
-    assert num_workers_ref(80, 129, 1) == 26
+    assert num_workers_ref(80, 129, 1) == 40
     assert num_workers_ref(1, 1024, 8) == 1
