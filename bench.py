@@ -63,10 +63,10 @@ def decode_kernel_name(w) -> str:
     return "mla_decode_wide_kernel" if w.s_q * w.h_q // w.h_kv > 128 else "mla_decode_kernel"
 
 
-def measured_traffic(workload: str):
+def measured_traffic(w):
     """HBM bytes per decode launch from committed rocprofv3 counter runs, if
     they were taken on the current kernel source (else None)."""
-    path = os.path.join(ROOT, "profiles", f"mla_decode_kernel_{workload}_traffic.json")
+    path = os.path.join(ROOT, "profiles", f"{decode_kernel_name(w)}_{w.name}_traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
@@ -249,7 +249,7 @@ def main():
         achieved, peak, unit = counts["total_bytes"] / dec_s / 1e9, HBM_PEAK_GBS, "GB/s"
     else:
         achieved, peak, unit = counts["flops"] / dec_s / 1e12, MFMA_BF16_PEAK_TFLOPS, "TFLOP/s"
-    traffic = measured_traffic(args.workload)
+    traffic = measured_traffic(w)
     out = {
         "metric": METRIC,
         "value": round(gbs, 2),
