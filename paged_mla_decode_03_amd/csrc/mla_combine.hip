@@ -61,23 +61,53 @@ __global__ __launch_bounds__(kCombineRowsPerBlock * 64) void mla_combine_kernel(
   const float* lse0 = p.ws_lse + (size_t)(s0 * p.h_kv + g) * p.rows + row;
   const float* o0 = p.ws_o + ((size_t)(s0 * p.h_kv + g) * p.rows + row) * kDv + lane * 8;
 
-  float M = -__builtin_huge_valf();
-  for (int i = lane; i < n; i += 64) M = fmaxf(M, lse0[(size_t)i * stride]);
-  M = wave_reduce_max(M);
+  // The first four splits' lse values and partial rows are loaded together,
+  // before any reduction, so a row with up to four splits costs one memory
+  // round trip; splits past the fourth follow four (then two) at a time.
+  constexpr int kFirst = 4;
+  f32x4 v0[kFirst][2];
+  float l0[kFirst];
+#pragma unroll
+  for (int k = 0; k < kFirst; ++k) {
+    if (k < n) {
+      const f32x4* src = (const f32x4*)(o0 + (size_t)k * stride * kDv);
+      v0[k][0] = *(src);
+      v0[k][1] = *(src + 1);
+      l0[k] = lse0[(size_t)k * stride];
+    } else {
+      v0[k][0] = v0[k][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+      l0[k] = -__builtin_huge_valf();
+    }
+  }
+  float M = fmaxf(fmaxf(l0[0], l0[1]), fmaxf(l0[2], l0[3]));   // the same in every lane
+  if (n > kFirst) {
+    float m = -__builtin_huge_valf();
+    for (int i = kFirst + lane; i < n; i += 64) m = fmaxf(m, lse0[(size_t)i * stride]);
+    M = fmaxf(M, wave_reduce_max(m));
+  }
   if (n == 0 || M == -__builtin_huge_valf()) {
     *(uint4*)op = uint4{0, 0, 0, 0};
     if (lane == 0) *lp = -__builtin_huge_valf();
     return;
   }
   float z = 0.f;
-  for (int i = lane; i < n; i += 64) z += expf(lse0[(size_t)i * stride] - M);
-  z = wave_reduce_sum(z);
+#pragma unroll
+  for (int k = 0; k < kFirst; ++k) z += expf(l0[k] - M);   // exp(-inf) = 0 past n
+  if (n > kFirst) {
+    float zr = 0.f;
+    for (int i = kFirst + lane; i < n; i += 64) zr += expf(lse0[(size_t)i * stride] - M);
+    z += wave_reduce_sum(zr);
+  }
   const float lse = M + logf(z);
 
-  // Splits in slot order, four (then two) at a time so that their loads are
-  // in flight together; each lane reads 32 bytes of each split's row.
   f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
-  int i = 0;
+#pragma unroll
+  for (int k = 0; k < kFirst; ++k) {
+    const float w = expf(l0[k] - lse);
+    a0 += w * v0[k][0];
+    a1 += w * v0[k][1];
+  }
+  int i = kFirst;
   for (; i + 4 <= n; i += 4) {
     f32x4 v[4][2];
     float w[4];
