@@ -35,8 +35,8 @@
 //     buffered; each wave issues 18 of a page's 72 DMAs among the previous
 //     page's score MFMAs.
 //   * LDS: two 72 KB page buffers and 16 KB of P fill the 160 KB.  P rows
-//     are 128 bytes with their 16-byte units XOR-swizzled by row, so neither
-//     its writes nor its reads conflict across 16 consecutive rows.
+//     are 128 bytes with their 16-byte units XOR-swizzled by row pair, so
+//     neither its writes nor its reads conflict across 16 consecutive rows.
 //   * The softmax reference point, the overflow rule with its in-place second
 //     pass, the key masking and the page order are those of mla_decode.hip.
 #include <utility>
@@ -55,7 +55,8 @@ namespace {
 // placed here by hand.  The hazard checker does not see these MFMAs: their
 // sources are LDS/global loads (no VALU write shortly before), each chain's
 // accumulator is touched only by these MFMAs, and the score stream ends with
-// qk_drain(), which waits out the last result before any VALU reads it.
+// qk_drain(), which waits out the last result before anything reads the
+// scores.
 __device__ inline f32x4 mfma_qk_first(bf16x8 a, bf16x8 b) {
   f32x4 d;
   asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "v"(b));
@@ -65,9 +66,12 @@ __device__ inline void mfma_qk(f32x4& c, bf16x8 a, bf16x8 b) {
   asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+v"(c) : "v"(a), "v"(b));
 }
 // 24 wait states: more than an 8-pass XDL write needs before a VALU, LDS or
-// memory instruction reads or overwrites its result.
-__device__ inline void qk_drain(f32x4& c) {
-  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(c));
+// memory instruction reads or overwrites its result.  It names all eight
+// score tiles as operands, so no read of any of them can be placed before it.
+__device__ inline void qk_drain(f32x4 (&s)[4][2]) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"
+               : "+v"(s[0][0]), "+v"(s[0][1]), "+v"(s[1][0]), "+v"(s[1][1]),
+                 "+v"(s[2][0]), "+v"(s[2][1]), "+v"(s[3][0]), "+v"(s[3][1]));
 }
 
 // Byte offset of 16-byte unit u (0..7) of row r of the P buffer.
@@ -286,7 +290,7 @@ __device__ __forceinline__ void wide_worker(const DecodeParams& p, char (*lds_pa
             s[kt][1] = mfma_qk_first(kf[F], qf[1][ks]);
           else
             mfma_qk(s[kt][1], kf[F], qf[1][ks]);
-          if constexpr (F == kFrags - 1) qk_drain(s[kt][1]);
+          if constexpr (F == kFrags - 1) qk_drain(s);
           if constexpr (F + kKAhead < kFrags) kf[F + kKAhead] = read_k((F + kKAhead) % 4, (F + kKAhead) / 4);
           dma_step.template operator()<2 * F + 1>();
           __builtin_amdgcn_sched_barrier(0);
