@@ -49,9 +49,17 @@ def parse():
     return ap.parse_args()
 
 
-def kernel_source_hash() -> str:
+KERNEL_SOURCES = {
+    "mla_decode_kernel": ("mla_decode.hip", "mla_decode_common.h", "mla_kernels.h"),
+    "mla_decode_wide_kernel": ("mla_decode_wide.hip", "mla_decode_common.h", "mla_kernels.h"),
+}
+
+
+def kernel_source_hash(kernel: str) -> str:
+    """First 16 hex digits of the sha256 of the sources one decode kernel is
+    built from: a traffic record counts only for the source it was taken on."""
     h = hashlib.sha256()
-    for name in ("mla_decode.hip", "mla_decode_wide.hip", "mla_decode_common.h", "mla_kernels.h"):
+    for name in KERNEL_SOURCES[kernel]:
         with open(os.path.join(ROOT, "paged_mla_decode_03_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -71,7 +79,7 @@ def measured_traffic(w):
         return None
     with open(path) as f:
         rec = json.load(f)
-    if rec.get("kernel_source_hash") != kernel_source_hash():
+    if rec.get("kernel_source_hash") != kernel_source_hash(decode_kernel_name(w)):
         return None
     return rec.get("hbm_bytes_per_launch")
 
