@@ -45,6 +45,8 @@ SHAPES = [
     (2, 128, 1, True, [1, 2, 3, 64, 65, 513]),     # causal s_q = 2, 256 rows
     (3, 128, 1, True, [300, 64, 129]),             # causal, three 128-row blocks (rotated page groups)
     (2, 64, 1, True, [90, 700, 3]),                # causal, 128 rows: two 64-row blocks (rotated page pairs)
+    (4, 128, 1, True, [257, 64, 1000]),            # causal, 512 rows: four 128-row blocks (rotated groups of 4)
+    (8, 16, 1, True, [9, 640]),                    # causal, 8 query tokens x 16 heads = 128 rows
     (3, 16, 1, True, [1, 2, 5, 70]),               # rows that see nothing
     (1, 128, 2, False, [100, 257]),                # two latent heads
     (2, 128, 2, True, [70, 200]),                  # two latent heads of 128 rows
