@@ -73,16 +73,22 @@ __device__ inline __amdgpu_buffer_rsrc_t page_resource(const char* page_head, ui
 // (chunks 8*(j%9) ..+7).  Both addresses are a per-wave base plus a
 // compile-time offset (k is a constant in every call), so the page's DMAs
 // hold no scalar registers across the page loop.
+// One wave-wide DMA: lane u reads 16 bytes at the resource's base +
+// lane_off(u) + soff, and LDS receives them at m0 + 16u.
+__device__ inline void lds_dma16(uint32_t m0, uint32_t lane_off, __amdgpu_buffer_rsrc_t rsrc, uint32_t soff) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               :
+               : "s"(m0), "v"(lane_off), "s"(rsrc), "s"(soff)
+               : "memory", "m0");
+}
+
 template <int kPerWave>
 __device__ inline void stage_tile(__amdgpu_buffer_rsrc_t rsrc, uint32_t lane_off, int row_stride_bytes,
                                   uint32_t lds_dst, int wave, int k) {
   static_assert(kPerWave % 9 == 0 && (kPageBytes / 1024) % kPerWave == 0, "whole tile rows per wave");
   const uint32_t m0 = lds_dst + (uint32_t)(wave * kPerWave * 1024) + (uint32_t)(k * 1024);
   const uint32_t soff = (wave * (kPerWave / 9) + k / 9) * 8 * row_stride_bytes + (k % 9) * 128;
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
-               :
-               : "s"(m0), "v"(lane_off), "s"(rsrc), "s"(soff)
-               : "memory", "m0");
+  lds_dma16(m0, lane_off, rsrc, soff);
 }
 
 template <int kPerWave>

@@ -37,8 +37,10 @@
 //   * LDS: two 72 KB page buffers and 16 KB of P fill the 160 KB.  P rows
 //     are 128 bytes with their 16-byte units XOR-swizzled by row pair, so
 //     neither its writes nor its reads conflict across 16 consecutive rows.
-//   * The softmax reference point, the overflow rule with its in-place second
-//     pass, the key masking and the page order are those of mla_decode.hip.
+//   * Softmax in base 2 against a per-row reference point: the row's maximum
+//     over the segment's first page.  The overflow rule with its in-place
+//     second pass, the key masking and the page order are those of
+//     mla_decode.hip.
 #include <utility>
 
 #include "mla_decode_common.h"

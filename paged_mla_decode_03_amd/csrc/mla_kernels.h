@@ -16,14 +16,11 @@ constexpr int kRowBytes = kDqk * 2;                // 1152 bytes of bf16
 constexpr int kChunksPerRow = kRowBytes / 16;      // 72 chunks of 16 bytes
 constexpr int kPageBytes = kPage * kRowBytes;      // 73728 bytes staged in LDS per page
 constexpr int kPageChunks = kPage * kChunksPerRow; // 4608
-constexpr int kLdsDmaPerWave = kPageChunks / 64 / kWaves;  // 9 wave-wide 16-byte DMA loads
 constexpr int kNumXcd = 8;                         // MI355X: 8 XCDs, round-robin block dispatch
 constexpr int kMetaInts = 8;
 constexpr int kMaxWorkers = 4096;
 constexpr int kSchedThreads = 256;
 constexpr int kCombineRowsPerBlock = 4;            // one wave per (sequence, head, query row)
-constexpr int kPRowBytes = 2 * kPage + 16;         // one row of softmax weights in LDS, padded against bank conflicts
-constexpr int kPBytes = kRowsPerBlock * kPRowBytes;
 
 // Wide decode workgroup: 128 query rows of a head, 4 waves (one per SIMD, 512
 // registers each), used when a head has more than 128 query rows.  Its two
