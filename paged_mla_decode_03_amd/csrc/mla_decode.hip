@@ -23,8 +23,7 @@
 //   * Output waves 4..7: wave 4+o owns output columns 128o..128o+127 for all
 //     64 rows (32 accumulator tiles that only MFMAs touch) and accumulates
 //     O^T += V^T P^T for one half page per step (8 column tiles x 4 row
-//     tiles; V^T through the transposing ds_read_b64_tr_b16).  It also issues
-//     the half-page DMAs.
+//     tiles; V^T through the transposing ds_read_b64_tr_b16).
 //   * Step k of a segment: the score waves work on half page k+1 while the
 //     output waves work on half page k, so on each SIMD one wave's softmax and
 //     LDS waits overlap the other's MFMAs.  One workgroup barrier per step.
@@ -33,9 +32,10 @@
 //     XOR-swizzled by row) and two 4 KB P buffers (half page q's weights in
 //     buffer q % 2).  Pages move HBM -> LDS with buffer_load_dwordx4 ... lds
 //     (no VGPR staging; the buffer resource bounds every read to the page).
-//     During step k the output waves issue the DMAs of half page k+3 and,
-//     before the step's barrier, wait for those of half page k+2, which the
-//     score waves read in step k+1.
+//     During step k the waves issue the DMAs of half page k+3 (output waves
+//     6 each before their MFMAs, score waves 3 each after their softmax) and,
+//     before the step's barrier, wait for their share of half page k+2,
+//     which the score waves read in step k+1.
 //   * Softmax runs in base 2 with the scale folded into one multiply.  Each
 //     row keeps a reference point m (its maximum over the segment's first half
 //     page) and accumulates unnormalised weights 2^(s - m) <= 2^48; that is
@@ -64,7 +64,14 @@ constexpr int kHalfBytes = kHalfRows * kRowBytes;     // 36864 bytes per ring sl
 constexpr int kRingSlots = 4;
 constexpr int kPRowBytes = 2 * kHalfRows;           // one row of P: 32 bf16
 constexpr int kPBytes = kRowsPerBlock * kPRowBytes;   // 4 KB per P buffer
-constexpr int kHalfDmaPerWave = kHalfRows * kChunksPerRow / 64 / 4;   // 9 per output wave
+// A half page is 36 wave-wide DMAs: tile row r (rows 8r..8r+7) x 9 tile
+// columns.  Tile row r is issued by score wave r (columns 6..8, after its
+// softmax, where it would otherwise wait at the barrier) and output wave 4+r
+// (columns 0..5, before its MFMAs): a DMA stalls its wave at issue for about
+// a hundred cycles while the memory queue is full.
+constexpr int kScoreDma = 3;
+constexpr int kOutputDma = 6;
+static_assert(kScoreDma + kOutputDma == kHalfRows * kChunksPerRow / 64 / 4, "9 tile columns per tile row");
 
 // Byte offset of 16-byte unit u (0..3) of row r of a P buffer: rows of 64
 // bytes, units XOR-swizzled by r / 4, so 16 consecutive rows read or write
@@ -73,10 +80,18 @@ __device__ inline uint32_t p_unit_offset(int r, int u) {
   return (uint32_t)(r * kPRowBytes + ((u ^ ((r >> 2) & 3)) * 16));
 }
 
-// Wait until at most 9 of this wave's vector memory operations (its own
-// half-page DMAs: one half page's worth) are in flight, in inline assembly
-// like wait_dma_all.
-__device__ inline void wait_dma_keep9() { asm volatile("s_waitcnt vmcnt(9)" ::: "memory"); }
+// Wait until at most n of this wave's vector memory operations (its own
+// DMAs of one half page) are in flight, in inline assembly like wait_dma_all.
+template <int n>
+__device__ inline void wait_dma_keep() {
+  static_assert(n >= 2 && n <= 7, "wait counts written out below");
+  if constexpr (n == 2) asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
+  if constexpr (n == 3) asm volatile("s_waitcnt vmcnt(3)" ::: "memory");
+  if constexpr (n == 4) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+  if constexpr (n == 5) asm volatile("s_waitcnt vmcnt(5)" ::: "memory");
+  if constexpr (n == 6) asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
+  if constexpr (n == 7) asm volatile("s_waitcnt vmcnt(7)" ::: "memory");
+}
 
 }  // namespace
 
@@ -92,7 +107,6 @@ struct DecodeShared {
 // score waves' Q and the output waves' accumulators never share registers.
 template <bool kSingleHead, bool scorer>
 __device__ __forceinline__ void decode_role(const DecodeParams& p, DecodeShared& sh, const int32_t* meta, int g, int rb) {
-  static_assert(kHalfDmaPerWave == 9, "one 8-row tile row of a half page per output wave");
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
@@ -113,23 +127,26 @@ __device__ __forceinline__ void decode_role(const DecodeParams& p, DecodeShared&
   const uint32_t ring_base = (uint32_t)(uintptr_t)&sh.ring[0][0];
   const uint32_t p_base = (uint32_t)(uintptr_t)&sh.p[0][0];
 
-  // Load cursor over half pages (output waves issue the DMAs): page (lb,
-  // lpage) of segment [lp0, lend), half lhalf; gq counts half pages issued.
+  // Load cursor over half pages (each wave keeps its own copy and issues its
+  // share of the DMAs): page (lb, lpage) of segment [lp0, lend), half lhalf;
+  // gq counts half pages issued.
   int lb = cb, lpage = cpage, lend = cend, lp0 = cpage, lhalf = 0, gq = 0;
   bool lvalid = true;
   int lpid = ld_uniform(p.block_table + (size_t)lb * p.max_pages + page_in_order(lpage, lp0, lend, rb, nrb));
-  const int ow = wave - 4;   // output wave index (DMA tile row of a half page)
-  // Issue the DMAs of the load cursor's half page into its ring slot and
-  // advance the cursor; returns whether anything was issued.
+  const int ow = wave - 4;   // output wave index
+  constexpr int kDma = scorer ? kScoreDma : kOutputDma;   // this wave's DMAs per half page
+  constexpr int kCol0 = scorer ? kOutputDma : 0;          // its first tile column
+  const int trow = wave & 3;                              // its tile row of a half page
+  // Issue this wave's DMAs of the load cursor's half page into its ring slot
+  // and advance the cursor; returns whether anything was issued.
   auto issue_half = [&]() __attribute__((always_inline)) {
     if (!lvalid) return false;
     const __amdgpu_buffer_rsrc_t rsrc = page_resource(kv_head + (size_t)lpid * page_stride_bytes, page_span);
-    const uint32_t dst = ring_base + (uint32_t)((gq & (kRingSlots - 1)) * kHalfBytes) + (uint32_t)(ow * 9 * 1024);
-    const int soff0 = (kHalfRows * lhalf + 8 * ow) * row_stride_bytes;
+    const uint32_t dst =
+        ring_base + (uint32_t)((gq & (kRingSlots - 1)) * kHalfBytes) + (uint32_t)((trow * 9 + kCol0) * 1024);
+    const int soff0 = (kHalfRows * lhalf + 8 * trow) * row_stride_bytes + kCol0 * 128;
 #pragma unroll
-    for (int k = 0; k < kHalfDmaPerWave; ++k) {
-      lds_dma16(dst + (uint32_t)(k * 1024), lane_src_off, rsrc, (uint32_t)(soff0 + k * 128));
-    }
+    for (int j = 0; j < kDma; ++j) lds_dma16(dst + (uint32_t)(j * 1024), lane_src_off, rsrc, (uint32_t)(soff0 + j * 128));
     ++gq;
     if (lhalf == 0) {
       lhalf = 1;
@@ -140,11 +157,11 @@ __device__ __forceinline__ void decode_role(const DecodeParams& p, DecodeShared&
     }
     return true;
   };
-  // End of a step for the output waves: wait for the half page the score
-  // waves read next (all but the 9 DMAs just issued, if any).
+  // End of a step: wait for this wave's share of the half page the score
+  // waves read next (all but the DMAs just issued, if any).
   auto wait_next = [&](bool issued) __attribute__((always_inline)) {
     if (issued)
-      wait_dma_keep9();
+      wait_dma_keep<kDma>();
     else
       wait_dma_all();
   };
@@ -174,7 +191,7 @@ __device__ __forceinline__ void decode_role(const DecodeParams& p, DecodeShared&
   };
 
   // Prologue of the worker: half pages 0 and 1 in flight, wait for 0.
-  if constexpr (!scorer) {
+  {
     issue_half();
     const bool issued = issue_half();
     wait_next(issued);
@@ -317,6 +334,10 @@ __device__ __forceinline__ void decode_role(const DecodeParams& p, DecodeShared&
             *(__attribute__((address_space(3))) u32x4*)(p_base + (uint32_t)((hp & 1) * kPBytes) + pw_off) =
                 u32x4{pk[0][0], pk[0][1], pk[1][0], pk[1][1]};
           }
+          // This wave's share of half page gbase+k+3, then wait for its share
+          // of half page gbase+k+2 (see the output waves).
+          const bool issued = gq == gbase + k + 3 && issue_half();
+          wait_next(issued);
         } else {
           // ---- output waves: DMAs of half page gbase+k+3, outputs of half page k ----
           // (The last step of the previous segment already issued this
@@ -390,7 +411,7 @@ __device__ __forceinline__ void decode_role(const DecodeParams& p, DecodeShared&
       // the segment's first half page.
       if constexpr (scorer) m_ref = row_max4(m_seen);
       second_pass = true;
-      if constexpr (!scorer) {
+      {
         wait_dma_all();
         lb = b;
         lpage = seg_page0;
