@@ -17,6 +17,9 @@ What it computes (deepseek.csdn.net, "FlashMLA ... 详解", section 2.2 "DeepSee
   so the output stays in latent space.
 * The paged cache of section 4.2(1): 64-token blocks, ``block_table`` maps a
   sequence's logical block to its physical page.
+* Appending new tokens to the paged cache (:func:`kvcache_append_ref`): the
+  cache keeps every earlier token's latent row, and a new token's row goes to
+  the page and slot its logical position maps to.
 * The call on the dolphin-ai.jp FlashMLA page ("FlashMLA の使用方法", step 4):
   ``flash_mla_with_kvcache(q, kvcache, block_table, cache_seqlens, dv, ...,
   causal)`` returns the output and the log-sum-exp.
@@ -164,3 +167,43 @@ def lse_combine_ref(partial_o: np.ndarray, partial_lse: np.ndarray):
         w = np.exp(ls - lse[r])
         O[r] = (w[:, None] * partial_o[:, r, :]).sum(axis=0)
     return O, lse
+
+
+def kvcache_append_ref(kvcache, block_table, cache_seqlens, kv_new):
+    """Write the latent rows of new tokens into the paged cache.
+
+    The cache holds each token's [c^KV; k^R] row once it is computed, so a
+    decode step only computes the new token's row and keeps every earlier one
+    (deepseek.csdn.net FlashMLA article, section 4.1 on the KV cache); pages
+    of 64 slots are mapped through block_table (same article, section
+    4.2(1)).  New token i of sequence b
+    takes logical position L_b + i, where L_b = cache_seqlens[b] counts the
+    tokens cached before the call, i.e. page block_table[b][(L_b + i) // 64],
+    slot (L_b + i) % 64.
+
+    kvcache [P][64][h_kv][D] and kv_new [B][s_new][h_kv][D] are arrays of one
+    element type (bf16 as uint16 bits, or any numpy dtype): this is a copy,
+    so the result is exact.  A row whose position lies past the block
+    table (L_b < 0, or (L_b + i) // 64 >= max_pages) or whose page id lies
+    outside [0, P) is not written and is counted.  Returns (new cache,
+    number of rows not written)."""
+    out = np.array(kvcache, copy=True)
+    new = np.asarray(kv_new)
+    bt = np.asarray(block_table)
+    L = np.asarray(cache_seqlens).astype(np.int64)
+    B, s_new, h_kv, D = new.shape
+    P, page, h_kv2, D2 = out.shape
+    assert page == PAGE_SIZE and h_kv2 == h_kv and D2 == D and bt.shape[0] == B and L.shape == (B,)
+    max_pages = bt.shape[1]
+    bad = 0
+    for b in range(B):
+        for i in range(s_new):
+            pos = int(L[b]) + i
+            blk = pos // PAGE_SIZE
+            pid = int(bt[b, blk]) if L[b] >= 0 and blk < max_pages else -1
+            for g in range(h_kv):
+                if not 0 <= pid < P:
+                    bad += 1
+                    continue
+                out[pid, pos % PAGE_SIZE, g, :] = new[b, i, g, :]
+    return out, bad
