@@ -43,6 +43,10 @@ def parse():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=15.0)
+    ap.add_argument("--op", choices=["decode", "append"], default="decode",
+                    help="append: time the cache append of the workload's new tokens instead (its own JSON line)")
+    ap.add_argument("--append-tokens", type=int, default=0,
+                    help="new tokens per sequence for --op append (default: the workload's s_q)")
     ap.add_argument("--copy-mb", type=int, default=0,
                     help="before the timed steps, run one plain device copy of this many MiB: the known-size "
                          "kernel that scales the decode kernel's HBM counters in a rocprofv3 --pmc run")
@@ -109,6 +113,78 @@ def cpu_baseline(inp, budget_s: float) -> dict:
             "sample": f"{len(done)} of {w.batch} sequences ({int(L[done].sum())} cached tokens), float64 numpy"}
 
 
+def bench_append(args):
+    """The cache append of one step's new tokens (or of --append-tokens per
+    sequence, as a prefill writes them), launched back to back between two
+    events on its stream; algorithmic bytes = the new rows read and written
+    plus the lengths and block-table entries read."""
+    import torch
+
+    sys.path.insert(0, ROOT)
+    from paged_mla_decode_03_amd import kvcache_append
+    from workloads import WORKLOADS, make_append_inputs
+
+    dev = torch.device("cuda", 0)
+    w = WORKLOADS[args.workload]
+    s_new = args.append_tokens or w.s_q
+    print(f"[bench] generating append inputs for {args.workload}, {s_new} new tokens (seed {args.seed})",
+          file=sys.stderr, flush=True)
+    inp, kv_new = make_append_inputs(w, args.seed, s_new)
+    kv, new = inp.kvcache.to(dev), kv_new.to(dev)
+    bt, L = inp.block_table.to(dev), inp.cache_seqlens.to(dev)
+    rows = w.batch * s_new * w.h_kv
+    nbytes = 2 * rows * 576 * 2 + w.batch * 4 + w.batch * s_new * 4
+    for _ in range(args.warmup):
+        kvcache_append(new, kv, bt, L)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    for _ in range(args.steps):
+        kvcache_append(new, kv, bt, L)
+    e1.record()
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    ev_ms = e0.elapsed_time(e1) / args.steps
+    # Through the Python binding a launch costs more host time than a
+    # decode-size append takes on the GPU, so the eager loop above measures
+    # the host.  The roofline takes the GPU's own rate: the same launches
+    # captured once into a HIP graph and replayed (each replay rewrites the
+    # same rows, so the cache is checked against the eager result after it).
+    want = kv.clone()
+    n_graph = 50
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for _ in range(n_graph):
+            kvcache_append(new, kv, bt, L)
+    reps = max(1, args.steps // n_graph)
+    graph.replay()
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    if not torch.equal(kv, want):
+        raise RuntimeError("graph replays of the append changed the cache")
+    graph_ms = e0.elapsed_time(e1) / (reps * n_graph)
+    print(f"[bench] append: {ev_ms * 1e3:.2f} us per launch (events, back to back, host-bound at small sizes), "
+          f"{wall_ms * 1e3:.2f} us wall, {graph_ms * 1e3:.2f} us per launch replayed from a graph",
+          file=sys.stderr, flush=True)
+    gbs = nbytes / (wall_ms * 1e-3) / 1e9
+    achieved = nbytes / (graph_ms * 1e-3) / 1e9
+    out = {"metric": "paged MLA cache append: achieved HBM GB/s", "value": round(gbs, 2), "unit": "GB/s",
+           "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(wall_ms, 5),
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+           "config": {"workload": f"{args.workload} append", "batch": w.batch, "new_tokens": s_new, "h_kv": w.h_kv,
+                      "d_qk": 576, "page_size": 64, "seed": args.seed},
+           "append_eager_us": round(ev_ms * 1e3, 2), "append_graph_us": round(graph_ms * 1e3, 3),
+           "roofline": {"kernel": "mla_append_kernel", "bound": "hbm", "achieved": round(achieved, 2),
+                        "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                        "traffic": None, "per_launch": {"bytes": nbytes}}}
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -116,6 +192,9 @@ def main():
                           "(the decode shards by sequence with no exchange, see the design notes)",
                           "n_gpus": args.gpus}))
         sys.exit(2)
+    if args.op == "append":
+        bench_append(args)
+        return
 
     import torch
 

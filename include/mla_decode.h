@@ -168,6 +168,37 @@ int mla_combine_splits(const int32_t* num_splits, int batch, int s_q, int h_q, i
                        int num_workers, void* o, float* lse, const void* workspace,
                        size_t workspace_bytes, void* stream);
 
+/* The step before decode: write the latent rows of new tokens into the
+ * paged cache.  The cache keeps the [c^KV (512); k^R (64)] row of every
+ * token already seen, and a step computes only the new token's row and adds
+ * it (deepseek.csdn.net FlashMLA article, section 4.1); pages of 64 slots
+ * are mapped through block_table (same article, section 4.2(1)).
+ *
+ *   kv_new         [dev] bf16 [batch][s_new][h_kv][576]: rows to append.
+ *   kvcache        [dev] bf16 [num_pages][64][h_kv][576], written in place.
+ *   block_table    [dev] int32 [batch][max_pages_per_seq].
+ *   cache_seqlens  [dev] int32 [batch]: tokens cached BEFORE this call.  New
+ *                  token i of sequence b goes to position L_b + i, i.e. page
+ *                  block_table[b][(L_b + i) / 64], slot (L_b + i) % 64.  The
+ *                  call does not change cache_seqlens: the caller adds s_new
+ *                  before the decode that reads the new rows.
+ *   bad_rows       [dev] int32 counter or NULL: incremented once per
+ *                  (token, latent head) row that is not written because its
+ *                  position has no valid page (L_b < 0, position past the
+ *                  block table, page id outside [0, num_pages)).  The caller
+ *                  clears it.  Such rows are never written, so unlike the
+ *                  decode's reads, a bad table entry cannot corrupt memory.
+ *
+ * The pages that receive rows must be owned by one sequence (a page shared
+ * by two sequences that both append to it is a race), and kv_new must not
+ * overlap kvcache.  Errors: MLA_ERR_INVALID_ARG for null pointers (other
+ * than bad_rows) or non-positive sizes, MLA_ERR_UNSUPPORTED for d_qk != 576,
+ * pointers not 16-byte (bf16 arrays) or 4-byte (int32) aligned, or sizes
+ * past the library's limits. */
+int mla_kvcache_append(const void* kv_new, void* kvcache, const int32_t* block_table, int max_pages_per_seq,
+                       int num_pages, const int32_t* cache_seqlens, int batch, int s_new, int h_kv, int d_qk,
+                       int32_t* bad_rows, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -69,6 +69,7 @@ def _load():
     lib.mla_decode_splitkv_timed.argtypes = decode_args + [vp, vp]
     lib.mla_combine_splits.restype = c_int
     lib.mla_combine_splits.argtypes = [vp, c_int, c_int, c_int, c_int, c_int, c_int, vp, vp, vp, c_size_t, vp]
+    lib.mla_kvcache_append.argtypes = [vp, vp, vp, c_int, c_int, vp, c_int, c_int, c_int, c_int, vp, vp]
     _lib = lib
     return lib
 
@@ -225,3 +226,35 @@ def mla_combine_splits(num_splits: torch.Tensor, s_q: int, h_q: int, h_kv: int, 
         num_splits.data_ptr(), B, s_q, h_q, h_kv, dv, W, buffers.o.data_ptr(), buffers.lse.data_ptr(),
         buffers.workspace.data_ptr(), buffers.workspace.numel(), stream))
     return buffers.o, buffers.lse
+
+
+def kvcache_append(kv_new: torch.Tensor, kvcache: torch.Tensor, block_table: torch.Tensor,
+                   cache_seqlens: torch.Tensor, bad_rows: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Write kv_new [B][s_new][h_kv][576] (bf16) into the paged cache in place:
+    new token i of sequence b goes to position cache_seqlens[b] + i.  Does not
+    change cache_seqlens.  Rows without a valid page are skipped and, if
+    ``bad_rows`` (an int32 device scalar the caller clears) is given, counted.
+    Returns kvcache."""
+    device = kvcache.device
+    if device.type != "cuda":
+        raise ValueError("kvcache_append runs on a GPU; kvcache is on " + str(device))
+    _require(kv_new, "kv_new", torch.bfloat16, device)
+    _require(kvcache, "kvcache", torch.bfloat16, device)
+    _require(block_table, "block_table", torch.int32, device)
+    _require(cache_seqlens, "cache_seqlens", torch.int32, device)
+    if bad_rows is not None:
+        _require(bad_rows, "bad_rows", torch.int32, device)
+        if bad_rows.numel() != 1:
+            raise ValueError("bad_rows must hold one int32")
+    if kv_new.dim() != 4 or kvcache.dim() != 4 or block_table.dim() != 2:
+        raise ValueError("kv_new must be [B][s_new][h_kv][576], kvcache [P][64][h_kv][576], block_table [B][max_pages]")
+    B, s_new, h_kv, d = kv_new.shape
+    if kvcache.shape[1] != PAGE_SIZE or kvcache.shape[2] != h_kv or kvcache.shape[3] != d:
+        raise ValueError("kvcache must be [P][64][h_kv][576] with the h_kv of kv_new")
+    if block_table.shape[0] != B or cache_seqlens.numel() != B:
+        raise ValueError("block_table / cache_seqlens batch does not match kv_new")
+    _check("mla_kvcache_append", _load().mla_kvcache_append(
+        kv_new.data_ptr(), kvcache.data_ptr(), block_table.data_ptr(), block_table.shape[1], kvcache.shape[0],
+        cache_seqlens.data_ptr(), B, s_new, h_kv, d, bad_rows.data_ptr() if bad_rows is not None else None,
+        _stream_handle(device)))
+    return kvcache

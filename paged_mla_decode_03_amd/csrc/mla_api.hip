@@ -172,6 +172,20 @@ int launch_combine(const mla::DecodeParams& d, hipStream_t stream) {
   return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
 
+int check_append(const void* kv_new, const void* kvcache, const int32_t* block_table, int max_pages_per_seq,
+                 int num_pages, const int32_t* cache_seqlens, int batch, int s_new, int h_kv, int d_qk,
+                 const int32_t* bad_rows) {
+  if (!kv_new || !kvcache || !block_table || !cache_seqlens) return MLA_ERR_INVALID_ARG;
+  if (batch <= 0 || s_new <= 0 || h_kv <= 0 || max_pages_per_seq <= 0 || num_pages <= 0) return MLA_ERR_INVALID_ARG;
+  if (d_qk != MLA_D_QK) return MLA_ERR_UNSUPPORTED;
+  if (!aligned(kv_new, 16) || !aligned(kvcache, 16) || !aligned(block_table, 4) || !aligned(cache_seqlens, 4) ||
+      !aligned(bad_rows, 4))
+    return MLA_ERR_UNSUPPORTED;
+  if ((long long)batch * s_new * h_kv * mla::kChunksPerRow >= (1LL << 31)) return MLA_ERR_UNSUPPORTED;
+  if ((long long)num_pages * MLA_PAGE_SIZE * h_kv * MLA_D_QK >= (1LL << 40)) return MLA_ERR_UNSUPPORTED;
+  return MLA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -288,6 +302,29 @@ int mla_decode_paged(const void* q, const void* kvcache, const int32_t* block_ta
   st = launch_decode(p, (hipStream_t)stream);
   if (st != MLA_OK) return st;
   return launch_combine(p, (hipStream_t)stream);
+}
+
+int mla_kvcache_append(const void* kv_new, void* kvcache, const int32_t* block_table, int max_pages_per_seq,
+                       int num_pages, const int32_t* cache_seqlens, int batch, int s_new, int h_kv, int d_qk,
+                       int32_t* bad_rows, void* stream) {
+  const int st = check_append(kv_new, kvcache, block_table, max_pages_per_seq, num_pages, cache_seqlens, batch,
+                              s_new, h_kv, d_qk, bad_rows);
+  if (st != MLA_OK) return st;
+  mla::AppendParams p;
+  p.kv_new = (const uint16_t*)kv_new;
+  p.kv = (uint16_t*)kvcache;
+  p.block_table = block_table;
+  p.seqlens = cache_seqlens;
+  p.bad_rows = bad_rows;
+  p.batch = batch;
+  p.s_new = s_new;
+  p.h_kv = h_kv;
+  p.max_pages = max_pages_per_seq;
+  p.num_pages = num_pages;
+  p.chunks = batch * s_new * h_kv * mla::kChunksPerRow;
+  const int blocks = (p.chunks + mla::kAppendThreads - 1) / mla::kAppendThreads;
+  hipLaunchKernelGGL(mla::mla_append_kernel, dim3(blocks), dim3(mla::kAppendThreads), 0, (hipStream_t)stream, p);
+  return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
 
 }  // extern "C"

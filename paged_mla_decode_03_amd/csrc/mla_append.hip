@@ -1,0 +1,44 @@
+// Append of new tokens' latent rows to the paged cache.
+//
+// The cache keeps the [c^KV; k^R] row of every token already seen, so a
+// decode step computes only the new token's row and adds it (deepseek.csdn.net
+// FlashMLA article, section 4.1); the cache is a pool of 64-slot pages mapped
+// through block_table (same article, section 4.2(1)).  New token i of
+// sequence b takes logical position L_b + i, L_b = cache_seqlens[b]: page
+// block_table[b][(L_b + i) / 64], slot (L_b + i) % 64.
+//
+// A copy, bound by HBM and, at decode sizes, by the launch itself: one
+// thread moves one 16-byte chunk of a row (72 per row), so each wave reads
+// and writes 1 KB of consecutive bytes and no byte is touched twice.  A row
+// whose position has no valid page (negative length, past the block table,
+// page id outside the pool) is not written; it is counted in bad_rows.
+#include <hip/hip_runtime.h>
+
+#include "mla_kernels.h"
+
+namespace mla {
+
+__global__ __launch_bounds__(kAppendThreads) void mla_append_kernel(AppendParams p) {
+  const int t = blockIdx.x * kAppendThreads + threadIdx.x;
+  if (t >= p.chunks) return;
+  const int row = t / kChunksPerRow;                 // (b * s_new + i) * h_kv + g
+  const int chunk = t - row * kChunksPerRow;
+  const int g = row % p.h_kv;
+  const int bi = row / p.h_kv;
+  const int i = bi % p.s_new;
+  const int b = bi / p.s_new;
+  const int len = p.seqlens[b];
+  const long long pos = (long long)len + i;
+  const long long blk = pos / kPage;
+  int pid = -1;
+  if (len >= 0 && blk < p.max_pages) pid = p.block_table[(size_t)b * p.max_pages + blk];
+  if (pid < 0 || pid >= p.num_pages) {
+    if (chunk == 0 && p.bad_rows) atomicAdd(p.bad_rows, 1);
+    return;
+  }
+  const size_t slot = ((size_t)pid * kPage + (size_t)(pos - blk * kPage)) * p.h_kv + g;
+  const uint4 v = reinterpret_cast<const uint4*>(p.kv_new)[(size_t)row * kChunksPerRow + chunk];
+  reinterpret_cast<uint4*>(p.kv)[slot * kChunksPerRow + chunk] = v;
+}
+
+}  // namespace mla

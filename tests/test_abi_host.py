@@ -30,7 +30,7 @@ def test_header_declares_the_boundary():
     names = set(declared_functions())
     assert {"mla_get_metadata", "mla_decode_paged", "mla_num_workers", "mla_workspace_bytes",
             "mla_status_string", "mla_decode_splitkv", "mla_decode_splitkv_timed", "mla_combine_splits",
-            "mla_sched_fixed_overhead"} <= names
+            "mla_sched_fixed_overhead", "mla_kvcache_append"} <= names
 
 
 def test_library_exports_every_declared_symbol():
@@ -120,3 +120,16 @@ def test_metadata_and_combine_reject_invalid_arguments():
     n = ctypes.c_int(0)
     assert lib.mla_num_workers(0, 0, 1, ctypes.byref(n)) == -1
     assert lib.mla_num_workers(0, 16, 1, None) == -1
+
+
+def test_append_rejects_invalid_arguments():
+    lib = _lib()
+    ok = dict(kv_new=FAKE, kv=FAKE, bt=FAKE, max_pages=4, num_pages=8, L=FAKE, batch=2, s_new=1, h_kv=1, d=576,
+              bad=None, stream=None)
+    for kw, status in [(dict(kv_new=None), -1), (dict(kv=None), -1), (dict(bt=None), -1), (dict(L=None), -1),
+                       (dict(batch=0), -1), (dict(s_new=0), -1), (dict(h_kv=0), -1), (dict(max_pages=0), -1),
+                       (dict(num_pages=-1), -1), (dict(d=512), -2), (dict(kv_new=FAKE + 8), -2),
+                       (dict(kv=FAKE + 8), -2), (dict(bt=FAKE + 2), -2), (dict(bad=FAKE + 2), -2),
+                       (dict(batch=1 << 20, s_new=1 << 6), -2), (dict(num_pages=1 << 30), -2)]:
+        args = dict(ok, **kw)
+        assert lib.mla_kvcache_append(*args.values()) == status, kw

@@ -176,6 +176,24 @@ def make_inputs(w: Workload | str, seed: int = 0, *, seqlens=None, poison: bool 
     return DecodeInputs(w, seed, q, kv, torch.from_numpy(bt), torch.from_numpy(L.astype(np.int32)))
 
 
+def make_append_inputs(w: Workload | str, seed: int = 0, s_new: int = 1, *, seqlens=None,
+                       extra_pages: int = 0):
+    """Inputs of a cache append: the workload's lengths L (or ``seqlens``)
+    are drawn as for a decode step, the block table maps pages for L + s_new
+    tokens, and ``cache_seqlens`` holds L (the tokens cached before the
+    append).  Returns (inputs, kv_new bf16 [B][s_new][h_kv][576])."""
+    if isinstance(w, str):
+        w = WORKLOADS[w]
+    if seqlens is None:
+        seqlens = draw_seqlens(w, np.random.Generator(np.random.PCG64(seed)))
+    L = np.asarray(seqlens, dtype=np.int64)
+    inp = make_inputs(w, seed, seqlens=L + s_new, extra_pages=extra_pages)
+    inp.cache_seqlens = torch.from_numpy(L.astype(np.int32))
+    rng = np.random.Generator(np.random.PCG64(seed + 7919))
+    kv_new = bf16_normal(rng, (len(L), s_new, w.h_kv, w.d_qk))
+    return inp, kv_new
+
+
 def algorithmic_counts(w: Workload, seqlens: np.ndarray, max_pages_per_seq: int) -> dict:
     """Bytes and flops one decode step needs by definition: every visible latent
     row read once (h_kv * 576 bf16 per token), q read once, o and lse written
