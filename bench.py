@@ -137,6 +137,11 @@ def bench_append(args):
     for _ in range(args.warmup):
         kvcache_append(new, kv, bt, L)
     torch.cuda.synchronize()
+    if args.copy_mb > 0:              # the counters' calibration copy, as for the decode
+        src = torch.empty(args.copy_mb << 20, dtype=torch.uint8, device=dev)
+        torch.empty_like(src).copy_(src)
+        torch.cuda.synchronize()
+        del src
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
     e0.record()
