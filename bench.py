@@ -56,6 +56,7 @@ def parse():
 KERNEL_SOURCES = {
     "mla_decode_kernel": ("mla_decode.hip", "mla_decode_common.h", "mla_kernels.h"),
     "mla_decode_wide_kernel": ("mla_decode_wide.hip", "mla_decode_common.h", "mla_kernels.h"),
+    "mla_append_kernel": ("mla_append.hip", "mla_kernels.h"),
 }
 
 
@@ -75,15 +76,16 @@ def decode_kernel_name(w) -> str:
     return "mla_decode_wide_kernel" if w.s_q * w.h_q // w.h_kv > 128 else "mla_decode_kernel"
 
 
-def measured_traffic(w):
-    """HBM bytes per decode launch from committed rocprofv3 counter runs, if
-    they were taken on the current kernel source (else None)."""
-    path = os.path.join(ROOT, "profiles", f"{decode_kernel_name(w)}_{w.name}_traffic.json")
+def measured_traffic(w, kernel=None, workload=None):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they
+    were taken on the current kernel source (else None)."""
+    kernel = kernel or decode_kernel_name(w)
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload or w.name}_traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f)
-    if rec.get("kernel_source_hash") != kernel_source_hash(decode_kernel_name(w)):
+    if rec.get("kernel_source_hash") != kernel_source_hash(kernel):
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -186,7 +188,8 @@ def bench_append(args):
            "append_eager_us": round(ev_ms * 1e3, 2), "append_graph_us": round(graph_ms * 1e3, 3),
            "roofline": {"kernel": "mla_append_kernel", "bound": "hbm", "achieved": round(achieved, 2),
                         "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                        "traffic": None, "per_launch": {"bytes": nbytes}}}
+                        "traffic": measured_traffic(w, "mla_append_kernel", f"{args.workload}_append{s_new}"),
+                        "per_launch": {"bytes": nbytes}}}
     print(json.dumps(out), flush=True)
 
 
