@@ -56,7 +56,7 @@ def parse():
 KERNEL_SOURCES = {
     "mla_decode_kernel": ("mla_decode.hip", "mla_decode_common.h", "mla_kernels.h"),
     "mla_decode_wide_kernel": ("mla_decode_wide.hip", "mla_decode_common.h", "mla_kernels.h"),
-    "mla_append_kernel": ("mla_append.hip", "mla_kernels.h"),
+    "mla_append_kernel": ("mla_append.hip", "mla_append.h", "mla_kernels.h"),
 }
 
 

@@ -8,6 +8,7 @@
 
 #include "../../include/mla_decode.h"
 #include "mla_kernels.h"
+#include "mla_append.h"
 
 namespace {
 

@@ -14,7 +14,7 @@
 // page id outside the pool) is not written; it is counted in bad_rows.
 #include <hip/hip_runtime.h>
 
-#include "mla_kernels.h"
+#include "mla_append.h"
 
 namespace mla {
 

@@ -21,7 +21,6 @@ constexpr int kMetaInts = 8;
 constexpr int kMaxWorkers = 4096;
 constexpr int kSchedThreads = 256;
 constexpr int kCombineRowsPerBlock = 4;            // one wave per (sequence, head, query row)
-constexpr int kAppendThreads = 256;
 
 // Wide decode workgroup: 128 query rows of a head, 4 waves (one per SIMD, 512
 // registers each), used when a head has more than 128 query rows.  Its two
@@ -67,16 +66,6 @@ struct CombineParams {
   int batch, s_q, h_q, h_kv, rows, group;
 };
 
-struct AppendParams {
-  const uint16_t* kv_new;      // [batch][s_new][h_kv][576]
-  uint16_t* kv;                // [num_pages][64][h_kv][576]
-  const int32_t* block_table;  // [batch][max_pages]
-  const int32_t* seqlens;      // [batch], tokens cached before the append
-  int32_t* bad_rows;           // optional counter of rows without a valid page
-  int batch, s_new, h_kv, max_pages, num_pages;
-  int chunks;                  // batch * s_new * h_kv * kChunksPerRow
-};
-
 struct SchedParams {
   const int32_t* seqlens;
   int32_t* meta;
@@ -92,6 +81,5 @@ template <bool kSingleHead>
 __global__ void mla_decode_wide_kernel(DecodeParams p);
 __global__ void mla_combine_kernel(CombineParams p);
 __global__ void mla_sched_kernel(SchedParams p);
-__global__ void mla_append_kernel(AppendParams p);
 
 }  // namespace mla
