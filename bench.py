@@ -37,8 +37,13 @@ BOUND = {"mem_bound": "hbm", "var_len": "hbm", "skewed": "hbm", "causal_sq2": "m
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=200)
+    # Until a few hundred launches have gone through, the gaps between
+    # back-to-back kernels are ~20 us longer (mem_bound step 121 us after 10
+    # warmup steps, 98.6 after 100, 94.6 after 300 and 95.0 after 1000; the
+    # kernels' own durations do not change), so the default warmup is 300
+    # steps (about 30 ms).
+    ap.add_argument("--warmup", type=int, default=300)
     ap.add_argument("--workload", default="mem_bound")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
