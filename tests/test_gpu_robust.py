@@ -59,13 +59,14 @@ def test_causal_single_token_equals_noncausal():
     assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
 
 
-def test_combine_kernel_alone_on_synthetic_partials():
+@pytest.mark.parametrize("counts", [[1, 3, 36], [2, 19, 5], [7, 13, 0], [11, 8, 22]])
+def test_combine_kernel_alone_on_synthetic_partials(counts):
     """Write partials for 3 sequences straight into the workspace and check
-    the merge against the oracle's formula (one split left alone, one with
-    an empty split, one with many)."""
+    the merge against the oracle's formula (a split left alone, an empty
+    split, many splits: the kernel takes splits 4 at first, then 4, 2 and 1
+    at a time, and these counts reach every such tail)."""
     B, s_q, h_q, h_kv, dv, W = 3, 1, 64, 1, 512, 40
     R = s_q * h_q // h_kv
-    counts = [1, 3, 36]
     ns = torch.tensor(np.concatenate([[0], np.cumsum(counts)]), dtype=torch.int32, device=DEV)
     q = torch.zeros((B, s_q, h_q, 576), dtype=torch.bfloat16, device=DEV)
     kv = torch.zeros((1, 64, h_kv, 576), dtype=torch.bfloat16, device=DEV)
@@ -77,7 +78,7 @@ def test_combine_kernel_alone_on_synthetic_partials():
     rng = np.random.default_rng(0)
     po = rng.standard_normal((slots, h_kv, R, dv)).astype(np.float32)
     pl = rng.normal(3.0, 2.0, (slots, h_kv, R)).astype(np.float32)
-    pl[1 + 1] = -np.inf                         # sequence 1: one split saw no key
+    pl[int(np.cumsum(counts)[0]) + 1] = -np.inf  # sequence 1: its second split saw no key
     ws_o.copy_(torch.from_numpy(po))
     ws_l.copy_(torch.from_numpy(pl))
     buf.o.fill_(7.0)
@@ -86,9 +87,11 @@ def test_combine_kernel_alone_on_synthetic_partials():
     torch.cuda.synchronize()
     o = buf.o.float().cpu().numpy()
     lse = buf.lse.cpu().numpy()
-    assert (o[0] == 7.0).all() and (lse[0] == 7.0).all()   # single split: left to the decode kernel
-    for b in (1, 2):
+    for b in range(B):
         s0, n = int(ns[b]), counts[b]
+        if n == 1:                               # single split: left to the decode kernel
+            assert (o[b] == 7.0).all() and (lse[b] == 7.0).all()
+            continue
         O, L = lse_combine_ref(po[s0:s0 + n, 0].astype(np.float64), pl[s0:s0 + n, 0].astype(np.float64))
         np.testing.assert_allclose(o[b, 0], O, rtol=0, atol=2e-2 * max(1, np.abs(O).max()))
         np.testing.assert_allclose(lse[b, :, 0], L, rtol=0, atol=1e-5 * max(1, np.abs(L).max()))
