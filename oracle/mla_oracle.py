@@ -207,3 +207,34 @@ def kvcache_append_ref(kvcache, block_table, cache_seqlens, kv_new):
                     continue
                 out[pid, pos % PAGE_SIZE, g, :] = new[b, i, g, :]
     return out, bad
+
+
+def absorb_q_ref(q_nope, q_rope, w_uk_t):
+    """Absorbed query rows (deepseek.csdn.net FlashMLA article, section 2.2,
+    the matrix-absorption paragraph): since k^C = W^UK c^KV, the score
+    q^C . k^C equals (W^UK^T q^C) . c^KV, so a head's query against the cached
+    latent row is [W^UK^T q^C ; q^R].
+
+    q_nope [T][h][128], q_rope [T][h][64], w_uk_t [h][512][128] (W^UK of
+    each head stored transposed, c-major).  Returns [T][h][576] in float64."""
+    qn, qr, w = as_f64(q_nope), as_f64(q_rope), as_f64(w_uk_t)
+    T, H, _ = qn.shape
+    out = np.zeros((T, H, w.shape[1] + qr.shape[2]))
+    for h in range(H):
+        out[:, h, : w.shape[1]] = qn[:, h, :] @ w[h].T
+        out[:, h, w.shape[1]:] = qr[:, h, :]
+    return out
+
+
+def absorb_o_ref(o_latent, w_uv):
+    """Per-head output from the latent one (same paragraph): v^C = W^UV c^KV,
+    and the attention weights sum over the same keys, so sum_j p_j v^C_j =
+    W^UV sum_j p_j c^KV_j.
+
+    o_latent [T][h][512], w_uv [h][128][512].  Returns [T][h][128] in float64."""
+    o, w = as_f64(o_latent), as_f64(w_uv)
+    T, H, _ = o.shape
+    out = np.zeros((T, H, w.shape[1]))
+    for h in range(H):
+        out[:, h, :] = o[:, h, :] @ w[h].T
+    return out

@@ -84,11 +84,13 @@ def _brute_force_case(seqlens, s_q, h_q, h_kv, causal, seed):
                 o_ref[b, t, i] = sum(math.exp(s - m) / z * v for s, v in zip(scores, vals))
 
     # Absorbed: q~ = [W^UK^T q^C ; q^R], cached rows [c^KV ; k^R] in pages.
-    q_abs = np.concatenate([np.einsum("hdc,bthd->bthc", w_uk, qc), qr], axis=-1)
+    T = B * s_q
+    q_abs = mo.absorb_q_ref(qc.reshape(T, h_q, D_H), qr.reshape(T, h_q, D_HR),
+                            np.ascontiguousarray(w_uk.transpose(0, 2, 1))).reshape(B, s_q, h_q, D_QK)
     rows = [np.concatenate([c[b], kr[b]], axis=-1) for b in range(B)]
     kv, bt = _paged(rows, rng, h_kv)
     O, LSE = mla_decode_ref(q_abs, kv, bt, np.asarray(seqlens), dv=D_C, causal=causal)
-    o_from_latent = np.einsum("hdc,bthc->bthd", w_uv, O)
+    o_from_latent = mo.absorb_o_ref(O.reshape(T, h_q, D_C), w_uv).reshape(B, s_q, h_q, D_H)
     return o_ref, lse_ref, o_from_latent, LSE
 
 
@@ -321,3 +323,18 @@ def test_planted_mistakes_are_caught(kind, monkeypatch):
     else:
         monkeypatch.setattr(mo, "attend", _mutant_attend(kind))
     assert not _pins_pass(), f"planted mistake {kind!r} slipped through every pin"
+
+
+@pytest.mark.parametrize("kind", ["rope_dropped", "weight_untransposed_head", "output_heads_rolled"])
+def test_planted_absorption_mistakes_are_caught(kind, monkeypatch):
+    """P-1 runs its absorbed side through absorb_q_ref and absorb_o_ref, so it
+    pins them against the un-absorbed equations: plausible mistakes in them
+    fail it."""
+    aq, ao = mo.absorb_q_ref, mo.absorb_o_ref
+    if kind == "rope_dropped":
+        monkeypatch.setattr(mo, "absorb_q_ref", lambda qn, qr, w: aq(qn, 0 * np.asarray(qr), w))
+    elif kind == "weight_untransposed_head":
+        monkeypatch.setattr(mo, "absorb_q_ref", lambda qn, qr, w: aq(qn, qr, np.roll(w, 1, axis=0)))
+    else:
+        monkeypatch.setattr(mo, "absorb_o_ref", lambda o, w: np.roll(ao(o, w), 1, axis=1))
+    assert _p1_error((5, 70), 1, 4, 1, False, seed=3) > 1e-3
