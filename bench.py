@@ -48,8 +48,9 @@ def parse():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=15.0)
-    ap.add_argument("--op", choices=["decode", "append"], default="decode",
-                    help="append: time the cache append of the workload's new tokens instead (its own JSON line)")
+    ap.add_argument("--op", choices=["decode", "append", "absorb"], default="decode",
+                    help="append: time the cache append of the workload's new tokens instead; absorb: the "
+                         "per-head projections before and after the decode (each prints its own JSON line)")
     ap.add_argument("--append-tokens", type=int, default=0,
                     help="new tokens per sequence for --op append (default: the workload's s_q)")
     ap.add_argument("--copy-mb", type=int, default=0,
@@ -198,6 +199,69 @@ def bench_append(args):
     print(json.dumps(out), flush=True)
 
 
+def bench_absorb(args):
+    """The per-head projections around the decode for the workload's
+    B * s_q tokens and h_q heads (random bf16 weights of the model's shape):
+    the query absorption W^UK^T q^C and the output projection W^UV o, each
+    captured 50 times into a HIP graph and replayed, so the time is the GPU's
+    own.  Algorithmic bytes: each operand read once and each result written
+    once; flops 2 * tokens * h_q * 128 * 512 per projection."""
+    import torch
+
+    sys.path.insert(0, ROOT)
+    from paged_mla_decode_03_amd import absorb_o, absorb_q
+    from workloads import WORKLOADS, bf16_normal
+
+    dev = torch.device("cuda", 0)
+    w = WORKLOADS[args.workload]
+    T, H = w.batch * w.s_q, w.h_q
+    rng = np.random.Generator(np.random.PCG64(args.seed))
+    qn, qr = bf16_normal(rng, (T, H, 128)).to(dev), bf16_normal(rng, (T, H, 64)).to(dev)
+    w_uk_t, w_uv = bf16_normal(rng, (H, 512, 128)).to(dev), bf16_normal(rng, (H, 128, 512)).to(dev)
+    o = bf16_normal(rng, (T, H, 512)).to(dev)
+    q_out = torch.empty((T, H, 576), dtype=torch.bfloat16, device=dev)
+    u_out = torch.empty((T, H, 128), dtype=torch.bfloat16, device=dev)
+    bytes_q = 2 * (T * H * (128 + 64 + 576) + H * 512 * 128)
+    bytes_o = 2 * (T * H * (512 + 128) + H * 128 * 512)
+    flops = 2 * T * H * 128 * 512
+    times = {}
+    for name, fn in (("absorb_q", lambda: absorb_q(qn, qr, w_uk_t, q_out)), ("absorb_o", lambda: absorb_o(o, w_uv, u_out))):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        graph, n_graph = torch.cuda.CUDAGraph(), 50
+        with torch.cuda.graph(graph):
+            for _ in range(n_graph):
+                fn()
+        reps = max(1, args.steps // n_graph)
+        graph.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            graph.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        times[name] = e0.elapsed_time(e1) / (reps * n_graph)
+    tq, to = times["absorb_q"], times["absorb_o"]
+    print(f"[bench] absorb: query {tq * 1e3:.2f} us ({bytes_q / tq / 1e6:.0f} GB/s), "
+          f"output {to * 1e3:.2f} us ({bytes_o / to / 1e6:.0f} GB/s) per launch, graph replay", file=sys.stderr, flush=True)
+    total = bytes_q + bytes_o
+    achieved = total / ((tq + to) * 1e-3) / 1e9
+    out = {"metric": "MLA per-head projections around the decode: achieved HBM GB/s", "value": round(achieved, 2),
+           "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+           "ms_per_step": round(tq + to, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+           "dtype": "bf16", "data": "synthetic",
+           "config": {"workload": f"{args.workload} absorb", "tokens": T, "h_q": H, "d_h": 128, "d_c": 512,
+                      "seed": args.seed},
+           "absorb_q_us": round(tq * 1e3, 3), "absorb_o_us": round(to * 1e3, 3),
+           "tflops": round(2 * flops / ((tq + to) * 1e-3) / 1e12, 2),
+           "roofline": {"kernel": "mla_absorb_kernel", "bound": "hbm", "achieved": round(achieved, 2),
+                        "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                        "traffic": None, "per_launch": {"bytes_q": bytes_q, "bytes_o": bytes_o, "flops_each": flops}}}
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -207,6 +271,9 @@ def main():
         sys.exit(2)
     if args.op == "append":
         bench_append(args)
+        return
+    if args.op == "absorb":
+        bench_absorb(args)
         return
 
     import torch

@@ -199,6 +199,30 @@ int mla_kvcache_append(const void* kv_new, void* kvcache, const int32_t* block_t
                        int num_pages, const int32_t* cache_seqlens, int batch, int s_new, int h_kv, int d_qk,
                        int32_t* bad_rows, void* stream);
 
+/* The per-head projections on either side of the decode (deepseek.csdn.net
+ * FlashMLA article, section 2.2, the matrix-absorption paragraph): the
+ * decode works in the cache's latent space, so a head's query is absorbed
+ * into it before, q~ = [W^UK^T q^C ; q^R] (q^C . W^UK c = W^UK^T q^C . c),
+ * and its latent output is mapped to the head's value space after,
+ * u = W^UV o (W^UV is linear and the attention weights are shared).
+ * bf16 in and out, fp32 accumulation; d_h = 128, d_c = 512, RoPE part 64.
+ *
+ * mla_absorb_q:
+ *   q_nope  [dev] bf16 [tokens][h_q][128]  (q^C of every head)
+ *   q_rope  [dev] bf16 [tokens][h_q][64]   (q^R, copied unchanged)
+ *   w_uk_t  [dev] bf16 [h_q][512][128]     (each head's W^UK, transposed)
+ *   q_out   [dev] bf16 [tokens][h_q][576]  (the decode's q; tokens = B*s_q)
+ * mla_absorb_o:
+ *   o_latent [dev] bf16 [tokens][h_q][512] (the decode's o)
+ *   w_uv     [dev] bf16 [h_q][128][512]    (each head's W^UV)
+ *   out      [dev] bf16 [tokens][h_q][128]
+ * Outputs must not overlap inputs.  Errors: MLA_ERR_INVALID_ARG for null
+ * pointers or non-positive sizes, MLA_ERR_UNSUPPORTED for pointers that are
+ * not 16-byte aligned or sizes past the library's limits. */
+int mla_absorb_q(const void* q_nope, const void* q_rope, const void* w_uk_t, void* q_out, int tokens, int h_q,
+                 void* stream);
+int mla_absorb_o(const void* o_latent, const void* w_uv, void* out, int tokens, int h_q, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

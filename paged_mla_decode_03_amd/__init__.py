@@ -3,10 +3,10 @@
 The work runs in ``libmla_decode.so`` (hand-written HIP kernels behind a C ABI,
 ``include/mla_decode.h``); ``binding`` marshals torch tensors into it.
 """
-from .binding import (DecodeBuffers, MlaError, fixed_overhead_pages, get_mla_metadata, kvcache_append, library,
+from .binding import (DecodeBuffers, absorb_o, absorb_q, MlaError, fixed_overhead_pages, get_mla_metadata, kvcache_append, library,
                       mla_combine_splits, mla_decode_paged, mla_decode_splitkv, mla_decode_splitkv_timed,
                       num_workers, workspace_bytes)
 
-__all__ = ["DecodeBuffers", "MlaError", "fixed_overhead_pages", "get_mla_metadata", "kvcache_append", "library",
+__all__ = ["DecodeBuffers", "absorb_o", "absorb_q", "MlaError", "fixed_overhead_pages", "get_mla_metadata", "kvcache_append", "library",
            "mla_combine_splits", "mla_decode_paged", "mla_decode_splitkv", "mla_decode_splitkv_timed", "num_workers",
            "workspace_bytes"]

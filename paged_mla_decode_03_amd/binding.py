@@ -70,6 +70,8 @@ def _load():
     lib.mla_combine_splits.restype = c_int
     lib.mla_combine_splits.argtypes = [vp, c_int, c_int, c_int, c_int, c_int, c_int, vp, vp, vp, c_size_t, vp]
     lib.mla_kvcache_append.argtypes = [vp, vp, vp, c_int, c_int, vp, c_int, c_int, c_int, c_int, vp, vp]
+    lib.mla_absorb_q.argtypes = [vp, vp, vp, vp, c_int, c_int, vp]
+    lib.mla_absorb_o.argtypes = [vp, vp, vp, c_int, c_int, vp]
     _lib = lib
     return lib
 
@@ -258,3 +260,42 @@ def kvcache_append(kv_new: torch.Tensor, kvcache: torch.Tensor, block_table: tor
         cache_seqlens.data_ptr(), B, s_new, h_kv, d, bad_rows.data_ptr() if bad_rows is not None else None,
         _stream_handle(device)))
     return kvcache
+
+
+def absorb_q(q_nope: torch.Tensor, q_rope: torch.Tensor, w_uk_t: torch.Tensor,
+             out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Absorbed query rows [W^UK^T q^C ; q^R]: q_nope [..., h_q, 128] and
+    q_rope [..., h_q, 64] (bf16), w_uk_t [h_q, 512, 128] (each head's W^UK
+    transposed).  Returns [..., h_q, 576] bf16."""
+    device = q_nope.device
+    for t, name in ((q_nope, "q_nope"), (q_rope, "q_rope"), (w_uk_t, "w_uk_t")):
+        _require(t, name, torch.bfloat16, device)
+    h = q_nope.shape[-2]
+    if q_nope.shape[-1] != 128 or q_rope.shape[:-1] != q_nope.shape[:-1] or q_rope.shape[-1] != 64 \
+            or tuple(w_uk_t.shape) != (h, 512, 128):
+        raise ValueError("expected q_nope [..., h, 128], q_rope [..., h, 64], w_uk_t [h, 512, 128]")
+    if out is None:
+        out = torch.empty(q_nope.shape[:-1] + (576,), dtype=torch.bfloat16, device=device)
+    _require(out, "out", torch.bfloat16, device)
+    tokens = q_nope.numel() // (h * 128)
+    _check("mla_absorb_q", _load().mla_absorb_q(q_nope.data_ptr(), q_rope.data_ptr(), w_uk_t.data_ptr(),
+                                                out.data_ptr(), tokens, h, _stream_handle(device)))
+    return out
+
+
+def absorb_o(o_latent: torch.Tensor, w_uv: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Per-head outputs W^UV o from the decode's latent outputs: o_latent
+    [..., h_q, 512] and w_uv [h_q, 128, 512] (bf16).  Returns [..., h_q, 128]."""
+    device = o_latent.device
+    _require(o_latent, "o_latent", torch.bfloat16, device)
+    _require(w_uv, "w_uv", torch.bfloat16, device)
+    h = o_latent.shape[-2]
+    if o_latent.shape[-1] != 512 or tuple(w_uv.shape) != (h, 128, 512):
+        raise ValueError("expected o_latent [..., h, 512], w_uv [h, 128, 512]")
+    if out is None:
+        out = torch.empty(o_latent.shape[:-1] + (128,), dtype=torch.bfloat16, device=device)
+    _require(out, "out", torch.bfloat16, device)
+    tokens = o_latent.numel() // (h * 512)
+    _check("mla_absorb_o", _load().mla_absorb_o(o_latent.data_ptr(), w_uv.data_ptr(), out.data_ptr(), tokens, h,
+                                                _stream_handle(device)))
+    return out

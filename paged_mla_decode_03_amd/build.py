@@ -20,7 +20,7 @@ CSRC = os.path.join(HERE, "csrc")
 LIB_NAME = "libmla_decode.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
 SOURCES = ["mla_api.hip", "mla_sched.hip", "mla_decode.hip", "mla_decode_wide.hip", "mla_combine.hip",
-           "mla_append.hip"]
+           "mla_append.hip", "mla_absorb.hip"]
 ARCH = "gfx950"
 
 # Packed fp32 VALU forms are kept out of the generated code; -O3 would

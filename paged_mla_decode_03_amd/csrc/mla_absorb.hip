@@ -1,0 +1,103 @@
+// Per-head projections around the decode kernel (gfx950).
+//
+// The decode kernel works in the latent space of the cache (deepseek.csdn.net
+// FlashMLA article, section 2.2, the matrix-absorption paragraph): a head's
+// query enters as [W^UK^T q^C (512); q^R (64)], since q^C . (W^UK c) =
+// (W^UK^T q^C) . c, and its output leaves as the latent sum o = sum_j p_j c_j,
+// which W^UV maps to the head's value space, since W^UV is linear and the
+// weights p_j are shared.  Both are per-head products with a weight shared by
+// all tokens:
+//     query:  q~[t][h][0:512] = sum_d q^C[t][h][d] * W^UK[h][d][:]   (K = 128, N = 512)
+//     output: u[t][h][0:128]  = sum_c o[t][h][c]  * W^UV[h][:][c]   (K = 512, N = 128)
+// with the query weight passed c-major, W^UK^T [h][512][128], so that both
+// read their weight rows along K.
+//
+// At decode sizes (tens to hundreds of tokens) the weights dominate the bytes
+// (16.8 MB each for 128 heads) and the products are bound by HBM, not by the
+// matrix cores, so the kernel reads every operand straight from memory into
+// MFMA fragments: a workgroup takes one head, 64 output columns and 64
+// tokens; wave w computes the 16 x 64 tile of columns 16w..16w+15 as
+// D^T = Bt A^T with v_mfma_f32_16x16x32_bf16 (weight rows as the A operand,
+// token rows as the B operand, both 16-byte loads along K), so each lane ends
+// with 4 consecutive output columns of one token, stored as 8 bytes.
+#include <hip/hip_runtime.h>
+
+#include "mla_absorb.h"
+
+namespace mla {
+
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ inline uint32_t pack2(float a, float b) {
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){a, b}, bf16x2));
+}
+
+__device__ inline bf16x8 load8(const uint16_t* p) { return __builtin_bit_cast(bf16x8, *(const uint4*)p); }
+
+}  // namespace
+
+template <int K, int N>
+__global__ __launch_bounds__(kAbsorbThreads) void mla_absorb_kernel(AbsorbParams p) {
+  static_assert(K % 32 == 0 && N % kAbsorbTileN == 0, "whole tiles");
+  const int h = blockIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int n0 = blockIdx.y * kAbsorbTileN + 16 * wave;
+  const int t0 = blockIdx.z * kAbsorbTileT;
+  const int col = lane & 15;         // weight row (A operand) / token (B operand) within a tile
+  const int kq = 8 * (lane >> 4);    // this lane's 8 values of each 32-wide k step
+
+  const uint16_t* wrow = p.bt + ((size_t)h * N + n0 + col) * K + kq;
+  const uint16_t* arow[4];
+#pragma unroll
+  for (int tt = 0; tt < 4; ++tt) {
+    const int t = min(t0 + 16 * tt + col, p.T - 1);       // rows past T read row T-1; never stored
+    arow[tt] = p.a + (size_t)t * p.a_t + (size_t)h * K + kq;
+  }
+  f32x4 acc[4] = {};
+  constexpr int kUnroll = K / 32 < 4 ? K / 32 : 4;
+  for (int k0 = 0; k0 < K; k0 += 32 * kUnroll) {
+    bf16x8 wf[kUnroll], af[kUnroll][4];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      wf[u] = load8(wrow + k0 + 32 * u);
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt) af[u][tt] = load8(arow[tt] + k0 + 32 * u);
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u)
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt)
+        acc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[u], af[u][tt], acc[tt], 0, 0, 0);
+  }
+  // acc[tt][i] = C[token t0 + 16 tt + col][column n0 + 4 (lane >> 4) + i]
+#pragma unroll
+  for (int tt = 0; tt < 4; ++tt) {
+    const int t = t0 + 16 * tt + col;
+    if (t < p.T) {
+      uint16_t* dst = p.c + (size_t)t * p.c_t + (size_t)h * p.c_h + n0 + 4 * (lane >> 4);
+      *(u32x2*)dst = u32x2{pack2(acc[tt][0], acc[tt][1]), pack2(acc[tt][2], acc[tt][3])};
+    }
+  }
+  // The query's RoPE part is carried over unchanged (first column tile only).
+  if (p.rope && blockIdx.y == 0) {
+    for (int i = threadIdx.x; i < kAbsorbTileT * (kDr / 8); i += kAbsorbThreads) {
+      const int t = t0 + i / (kDr / 8);
+      const int c8 = 8 * (i % (kDr / 8));
+      if (t < p.T)
+        *(uint4*)(p.c + (size_t)t * p.c_t + (size_t)h * p.c_h + N + c8) =
+            *(const uint4*)(p.rope + ((size_t)t * p.H + h) * kDr + c8);
+    }
+  }
+}
+
+template __global__ void mla_absorb_kernel<kDh, 512>(AbsorbParams p);
+template __global__ void mla_absorb_kernel<512, kDh>(AbsorbParams p);
+
+}  // namespace mla

@@ -9,6 +9,7 @@
 #include "../../include/mla_decode.h"
 #include "mla_kernels.h"
 #include "mla_append.h"
+#include "mla_absorb.h"
 
 namespace {
 
@@ -326,6 +327,66 @@ int mla_kvcache_append(const void* kv_new, void* kvcache, const int32_t* block_t
   const int blocks = (p.chunks + mla::kAppendThreads - 1) / mla::kAppendThreads;
   hipLaunchKernelGGL(mla::mla_append_kernel, dim3(blocks), dim3(mla::kAppendThreads), 0, (hipStream_t)stream, p);
   return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+namespace {
+
+int launch_absorb(const mla::AbsorbParams& p, bool query, hipStream_t stream) {
+  const int n = query ? 512 : mla::kDh;
+  const dim3 grid(p.H, n / mla::kAbsorbTileN, (p.T + mla::kAbsorbTileT - 1) / mla::kAbsorbTileT);
+  if (query)
+    hipLaunchKernelGGL((mla::mla_absorb_kernel<mla::kDh, 512>), grid, dim3(mla::kAbsorbThreads), 0, stream, p);
+  else
+    hipLaunchKernelGGL((mla::mla_absorb_kernel<512, mla::kDh>), grid, dim3(mla::kAbsorbThreads), 0, stream, p);
+  return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+int check_absorb_sizes(int tokens, int h_q) {
+  if (tokens <= 0 || h_q <= 0) return MLA_ERR_INVALID_ARG;
+  if ((long long)tokens * h_q * MLA_D_QK >= (1LL << 31) || h_q > 65535 ||
+      (tokens + mla::kAbsorbTileT - 1) / mla::kAbsorbTileT > 65535)
+    return MLA_ERR_UNSUPPORTED;
+  return MLA_OK;
+}
+
+}  // namespace
+
+int mla_absorb_q(const void* q_nope, const void* q_rope, const void* w_uk_t, void* q_out, int tokens, int h_q,
+                 void* stream) {
+  if (!q_nope || !q_rope || !w_uk_t || !q_out) return MLA_ERR_INVALID_ARG;
+  const int st = check_absorb_sizes(tokens, h_q);
+  if (st != MLA_OK) return st;
+  if (!aligned(q_nope, 16) || !aligned(q_rope, 16) || !aligned(w_uk_t, 16) || !aligned(q_out, 16))
+    return MLA_ERR_UNSUPPORTED;
+  mla::AbsorbParams p;
+  p.a = (const uint16_t*)q_nope;
+  p.bt = (const uint16_t*)w_uk_t;
+  p.c = (uint16_t*)q_out;
+  p.rope = (const uint16_t*)q_rope;
+  p.T = tokens;
+  p.H = h_q;
+  p.a_t = (long long)h_q * mla::kDh;
+  p.c_t = (long long)h_q * MLA_D_QK;
+  p.c_h = MLA_D_QK;
+  return launch_absorb(p, true, (hipStream_t)stream);
+}
+
+int mla_absorb_o(const void* o_latent, const void* w_uv, void* out, int tokens, int h_q, void* stream) {
+  if (!o_latent || !w_uv || !out) return MLA_ERR_INVALID_ARG;
+  const int st = check_absorb_sizes(tokens, h_q);
+  if (st != MLA_OK) return st;
+  if (!aligned(o_latent, 16) || !aligned(w_uv, 16) || !aligned(out, 16)) return MLA_ERR_UNSUPPORTED;
+  mla::AbsorbParams p;
+  p.a = (const uint16_t*)o_latent;
+  p.bt = (const uint16_t*)w_uv;
+  p.c = (uint16_t*)out;
+  p.rope = nullptr;
+  p.T = tokens;
+  p.H = h_q;
+  p.a_t = (long long)h_q * MLA_D_V;
+  p.c_t = (long long)h_q * mla::kDh;
+  p.c_h = mla::kDh;
+  return launch_absorb(p, false, (hipStream_t)stream);
 }
 
 }  // extern "C"

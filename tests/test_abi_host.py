@@ -30,7 +30,8 @@ def test_header_declares_the_boundary():
     names = set(declared_functions())
     assert {"mla_get_metadata", "mla_decode_paged", "mla_num_workers", "mla_workspace_bytes",
             "mla_status_string", "mla_decode_splitkv", "mla_decode_splitkv_timed", "mla_combine_splits",
-            "mla_sched_fixed_overhead", "mla_kvcache_append"} <= names
+            "mla_sched_fixed_overhead", "mla_kvcache_append", "mla_absorb_q",
+            "mla_absorb_o"} <= names
 
 
 def test_library_exports_every_declared_symbol():
@@ -133,3 +134,15 @@ def test_append_rejects_invalid_arguments():
                        (dict(batch=1 << 20, s_new=1 << 6), -2), (dict(num_pages=1 << 30), -2)]:
         args = dict(ok, **kw)
         assert lib.mla_kvcache_append(*args.values()) == status, kw
+
+
+def test_absorb_rejects_invalid_arguments():
+    lib = _lib()
+    assert lib.mla_absorb_q(None, FAKE, FAKE, FAKE, 4, 128, None) == -1
+    assert lib.mla_absorb_q(FAKE, FAKE, FAKE, FAKE, 0, 128, None) == -1
+    assert lib.mla_absorb_q(FAKE, FAKE, FAKE, FAKE, 4, -1, None) == -1
+    assert lib.mla_absorb_q(FAKE, FAKE + 8, FAKE, FAKE, 4, 128, None) == -2
+    assert lib.mla_absorb_q(FAKE, FAKE, FAKE, FAKE, 1 << 20, 128, None) == -2
+    assert lib.mla_absorb_o(FAKE, None, FAKE, 4, 128, None) == -1
+    assert lib.mla_absorb_o(FAKE, FAKE, FAKE + 2, 4, 128, None) == -2
+    assert lib.mla_absorb_o(FAKE, FAKE, FAKE, 4, 0, None) == -1
