@@ -14,12 +14,12 @@
 //
 // At decode sizes (tens to hundreds of tokens) the weights dominate the bytes
 // (16.8 MB each for 128 heads) and the products are bound by HBM, not by the
-// matrix cores, so the kernel reads every operand straight from memory into
-// MFMA fragments: a workgroup takes one head, 64 output columns and 64
-// tokens; wave w computes the 16 x 64 tile of columns 16w..16w+15 as
-// D^T = Bt A^T with v_mfma_f32_16x16x32_bf16 (weight rows as the A operand,
-// token rows as the B operand, both 16-byte loads along K), so each lane ends
-// with 4 consecutive output columns of one token, stored as 8 bytes.
+// matrix cores.  A workgroup takes one head, 64 output columns and 64 tokens:
+// it stages the 64 weight rows and 64 token rows in LDS once, and wave w
+// computes the 16 x 64 tile of columns 16w..16w+15 as D^T = Bt A^T with
+// v_mfma_f32_16x16x32_bf16 (weight rows as the A operand, token rows as the
+// B operand, both 16-byte reads along K), so each lane ends with 4
+// consecutive output columns of one token, stored as 8 bytes.
 #include <hip/hip_runtime.h>
 
 #include "mla_absorb.h"
@@ -45,38 +45,41 @@ __device__ inline bf16x8 load8(const uint16_t* p) { return __builtin_bit_cast(bf
 template <int K, int N>
 __global__ __launch_bounds__(kAbsorbThreads) void mla_absorb_kernel(AbsorbParams p) {
   static_assert(K % 32 == 0 && N % kAbsorbTileN == 0, "whole tiles");
+  // The workgroup's 64 weight rows and 64 token rows, staged once in LDS
+  // (rows padded by 16 bytes so that the 16 rows one fragment read touches
+  // fall in different banks); each wave then reads all 64 token rows but
+  // only its own 16 weight rows from there.
+  constexpr int kStride = K + 8;
+  __shared__ __attribute__((aligned(16))) uint16_t sw[kAbsorbTileN * kStride];
+  __shared__ __attribute__((aligned(16))) uint16_t sa[kAbsorbTileT * kStride];
   const int h = blockIdx.x;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int n0 = blockIdx.y * kAbsorbTileN + 16 * wave;
+  const int nb = blockIdx.y * kAbsorbTileN;
   const int t0 = blockIdx.z * kAbsorbTileT;
+  constexpr int kChunks = K / 8;                       // 16-byte chunks per row
+  for (int i = threadIdx.x; i < kAbsorbTileN * kChunks; i += kAbsorbThreads) {
+    const int r = i / kChunks, c = 8 * (i % kChunks);
+    *(uint4*)(sw + r * kStride + c) = *(const uint4*)(p.bt + ((size_t)h * N + nb + r) * K + c);
+    const int t = min(t0 + r, p.T - 1);                  // rows past T repeat row T-1; never stored
+    *(uint4*)(sa + r * kStride + c) = *(const uint4*)(p.a + (size_t)t * p.a_t + (size_t)h * K + c);
+  }
+  __syncthreads();
+
   const int col = lane & 15;         // weight row (A operand) / token (B operand) within a tile
   const int kq = 8 * (lane >> 4);    // this lane's 8 values of each 32-wide k step
-
-  const uint16_t* wrow = p.bt + ((size_t)h * N + n0 + col) * K + kq;
-  const uint16_t* arow[4];
-#pragma unroll
-  for (int tt = 0; tt < 4; ++tt) {
-    const int t = min(t0 + 16 * tt + col, p.T - 1);       // rows past T read row T-1; never stored
-    arow[tt] = p.a + (size_t)t * p.a_t + (size_t)h * K + kq;
-  }
+  const uint16_t* wrow = sw + (16 * wave + col) * kStride + kq;
   f32x4 acc[4] = {};
-  constexpr int kUnroll = K / 32 < 4 ? K / 32 : 4;
-  for (int k0 = 0; k0 < K; k0 += 32 * kUnroll) {
-    bf16x8 wf[kUnroll], af[kUnroll][4];
+#pragma unroll 4
+  for (int k0 = 0; k0 < K; k0 += 32) {
+    const bf16x8 wf = load8(wrow + k0);
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      wf[u] = load8(wrow + k0 + 32 * u);
-#pragma unroll
-      for (int tt = 0; tt < 4; ++tt) af[u][tt] = load8(arow[tt] + k0 + 32 * u);
-    }
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u)
-#pragma unroll
-      for (int tt = 0; tt < 4; ++tt)
-        acc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[u], af[u][tt], acc[tt], 0, 0, 0);
+    for (int tt = 0; tt < 4; ++tt)
+      acc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf, load8(sa + (16 * tt + col) * kStride + kq + k0),
+                                                        acc[tt], 0, 0, 0);
   }
-  // acc[tt][i] = C[token t0 + 16 tt + col][column n0 + 4 (lane >> 4) + i]
+  // acc[tt][i] = C[token t0 + 16 tt + col][column nb + 16 wave + 4 (lane >> 4) + i]
+  const int n0 = nb + 16 * wave;
 #pragma unroll
   for (int tt = 0; tt < 4; ++tt) {
     const int t = t0 + 16 * tt + col;
