@@ -15,8 +15,9 @@
 // At decode sizes (tens to hundreds of tokens) the weights dominate the bytes
 // (16.8 MB each for 128 heads) and the products are bound by HBM, not by the
 // matrix cores.  A workgroup takes one head, 64 output columns and 64 tokens:
-// it stages the 64 weight rows and 64 token rows in LDS once, and wave w
-// computes the 16 x 64 tile of columns 16w..16w+15 as D^T = Bt A^T with
+// it stages the 64 token rows in LDS once (and, for the query projection,
+// the 64 weight rows too), and wave w computes the 16 x 64 tile of columns
+// 16w..16w+15 as D^T = Bt A^T with
 // v_mfma_f32_16x16x32_bf16 (weight rows as the A operand, token rows as the
 // B operand, both 16-byte reads along K), so each lane ends with 4
 // consecutive output columns of one token, stored as 8 bytes.
@@ -45,37 +46,50 @@ __device__ inline bf16x8 load8(const uint16_t* p) { return __builtin_bit_cast(bf
 template <int K, int N>
 __global__ __launch_bounds__(kAbsorbThreads) void mla_absorb_kernel(AbsorbParams p) {
   static_assert(K % 32 == 0 && N % kAbsorbTileN == 0, "whole tiles");
-  // The workgroup's 64 weight rows and 64 token rows, staged once in LDS
-  // (rows padded by 16 bytes so that the 16 rows one fragment read touches
-  // fall in different banks); each wave then reads all 64 token rows but
-  // only its own 16 weight rows from there.
+  // The workgroup's 64 token rows are staged once in LDS (rows padded by 16
+  // bytes so that the 16 rows one fragment read touches fall in different
+  // banks) and read there by all four waves.  Each wave's 16 weight rows are
+  // its own: with K = 512 they go straight from memory into registers (64
+  // VGPRs); with K = 128 they are staged in LDS with the token rows, which
+  // measured faster at decode sizes (64 tokens: 7.4 against 8.0 us).
+  constexpr bool kStageW = K <= 128;
   constexpr int kStride = K + 8;
-  __shared__ __attribute__((aligned(16))) uint16_t sw[kAbsorbTileN * kStride];
+  constexpr int kW = K / 32;
   __shared__ __attribute__((aligned(16))) uint16_t sa[kAbsorbTileT * kStride];
+  __shared__ __attribute__((aligned(16))) uint16_t sw[kStageW ? kAbsorbTileN * kStride : 8];
   const int h = blockIdx.x;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int nb = blockIdx.y * kAbsorbTileN;
   const int t0 = blockIdx.z * kAbsorbTileT;
-  constexpr int kChunks = K / 8;                       // 16-byte chunks per row
-  for (int i = threadIdx.x; i < kAbsorbTileN * kChunks; i += kAbsorbThreads) {
-    const int r = i / kChunks, c = 8 * (i % kChunks);
-    *(uint4*)(sw + r * kStride + c) = *(const uint4*)(p.bt + ((size_t)h * N + nb + r) * K + c);
-    const int t = min(t0 + r, p.T - 1);                  // rows past T repeat row T-1; never stored
-    *(uint4*)(sa + r * kStride + c) = *(const uint4*)(p.a + (size_t)t * p.a_t + (size_t)h * K + c);
-  }
-  __syncthreads();
-
   const int col = lane & 15;         // weight row (A operand) / token (B operand) within a tile
   const int kq = 8 * (lane >> 4);    // this lane's 8 values of each 32-wide k step
-  const uint16_t* wrow = sw + (16 * wave + col) * kStride + kq;
+  bf16x8 wf[kW];
+  if constexpr (!kStageW) {
+    const uint16_t* wrow = p.bt + ((size_t)h * N + nb + 16 * wave + col) * K + kq;
+#pragma unroll
+    for (int k = 0; k < kW; ++k) wf[k] = load8(wrow + 32 * k);
+  }
+  constexpr int kChunks = K / 8;                       // 16-byte chunks per row
+  for (int i = threadIdx.x; i < kAbsorbTileT * kChunks; i += kAbsorbThreads) {
+    const int r = i / kChunks, c = 8 * (i % kChunks);
+    const int t = min(t0 + r, p.T - 1);                  // rows past T repeat row T-1; never stored
+    *(uint4*)(sa + r * kStride + c) = *(const uint4*)(p.a + (size_t)t * p.a_t + (size_t)h * K + c);
+    if constexpr (kStageW)
+      *(uint4*)(sw + r * kStride + c) = *(const uint4*)(p.bt + ((size_t)h * N + nb + r) * K + c);
+  }
+  __syncthreads();
+  if constexpr (kStageW) {
+#pragma unroll
+    for (int k = 0; k < kW; ++k) wf[k] = load8(sw + (16 * wave + col) * kStride + kq + 32 * k);
+  }
+
   f32x4 acc[4] = {};
-#pragma unroll 4
-  for (int k0 = 0; k0 < K; k0 += 32) {
-    const bf16x8 wf = load8(wrow + k0);
+#pragma unroll
+  for (int k = 0; k < kW; ++k) {
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt)
-      acc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf, load8(sa + (16 * tt + col) * kStride + kq + k0),
+      acc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[k], load8(sa + (16 * tt + col) * kStride + kq + 32 * k),
                                                         acc[tt], 0, 0, 0);
   }
   // acc[tt][i] = C[token t0 + 16 tt + col][column nb + 16 wave + 4 (lane >> 4) + i]
