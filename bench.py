@@ -63,6 +63,7 @@ KERNEL_SOURCES = {
     "mla_decode_kernel": ("mla_decode.hip", "mla_decode_common.h", "mla_kernels.h"),
     "mla_decode_wide_kernel": ("mla_decode_wide.hip", "mla_decode_common.h", "mla_kernels.h"),
     "mla_append_kernel": ("mla_append.hip", "mla_append.h", "mla_kernels.h"),
+    "mla_absorb_kernel": ("mla_absorb.hip", "mla_absorb.h"),
 }
 
 
@@ -224,6 +225,11 @@ def bench_absorb(args):
     bytes_q = 2 * (T * H * (128 + 64 + 576) + H * 512 * 128)
     bytes_o = 2 * (T * H * (512 + 128) + H * 128 * 512)
     flops = 2 * T * H * 128 * 512
+    if args.copy_mb > 0:              # the counters' calibration copy, as for the decode
+        src = torch.empty(args.copy_mb << 20, dtype=torch.uint8, device=dev)
+        torch.empty_like(src).copy_(src)
+        torch.cuda.synchronize()
+        del src
     times = {}
     for name, fn in (("absorb_q", lambda: absorb_q(qn, qr, w_uk_t, q_out)), ("absorb_o", lambda: absorb_o(o, w_uv, u_out))):
         for _ in range(args.warmup):
@@ -258,7 +264,8 @@ def bench_absorb(args):
            "tflops": round(2 * flops / ((tq + to) * 1e-3) / 1e12, 2),
            "roofline": {"kernel": "mla_absorb_kernel", "bound": "hbm", "achieved": round(achieved, 2),
                         "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                        "traffic": None, "per_launch": {"bytes_q": bytes_q, "bytes_o": bytes_o, "flops_each": flops}}}
+                        "traffic": measured_traffic(w, "mla_absorb_kernel", f"{args.workload}_absorb"),
+                        "per_launch": {"bytes_q": bytes_q, "bytes_o": bytes_o, "flops_each": flops}}}
     print(json.dumps(out), flush=True)
 
 
