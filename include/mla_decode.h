@@ -32,9 +32,15 @@
  *     must stay alive until the stream has run the work.
  *   - Calls return MLA_OK or a negative status.  Arguments are checked on the
  *     host before anything is launched, so an invalid call launches nothing.
- *     The *contents* of block_table and cache_seqlens cannot be checked on the
- *     host: page ids outside [0, num_pages) or lengths above
- *     64 * max_pages_per_seq are undefined behaviour.
+ *     The *contents* of block_table and cache_seqlens live on the device and
+ *     are not checked by default.  The decode kernels never form an address
+ *     outside the cache from them: a page id outside [0, num_pages) is read
+ *     as a page of zeros, and blocks past max_pages_per_seq (a length above
+ *     64 * max_pages_per_seq) as such a page too; the output for that
+ *     sequence is then meaningless but finite.  mla_check_inputs() finds such
+ *     entries, and with MLA_DEBUG_CHECKS=1 in the environment (or
+ *     mla_set_debug_checks(1)) every decode call runs it first and returns
+ *     MLA_ERR_BAD_INPUT without launching the decode.
  *   - Fixed sizes: d_qk = 576, dv = 512, page size 64, bf16 q / kvcache / o,
  *     fp32 lse.  All tensors are dense and row-major in the layouts below.
  */
@@ -54,6 +60,7 @@ extern "C" {
 #define MLA_ERR_WORKSPACE (-3)    /* workspace smaller than mla_workspace_bytes() */
 #define MLA_ERR_METADATA (-4)     /* num_workers inconsistent with the launch */
 #define MLA_ERR_HIP (-5)          /* the HIP runtime reported an error */
+#define MLA_ERR_BAD_INPUT (-6)    /* debug checks: a block_table / cache_seqlens entry is out of range */
 
 #define MLA_PAGE_SIZE 64
 #define MLA_D_QK 576
@@ -167,6 +174,31 @@ int mla_decode_splitkv_timed(const void* q, const void* kvcache, const int32_t* 
 int mla_combine_splits(const int32_t* num_splits, int batch, int s_q, int h_q, int h_kv, int dv,
                        int num_workers, void* o, float* lse, const void* workspace,
                        size_t workspace_bytes, void* stream);
+
+/* Checker of the tables a decode reads (the paging contract of the
+ * deepseek.csdn.net FlashMLA article, section 4.2(1): logical block j of
+ * sequence b is physical page block_table[b][j]; the arguments of the call on
+ * the dolphin-ai.jp FlashMLA page, "FlashMLA の使用方法" step 4).  One
+ * workgroup checks, for every sequence b, that 0 <= L_b <= 64 *
+ * max_pages_per_seq and that block_table[b][j] lies in [0, num_pages) for
+ * every block j < ceil(L_b / 64) (padding past that is never read and not
+ * checked), and writes
+ *   result [dev] int32 [4]: number of bad entries, the first bad sequence
+ *                (-1 if none), its first bad block (-1 when its length is
+ *                bad), 0.
+ * Asynchronous on `stream` like every launch; the caller reads result after
+ * synchronising.  Errors: MLA_ERR_INVALID_ARG for null pointers or
+ * non-positive sizes, MLA_ERR_UNSUPPORTED for misaligned pointers. */
+int mla_check_inputs(const int32_t* block_table, int max_pages_per_seq, int num_pages,
+                     const int32_t* cache_seqlens, int batch, int32_t* result, void* stream);
+
+/* Turn the debug checks of every decode entry point on (1) or off (0) for
+ * the process, overriding MLA_DEBUG_CHECKS.  With them on, mla_decode_paged,
+ * mla_decode_splitkv and mla_decode_splitkv_timed run mla_check_inputs into
+ * the first 16 bytes of their workspace, synchronise `stream` to read its
+ * answer (so such calls cannot be captured into a graph), and return
+ * MLA_ERR_BAD_INPUT without launching anything more if an entry is bad. */
+void mla_set_debug_checks(int enable);
 
 /* The step before decode: write the latent rows of new tokens into the
  * paged cache.  The cache keeps the [c^KV (512); k^R (64)] row of every

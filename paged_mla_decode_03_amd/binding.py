@@ -72,6 +72,10 @@ def _load():
     lib.mla_kvcache_append.argtypes = [vp, vp, vp, c_int, c_int, vp, c_int, c_int, c_int, c_int, vp, vp]
     lib.mla_absorb_q.argtypes = [vp, vp, vp, vp, c_int, c_int, vp]
     lib.mla_absorb_o.argtypes = [vp, vp, vp, c_int, c_int, vp]
+    lib.mla_check_inputs.restype = c_int
+    lib.mla_check_inputs.argtypes = [vp, c_int, c_int, vp, c_int, vp, vp]
+    lib.mla_set_debug_checks.restype = None
+    lib.mla_set_debug_checks.argtypes = [c_int]
     _lib = lib
     return lib
 
@@ -132,17 +136,18 @@ def workspace_bytes(batch: int, s_q: int, h_q: int, h_kv: int, dv: int, W: int) 
 
 
 def _decode_call(entry: str, q, kvcache, block_table, cache_seqlens, dv, tile_scheduler_metadata, num_splits,
-                 causal, softmax_scale, o, lse, workspace, *extra):
+                 causal, softmax_scale, buffers, *extra):
     device = q.device
     B, s_q, h_q, d_qk = q.shape
     P, page, h_kv, d2 = kvcache.shape
     W = tile_scheduler_metadata.shape[0]
+    _check_buffers(buffers, B, s_q, h_q, h_kv, dv, W, device)
     stream = _stream_handle(device)
     _check(entry, getattr(_load(), entry)(
         q.data_ptr(), kvcache.data_ptr(), block_table.data_ptr(), block_table.shape[1], P,
         cache_seqlens.data_ptr(), B, s_q, h_q, h_kv, d_qk, dv, tile_scheduler_metadata.data_ptr(),
-        num_splits.data_ptr(), W, int(bool(causal)), float(softmax_scale or 0.0), o.data_ptr(), lse.data_ptr(),
-        workspace.data_ptr(), workspace.numel(), stream, *extra))
+        num_splits.data_ptr(), W, int(bool(causal)), float(softmax_scale or 0.0), buffers.o.data_ptr(),
+        buffers.lse.data_ptr(), buffers.workspace.data_ptr(), buffers.workspace.numel(), stream, *extra))
 
 
 class DecodeBuffers:
@@ -155,6 +160,22 @@ class DecodeBuffers:
         self.lse = torch.empty((B, h_q, s_q), dtype=torch.float32, device=q.device)
         self.workspace = torch.empty(max(workspace_bytes(B, s_q, h_q, h_kv, dv, W), 256), dtype=torch.uint8,
                                      device=q.device)
+
+
+def _check_buffers(buffers: "DecodeBuffers", B: int, s_q: int, h_q: int, h_kv: int, dv: int, W: int,
+                   device: torch.device):
+    """Caller-supplied outputs must match this call's shape: the library
+    writes o and lse for every (b, i, h) of the call."""
+    _require(buffers.o, "buffers.o", torch.bfloat16, device)
+    _require(buffers.lse, "buffers.lse", torch.float32, device)
+    _require(buffers.workspace, "buffers.workspace", torch.uint8, device)
+    if tuple(buffers.o.shape) != (B, s_q, h_q, dv):
+        raise ValueError(f"buffers.o has shape {tuple(buffers.o.shape)}, this call writes {(B, s_q, h_q, dv)}")
+    if tuple(buffers.lse.shape) != (B, h_q, s_q):
+        raise ValueError(f"buffers.lse has shape {tuple(buffers.lse.shape)}, this call writes {(B, h_q, s_q)}")
+    need = workspace_bytes(B, s_q, h_q, h_kv, dv, W)
+    if buffers.workspace.numel() < need:
+        raise ValueError(f"buffers.workspace holds {buffers.workspace.numel()} bytes, this call needs {need}")
 
 
 def _validate(q, kvcache, block_table, cache_seqlens, tile_scheduler_metadata, num_splits):
@@ -186,7 +207,7 @@ def mla_decode_paged(q: torch.Tensor, kvcache: torch.Tensor, block_table: torch.
     if buffers is None:
         buffers = DecodeBuffers(q, kvcache, dv, tile_scheduler_metadata.shape[0])
     _decode_call("mla_decode_paged", q, kvcache, block_table, cache_seqlens, dv, tile_scheduler_metadata,
-                 num_splits, causal, softmax_scale, buffers.o, buffers.lse, buffers.workspace)
+                 num_splits, causal, softmax_scale, buffers)
     return buffers.o, buffers.lse
 
 
@@ -197,7 +218,7 @@ def mla_decode_splitkv(q, kvcache, block_table, cache_seqlens, dv, tile_schedule
     if buffers is None:
         buffers = DecodeBuffers(q, kvcache, dv, tile_scheduler_metadata.shape[0])
     _decode_call("mla_decode_splitkv", q, kvcache, block_table, cache_seqlens, dv, tile_scheduler_metadata,
-                 num_splits, causal, softmax_scale, buffers.o, buffers.lse, buffers.workspace)
+                 num_splits, causal, softmax_scale, buffers)
     return buffers
 
 
@@ -214,8 +235,7 @@ def mla_decode_splitkv_timed(q, kvcache, block_table, cache_seqlens, dv, tile_sc
         if not e.cuda_event:     # torch creates the HIP event on its first record
             e.record()
     _decode_call("mla_decode_splitkv_timed", q, kvcache, block_table, cache_seqlens, dv, tile_scheduler_metadata,
-                 num_splits, causal, softmax_scale, buffers.o, buffers.lse, buffers.workspace,
-                 start.cuda_event, stop.cuda_event)
+                 num_splits, causal, softmax_scale, buffers, start.cuda_event, stop.cuda_event)
     return buffers
 
 
@@ -223,6 +243,8 @@ def mla_combine_splits(num_splits: torch.Tensor, s_q: int, h_q: int, h_kv: int, 
                        buffers: DecodeBuffers) -> Tuple[torch.Tensor, torch.Tensor]:
     """The combine kernel alone (last launch of mla_decode_paged)."""
     B = num_splits.numel() - 1
+    _require(num_splits, "num_splits", torch.int32, num_splits.device)
+    _check_buffers(buffers, B, s_q, h_q, h_kv, dv, W, num_splits.device)
     stream = _stream_handle(num_splits.device)
     _check("mla_combine_splits", _load().mla_combine_splits(
         num_splits.data_ptr(), B, s_q, h_q, h_kv, dv, W, buffers.o.data_ptr(), buffers.lse.data_ptr(),
@@ -277,6 +299,8 @@ def absorb_q(q_nope: torch.Tensor, q_rope: torch.Tensor, w_uk_t: torch.Tensor,
     if out is None:
         out = torch.empty(q_nope.shape[:-1] + (576,), dtype=torch.bfloat16, device=device)
     _require(out, "out", torch.bfloat16, device)
+    if tuple(out.shape) != tuple(q_nope.shape[:-1]) + (576,):
+        raise ValueError(f"out has shape {tuple(out.shape)}, expected {tuple(q_nope.shape[:-1]) + (576,)}")
     tokens = q_nope.numel() // (h * 128)
     _check("mla_absorb_q", _load().mla_absorb_q(q_nope.data_ptr(), q_rope.data_ptr(), w_uk_t.data_ptr(),
                                                 out.data_ptr(), tokens, h, _stream_handle(device)))
@@ -295,7 +319,36 @@ def absorb_o(o_latent: torch.Tensor, w_uv: torch.Tensor, out: Optional[torch.Ten
     if out is None:
         out = torch.empty(o_latent.shape[:-1] + (128,), dtype=torch.bfloat16, device=device)
     _require(out, "out", torch.bfloat16, device)
+    if tuple(out.shape) != tuple(o_latent.shape[:-1]) + (128,):
+        raise ValueError(f"out has shape {tuple(out.shape)}, expected {tuple(o_latent.shape[:-1]) + (128,)}")
     tokens = o_latent.numel() // (h * 512)
     _check("mla_absorb_o", _load().mla_absorb_o(o_latent.data_ptr(), w_uv.data_ptr(), out.data_ptr(), tokens, h,
                                                 _stream_handle(device)))
     return out
+
+
+def check_inputs(block_table: torch.Tensor, cache_seqlens: torch.Tensor, num_pages: int,
+                 result: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Run the table checker on the GPU: returns int32 [4] on the device
+    (bad entries, first bad sequence, its first bad block, 0); see
+    mla_check_inputs in the C header."""
+    device = block_table.device
+    _require(block_table, "block_table", torch.int32, device)
+    _require(cache_seqlens, "cache_seqlens", torch.int32, device)
+    if block_table.dim() != 2 or cache_seqlens.numel() != block_table.shape[0]:
+        raise ValueError("block_table must be [B][max_pages] and cache_seqlens [B]")
+    if result is None:
+        result = torch.empty(4, dtype=torch.int32, device=device)
+    _require(result, "result", torch.int32, device)
+    if result.numel() != 4:
+        raise ValueError("result must hold 4 int32")
+    _check("mla_check_inputs", _load().mla_check_inputs(
+        block_table.data_ptr(), block_table.shape[1], int(num_pages), cache_seqlens.data_ptr(),
+        block_table.shape[0], result.data_ptr(), _stream_handle(device)))
+    return result
+
+
+def set_debug_checks(enable: bool) -> None:
+    """Turn the checker in front of every decode call on or off (overrides
+    MLA_DEBUG_CHECKS for the process)."""
+    _load().mla_set_debug_checks(int(bool(enable)))

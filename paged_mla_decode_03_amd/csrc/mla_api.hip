@@ -2,6 +2,10 @@
 // workspace sizing, launch configuration.  Every check runs before any HIP
 // call, so an invalid call launches nothing and needs no device.
 #include <math.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <atomic>
 #include <mutex>
 
 #include <hip/hip_ext.h>
@@ -96,7 +100,7 @@ int check_decode(const void* q, const void* kvcache, const int32_t* block_table,
 }
 
 mla::DecodeParams decode_params(const void* q, const void* kvcache, const int32_t* block_table,
-                                int max_pages_per_seq, const int32_t* cache_seqlens, const Shape& s,
+                                int max_pages_per_seq, int num_pages, const int32_t* cache_seqlens, const Shape& s,
                                 const int32_t* meta, const int32_t* num_splits, int num_workers, int causal,
                                 float softmax_scale, void* o, float* lse, void* workspace) {
   mla::DecodeParams p;
@@ -119,6 +123,7 @@ mla::DecodeParams decode_params(const void* q, const void* kvcache, const int32_
   p.rows = s.rows;
   p.group = s.group;
   p.max_pages = max_pages_per_seq;
+  p.num_pages = num_pages;
   p.num_workers = num_workers;
   p.row_blocks = row_blocks_of(s.rows);
   p.causal = causal;
@@ -174,6 +179,49 @@ int launch_combine(const mla::DecodeParams& d, hipStream_t stream) {
   return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
 
+// Opt-in checks of the tables' contents (MLA_DEBUG_CHECKS=1 in the
+// environment, or mla_set_debug_checks): -1 = not yet read from the
+// environment.
+std::atomic<int> g_debug_checks{-1};
+
+bool debug_checks_on() {
+  int v = g_debug_checks.load();
+  if (v < 0) {
+    const char* e = getenv("MLA_DEBUG_CHECKS");
+    v = (e && e[0] && strcmp(e, "0") != 0) ? 1 : 0;
+    int expected = -1;
+    g_debug_checks.compare_exchange_strong(expected, v);
+    v = g_debug_checks.load();
+  }
+  return v == 1;
+}
+
+void launch_check(const int32_t* block_table, int max_pages, int num_pages, const int32_t* seqlens, int batch,
+                  int32_t* result, hipStream_t stream) {
+  mla::CheckParams c;
+  c.block_table = block_table;
+  c.seqlens = seqlens;
+  c.result = result;
+  c.batch = batch;
+  c.max_pages = max_pages;
+  c.num_pages = num_pages;
+  hipLaunchKernelGGL(mla::mla_check_kernel, dim3(1), dim3(mla::kCheckThreads), 0, stream, c);
+}
+
+// The debug path of a decode call: run the checker into the first 16 bytes
+// of the workspace (the decode writes it again afterwards) and wait for its
+// answer; the decode is launched only if every entry is valid.
+int debug_check_tables(const mla::DecodeParams& p, int num_pages, hipStream_t stream) {
+  int32_t* result = (int32_t*)p.ws_o;
+  launch_check(p.block_table, p.max_pages, num_pages, p.seqlens, p.batch, result, stream);
+  if (hipGetLastError() != hipSuccess) return MLA_ERR_HIP;
+  int32_t host[4] = {0, 0, 0, 0};
+  if (hipMemcpyAsync(host, result, sizeof(host), hipMemcpyDeviceToHost, stream) != hipSuccess ||
+      hipStreamSynchronize(stream) != hipSuccess)
+    return MLA_ERR_HIP;
+  return host[0] == 0 ? MLA_OK : MLA_ERR_BAD_INPUT;
+}
+
 int check_append(const void* kv_new, const void* kvcache, const int32_t* block_table, int max_pages_per_seq,
                  int num_pages, const int32_t* cache_seqlens, int batch, int s_new, int h_kv, int d_qk,
                  const int32_t* bad_rows) {
@@ -200,6 +248,7 @@ const char* mla_status_string(int status) {
     case MLA_ERR_WORKSPACE: return "MLA_ERR_WORKSPACE: workspace too small";
     case MLA_ERR_METADATA: return "MLA_ERR_METADATA: num_workers out of range";
     case MLA_ERR_HIP: return "MLA_ERR_HIP: HIP runtime error";
+    case MLA_ERR_BAD_INPUT: return "MLA_ERR_BAD_INPUT: block_table or cache_seqlens holds an invalid entry";
     default: return "unknown status";
   }
 }
@@ -253,8 +302,9 @@ int mla_decode_splitkv(const void* q, const void* kvcache, const int32_t* block_
                         h_kv, d_qk, dv, meta, num_splits, num_workers, causal, o, lse, workspace,
                         workspace_bytes_given, &s);
   if (st != MLA_OK) return st;
-  const mla::DecodeParams p = decode_params(q, kvcache, block_table, max_pages_per_seq, cache_seqlens, s, meta,
+  const mla::DecodeParams p = decode_params(q, kvcache, block_table, max_pages_per_seq, num_pages, cache_seqlens, s, meta,
                                             num_splits, num_workers, causal, softmax_scale, o, lse, workspace);
+  if (debug_checks_on() && (st = debug_check_tables(p, num_pages, (hipStream_t)stream)) != MLA_OK) return st;
   return launch_decode(p, (hipStream_t)stream);
 }
 
@@ -269,8 +319,9 @@ int mla_decode_splitkv_timed(const void* q, const void* kvcache, const int32_t* 
                         workspace_bytes_given, &s);
   if (st != MLA_OK) return st;
   if (!start_event || !stop_event) return MLA_ERR_INVALID_ARG;
-  const mla::DecodeParams p = decode_params(q, kvcache, block_table, max_pages_per_seq, cache_seqlens, s, meta,
+  const mla::DecodeParams p = decode_params(q, kvcache, block_table, max_pages_per_seq, num_pages, cache_seqlens, s, meta,
                                             num_splits, num_workers, causal, softmax_scale, o, lse, workspace);
+  if (debug_checks_on() && (st = debug_check_tables(p, num_pages, (hipStream_t)stream)) != MLA_OK) return st;
   return launch_decode(p, (hipStream_t)stream, (hipEvent_t)start_event, (hipEvent_t)stop_event);
 }
 
@@ -284,7 +335,7 @@ int mla_combine_splits(const int32_t* num_splits, int batch, int s_q, int h_q, i
   if (num_workers <= 0 || num_workers > MLA_MAX_WORKERS) return MLA_ERR_METADATA;
   if (!aligned(o, 16) || !aligned(lse, 4) || !aligned(workspace, 256)) return MLA_ERR_UNSUPPORTED;
   if (workspace_bytes_given < workspace_bytes(s, num_workers)) return MLA_ERR_WORKSPACE;
-  mla::DecodeParams d = decode_params(nullptr, nullptr, nullptr, 1, nullptr, s, nullptr, num_splits,
+  mla::DecodeParams d = decode_params(nullptr, nullptr, nullptr, 1, 1, nullptr, s, nullptr, num_splits,
                                       num_workers, 0, 0.f, o, lse, (void*)workspace);
   return launch_combine(d, (hipStream_t)stream);
 }
@@ -299,12 +350,25 @@ int mla_decode_paged(const void* q, const void* kvcache, const int32_t* block_ta
                         h_kv, d_qk, dv, meta, num_splits, num_workers, causal, o, lse, workspace,
                         workspace_bytes_given, &s);
   if (st != MLA_OK) return st;
-  const mla::DecodeParams p = decode_params(q, kvcache, block_table, max_pages_per_seq, cache_seqlens, s, meta,
+  const mla::DecodeParams p = decode_params(q, kvcache, block_table, max_pages_per_seq, num_pages, cache_seqlens, s, meta,
                                             num_splits, num_workers, causal, softmax_scale, o, lse, workspace);
+  if (debug_checks_on() && (st = debug_check_tables(p, num_pages, (hipStream_t)stream)) != MLA_OK) return st;
   st = launch_decode(p, (hipStream_t)stream);
   if (st != MLA_OK) return st;
   return launch_combine(p, (hipStream_t)stream);
 }
+
+int mla_check_inputs(const int32_t* block_table, int max_pages_per_seq, int num_pages,
+                     const int32_t* cache_seqlens, int batch, int32_t* result, void* stream) {
+  if (!block_table || !cache_seqlens || !result) return MLA_ERR_INVALID_ARG;
+  if (batch <= 0 || max_pages_per_seq <= 0 || num_pages <= 0) return MLA_ERR_INVALID_ARG;
+  if (!aligned(block_table, 4) || !aligned(cache_seqlens, 4) || !aligned(result, 4)) return MLA_ERR_UNSUPPORTED;
+  if ((long long)batch * (max_pages_per_seq + 1) >= (1LL << 40)) return MLA_ERR_UNSUPPORTED;
+  launch_check(block_table, max_pages_per_seq, num_pages, cache_seqlens, batch, result, (hipStream_t)stream);
+  return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+void mla_set_debug_checks(int enable) { g_debug_checks.store(enable ? 1 : 0); }
 
 int mla_kvcache_append(const void* kv_new, void* kvcache, const int32_t* block_table, int max_pages_per_seq,
                        int num_pages, const int32_t* cache_seqlens, int batch, int s_new, int h_kv, int d_qk,

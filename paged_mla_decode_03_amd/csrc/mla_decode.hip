@@ -132,7 +132,7 @@ __device__ __forceinline__ void decode_role(const DecodeParams& p, DecodeShared&
   // gq counts half pages issued.
   int lb = cb, lpage = cpage, lend = cend, lp0 = cpage, lhalf = 0, gq = 0;
   bool lvalid = true;
-  int lpid = ld_uniform(p.block_table + (size_t)lb * p.max_pages + page_in_order(lpage, lp0, lend, rb, nrb));
+  int lpid = page_id(p, lb, page_in_order(lpage, lp0, lend, rb, nrb));
   const int ow = wave - 4;   // output wave index
   constexpr int kDma = scorer ? kScoreDma : kOutputDma;   // this wave's DMAs per half page
   constexpr int kCol0 = scorer ? kOutputDma : 0;          // its first tile column
@@ -141,7 +141,7 @@ __device__ __forceinline__ void decode_role(const DecodeParams& p, DecodeShared&
   // and advance the cursor; returns whether anything was issued.
   auto issue_half = [&]() __attribute__((always_inline)) {
     if (!lvalid) return false;
-    const __amdgpu_buffer_rsrc_t rsrc = page_resource(kv_head + (size_t)lpid * page_stride_bytes, page_span);
+    const __amdgpu_buffer_rsrc_t rsrc = page_rsrc(kv_head, lpid, p.num_pages, page_stride_bytes, page_span);
     const uint32_t dst =
         ring_base + (uint32_t)((gq & (kRingSlots - 1)) * kHalfBytes) + (uint32_t)((trow * 9 + kCol0) * 1024);
     const int soff0 = (kHalfRows * lhalf + 8 * trow) * row_stride_bytes + kCol0 * 128;
@@ -153,7 +153,7 @@ __device__ __forceinline__ void decode_role(const DecodeParams& p, DecodeShared&
     } else {
       lhalf = 0;
       lvalid = next_page(meta, p.seqlens, lb, lpage, lend, lp0);
-      if (lvalid) lpid = ld_uniform(p.block_table + (size_t)lb * p.max_pages + page_in_order(lpage, lp0, lend, rb, nrb));
+      if (lvalid) lpid = page_id(p, lb, page_in_order(lpage, lp0, lend, rb, nrb));
     }
     return true;
   };
@@ -327,8 +327,8 @@ __device__ __forceinline__ void decode_role(const DecodeParams& p, DecodeShared&
               for (int h = 0; h < 2; ++h) {
                 const float w0 = __builtin_amdgcn_exp2f(__builtin_fmaf(x[i][2 * h], p.scale_log2, -mu));
                 const float w1 = __builtin_amdgcn_exp2f(__builtin_fmaf(x[i][2 * h + 1], p.scale_log2, -mu));
-                l_run += w0 + w1;
                 pk[i][h] = pack_bf16x2(w0, w1);
+                l_run += sum_bf16x2(pk[i][h]);
               }
             // Slot 8*grp4 + 4*i + e holds key 16i + 4*grp4 + e of the half page.
             *(__attribute__((address_space(3))) u32x4*)(p_base + (uint32_t)((hp & 1) * kPBytes) + pw_off) =
@@ -420,7 +420,7 @@ __device__ __forceinline__ void decode_role(const DecodeParams& p, DecodeShared&
         lhalf = 0;
         lvalid = true;
         gq = gbase;
-        lpid = ld_uniform(p.block_table + (size_t)lb * p.max_pages + page_in_order(lpage, lp0, lend, rb, nrb));
+        lpid = page_id(p, lb, page_in_order(lpage, lp0, lend, rb, nrb));
         issue_half();
         const bool issued = issue_half();
         wait_next(issued);

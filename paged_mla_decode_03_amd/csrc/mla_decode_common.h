@@ -29,7 +29,9 @@ constexpr int kWaitVmcnt0 = 0x0F70;
 // assembly, so that no pass can judge it redundant and drop it.
 __device__ inline void wait_dma_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
-__device__ inline int pages_of(int seqlen) { return (seqlen + kPage - 1) / kPage; }
+// Pages of a sequence of `seqlen` tokens (0 for seqlen <= 0; no overflow
+// near INT_MAX).
+__device__ inline int pages_of(int seqlen) { return seqlen > 0 ? (seqlen - 1) / kPage + 1 : 0; }
 
 // Read-only table entry at a wave-uniform address, through the constant
 // address space: a scalar load, counted by lgkmcnt.  Keeping the kernel's own
@@ -67,6 +69,16 @@ __device__ inline __amdgpu_buffer_rsrc_t page_resource(const char* page_head, ui
   return __builtin_amdgcn_make_buffer_rsrc((void*)page_head, (short)0, (int)page_bytes, (int)kBufferConfig);
 }
 
+// Buffer resource over page `pid` of the latent head whose first row starts
+// at kv_head.  A page id outside [0, num_pages) (a bad block_table entry)
+// gets a resource of size 0: its DMAs then read zeros and no address outside
+// the cache is ever formed.
+__device__ inline __amdgpu_buffer_rsrc_t page_rsrc(const char* kv_head, int pid, int num_pages, size_t page_stride,
+                                                   uint32_t page_bytes) {
+  const bool ok = (unsigned)pid < (unsigned)num_pages;
+  return page_resource(kv_head + (ok ? (size_t)pid * page_stride : (size_t)0), ok ? page_bytes : 0u);
+}
+
 // DMA number k (0 .. kPerWave-1) of this wave for one page, when each of the
 // workgroup's waves issues kPerWave of the page's 72: tile j = kPerWave *
 // wave + k, i.e. tile row j / 9 (rows 8*(j/9) ..+7) x tile column j % 9
@@ -92,9 +104,8 @@ __device__ inline void stage_tile(__amdgpu_buffer_rsrc_t rsrc, uint32_t lane_off
 }
 
 template <int kPerWave>
-__device__ inline void stage_page(const char* page_head, uint32_t page_bytes, uint32_t lane_off,
-                                  int row_stride_bytes, uint32_t lds_dst, int wave) {
-  const __amdgpu_buffer_rsrc_t rsrc = page_resource(page_head, page_bytes);
+__device__ inline void stage_page(__amdgpu_buffer_rsrc_t rsrc, uint32_t lane_off, int row_stride_bytes,
+                                  uint32_t lds_dst, int wave) {
 #pragma unroll
   for (int k = 0; k < kPerWave; ++k) stage_tile<kPerWave>(rsrc, lane_off, row_stride_bytes, lds_dst, wave, k);
 }
@@ -140,6 +151,22 @@ __device__ inline uint32_t pack_bf16x2(float a, float b) {
   typedef float f32x2 __attribute__((ext_vector_type(2)));
   typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
   return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){a, b}, bf16x2));
+}
+
+// Sum of the two bf16 values packed by pack_bf16x2, in fp32 (exact).  The
+// row sums are accumulated from the rounded weights that the PV product
+// actually uses, so that each output row is a convex combination of cached
+// values: the rounding of a weight then moves O only by that weight's share
+// of (v_j - O), never by a mismatch between the weights and their sum.
+__device__ inline float sum_bf16x2(uint32_t packed) {
+  return __builtin_bit_cast(float, packed << 16) + __builtin_bit_cast(float, packed & 0xFFFF0000u);
+}
+
+// Physical page of logical block j of sequence b.  A block past the end of
+// the table row (a length above 64 * max_pages) reads as -1, never as the
+// next row or past the table.
+__device__ inline int page_id(const DecodeParams& p, int b, int j) {
+  return j < p.max_pages ? ld_uniform(p.block_table + (size_t)b * p.max_pages + j) : -1;
 }
 
 // End page of sequence b's part of this worker's range.

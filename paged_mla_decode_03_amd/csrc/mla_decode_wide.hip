@@ -164,11 +164,11 @@ __device__ __forceinline__ void wide_worker(const DecodeParams& p, char (*lds_pa
   // is read now, one page ahead of its DMAs.
   int next_pid = 0;
   {
-    const int page_id = ld_uniform(p.block_table + (size_t)lb * p.max_pages + page_in_order(lpage, lp0, lend, rb, nrb));
+    const int first_pid = page_id(p, lb, page_in_order(lpage, lp0, lend, rb, nrb));
     lvalid = next_page(meta, p.seqlens, lb, lpage, lend, lp0);
-    stage_page<kWideDmaPerWave>(kv_head + (size_t)page_id * page_stride_bytes, page_span, lane_src_off,
-                                row_stride_bytes, lds_base, wave);
-    if (lvalid) next_pid = ld_uniform(p.block_table + (size_t)lb * p.max_pages + page_in_order(lpage, lp0, lend, rb, nrb));
+    stage_page<kWideDmaPerWave>(page_rsrc(kv_head, first_pid, p.num_pages, page_stride_bytes, page_span),
+                                lane_src_off, row_stride_bytes, lds_base, wave);
+    if (lvalid) next_pid = page_id(p, lb, page_in_order(lpage, lp0, lend, rb, nrb));
   }
 
   int it = 0;
@@ -226,7 +226,7 @@ __device__ __forceinline__ void wide_worker(const DecodeParams& p, char (*lds_pa
           __syncthreads();
         }
         const bool dma = lvalid;
-        const __amdgpu_buffer_rsrc_t dma_rsrc = page_resource(kv_head + (size_t)next_pid * page_stride_bytes, page_span);
+        const __amdgpu_buffer_rsrc_t dma_rsrc = page_rsrc(kv_head, next_pid, p.num_pages, page_stride_bytes, page_span);
         const uint32_t dma_dst = lds_base + ((it + 1) & 1) * kPageBytes;
 
         const uint32_t page_base = (uint32_t)(uintptr_t)buf;
@@ -305,7 +305,7 @@ __device__ __forceinline__ void wide_worker(const DecodeParams& p, char (*lds_pa
         // read here, where waiting for the scalar load costs nothing.
         if (lvalid) {
           lvalid = next_page(meta, p.seqlens, lb, lpage, lend, lp0);
-          if (lvalid) next_pid = ld_uniform(p.block_table + (size_t)lb * p.max_pages + page_in_order(lpage, lp0, lend, rb, nrb));
+          if (lvalid) next_pid = page_id(p, lb, page_in_order(lpage, lp0, lend, rb, nrb));
         }
 
         // ---- softmax weights (base 2) against the row references ----
@@ -353,8 +353,8 @@ __device__ __forceinline__ void wide_worker(const DecodeParams& p, char (*lds_pa
               for (int h = 0; h < 2; ++h) {
                 const float w0 = __builtin_amdgcn_exp2f(__builtin_fmaf(x[2 * kk + i][2 * h], p.scale_log2, -mu));
                 const float w1 = __builtin_amdgcn_exp2f(__builtin_fmaf(x[2 * kk + i][2 * h + 1], p.scale_log2, -mu));
-                l_run[j] += w0 + w1;
                 pk[i][h] = pack_bf16x2(w0, w1);
+                l_run[j] += sum_bf16x2(pk[i][h]);
               }
             // Slot 8*grp4 + 4*i + e of k-step kk holds key 32kk + 16i + 4*grp4 + e.
             *(__attribute__((address_space(3))) u32x4*)(pr_off[kk] + pw_base + (uint32_t)(j * 16 * kWidePRowBytes)) =
@@ -424,11 +424,11 @@ __device__ __forceinline__ void wide_worker(const DecodeParams& p, char (*lds_pa
       lp0 = seg_page0;
       cpage = seg_page0;
       {
-        const int page_id = ld_uniform(p.block_table + (size_t)lb * p.max_pages + page_in_order(lpage, lp0, lend, rb, nrb));
+        const int first_pid = page_id(p, lb, page_in_order(lpage, lp0, lend, rb, nrb));
         lvalid = next_page(meta, p.seqlens, lb, lpage, lend, lp0);
-        stage_page<kWideDmaPerWave>(kv_head + (size_t)page_id * page_stride_bytes, page_span, lane_src_off,
-                                    row_stride_bytes, lds_base + (it & 1) * kPageBytes, wave);
-        if (lvalid) next_pid = ld_uniform(p.block_table + (size_t)lb * p.max_pages + page_in_order(lpage, lp0, lend, rb, nrb));
+        stage_page<kWideDmaPerWave>(page_rsrc(kv_head, first_pid, p.num_pages, page_stride_bytes, page_span),
+                                    lane_src_off, row_stride_bytes, lds_base + (it & 1) * kPageBytes, wave);
+        if (lvalid) next_pid = page_id(p, lb, page_in_order(lpage, lp0, lend, rb, nrb));
       }
     }
 

@@ -51,6 +51,7 @@ struct DecodeParams {
   int rows;                     // R = s_q * h_q / h_kv
   int group;                    // G = h_q / h_kv
   int max_pages;
+  int num_pages;                // pages in the cache (page ids outside [0, num_pages) read as zeros)
   int num_workers;
   int row_blocks;               // ceil(R / rows_per_block(R))
   int causal;
@@ -75,11 +76,21 @@ struct SchedParams {
   int fixed_overhead;
 };
 
+constexpr int kCheckThreads = 1024;
+
+struct CheckParams {
+  const int32_t* block_table;   // [B][max_pages]
+  const int32_t* seqlens;       // [B]
+  int32_t* result;              // [4]
+  int batch, max_pages, num_pages;
+};
+
 template <bool kSingleHead>
 __global__ void mla_decode_kernel(DecodeParams p);
 template <bool kSingleHead>
 __global__ void mla_decode_wide_kernel(DecodeParams p);
 __global__ void mla_combine_kernel(CombineParams p);
 __global__ void mla_sched_kernel(SchedParams p);
+__global__ void mla_check_kernel(CheckParams p);
 
 }  // namespace mla

@@ -45,7 +45,9 @@ __device__ long long block_exclusive_scan(long long v, long long* tmp, long long
   return incl - v;
 }
 
-__device__ inline int pages_of(int seqlen) { return (seqlen + kPage - 1) / kPage; }
+// Pages of a sequence of `seqlen` tokens (0 for seqlen <= 0; no overflow
+// near INT_MAX).
+__device__ inline int pages_of(int seqlen) { return seqlen > 0 ? (seqlen - 1) / kPage + 1 : 0; }
 
 }  // namespace
 

@@ -1,9 +1,11 @@
 """Shared pieces of the GPU tests: run the HIP path through the C ABI on
 seeded inputs, and compare with the CPU oracle.
 
-Tolerances for bf16 inputs drawn from N(0, 1): max|dO| <= 1e-2,
-mean|dO| <= 1e-3, max|dLSE| <= 1e-3 (O is rounded once to bf16 at the end;
-the kernel computes in fp32 with bf16 softmax weights)."""
+Tolerances for bf16 inputs drawn from N(0, 1): max|dO| <= 1e-2 per element
+(raised to half a bf16 ulp plus the kernel's 2e-3 only where |O| >= 4, where
+the output grid itself is coarser), mean|dO| <= 1e-3 over the raw
+differences, max|dLSE| <= 1e-3.  O is rounded once to bf16 at the end; the
+kernel computes in fp32 with bf16 softmax weights."""
 from __future__ import annotations
 
 import numpy as np
@@ -46,25 +48,49 @@ def bf16_ulp(x):
     return np.exp2(np.floor(np.log2(np.maximum(np.abs(x), 2.0 ** -126))) - 7)
 
 
-def compare(o, lse, O, LSE, batch_subset=None, scale=1.0, ulp_aware=False, label=""):
+# Error of the kernel's output before its one rounding to bf16 (fp32
+# accumulation, bf16 softmax weights whose sum is the row's normaliser).
+KERNEL_EPS = 2e-3
+
+
+def o_bound(O, eps=KERNEL_EPS):
+    """Per-element bar on |o - O|: the benchmark spec's 1e-2, raised only where the
+    bf16 output grid itself is coarser than that.  A value within eps of O
+    rounds to nearest within half an ulp at |O| + eps, so no correct kernel
+    can do better than 0.5 * ulp(|O| + eps) + eps; that exceeds 1e-2 only
+    for |O| >= 4."""
+    return np.maximum(MAX_ABS_O, 0.5 * bf16_ulp(np.abs(O) + eps) + eps)
+
+
+def oracle_floor(O):
+    """max |bf16(O) - O|: the error of the exact result rounded once to bf16
+    (what a perfect kernel returns)."""
+    rounded = torch.from_numpy(np.ascontiguousarray(O)).to(torch.bfloat16).double().numpy()
+    return float(np.abs(rounded - O).max()) if O.size else 0.0
+
+
+def compare(o, lse, O, LSE, batch_subset=None, scale=1.0, label=""):
     """Assert the GPU result (o, lse) matches the oracle (O, LSE) on the
-    sequences in batch_subset (all when None).  `scale` widens the O bars for
-    inputs whose values are larger than N(0, 1).  With `ulp_aware`, an output
-    element may also differ by one bf16 ulp of its exact value plus 2e-3 (the
-    kernel's error before the final rounding, which may round to the far
-    neighbour): where |O| approaches 4 (rows that average one to three cached
-    values) the final bf16 rounding alone exceeds 1e-2."""
+    sequences in batch_subset (all when None): every element within
+    o_bound(O) (times `scale`, which widens the O bars for inputs whose values
+    are larger than N(0, 1)), the mean of the raw |o - O| within 1e-3, and
+    max |lse - LSE| within 1e-3.  Returns the statistics, with the oracle's
+    own bf16 floor beside them."""
     idx = slice(None) if batch_subset is None else np.asarray(batch_subset)
     o, O, lse, LSE = o[idx], O[idx], lse[idx], LSE[idx]
     assert np.isfinite(o).all(), f"{label}: non-finite output"
     d = np.abs(o - O)
-    if ulp_aware:
-        d = np.where(d <= bf16_ulp(O) + 2e-3, 0.0, d)
+    bound = o_bound(O) * scale
     neg = np.isneginf(LSE)
     assert (np.isneginf(lse) == neg).all(), f"{label}: -inf LSE pattern differs"
     dl = np.abs(lse[~neg] - LSE[~neg]) if (~neg).any() else np.zeros(1)
-    stats = dict(max_o=float(d.max()), mean_o=float(d.mean()), max_lse=float(dl.max()))
-    assert stats["max_o"] <= MAX_ABS_O * scale, f"{label}: {stats}"
+    worst = np.unravel_index(int(np.argmax(d - bound)), d.shape) if d.size else None
+    stats = dict(max_o=float(d.max()) if d.size else 0.0, mean_o=float(d.mean()) if d.size else 0.0,
+                 max_lse=float(dl.max()), oracle_floor=oracle_floor(O),
+                 worst_excess=float((d - bound).max()) if d.size else 0.0)
+    print(f"[parity] {label}: {stats}", flush=True)
+    assert (d <= bound).all(), f"{label}: |dO| {d[worst]:.4g} > bar {bound[worst]:.4g} at {worst} " \
+                               f"(O = {O[worst]:.6g}, o = {o[worst]:.6g}); {stats}"
     assert stats["mean_o"] <= MEAN_ABS_O * scale, f"{label}: {stats}"
     assert stats["max_lse"] <= MAX_ABS_LSE, f"{label}: {stats}"
     return stats

@@ -31,7 +31,7 @@ def test_header_declares_the_boundary():
     assert {"mla_get_metadata", "mla_decode_paged", "mla_num_workers", "mla_workspace_bytes",
             "mla_status_string", "mla_decode_splitkv", "mla_decode_splitkv_timed", "mla_combine_splits",
             "mla_sched_fixed_overhead", "mla_kvcache_append", "mla_absorb_q",
-            "mla_absorb_o"} <= names
+            "mla_absorb_o", "mla_check_inputs", "mla_set_debug_checks"} <= names
 
 
 def test_library_exports_every_declared_symbol():
@@ -49,9 +49,10 @@ def test_single_hip_runtime_in_process():
 
 def test_status_strings():
     lib = _lib()
-    for code in (0, -1, -2, -3, -4, -5):
-        assert lib.mla_status_string(code)
+    for code in (0, -1, -2, -3, -4, -5, -6):
+        assert lib.mla_status_string(code) != b"unknown status"
     assert b"WORKSPACE" in lib.mla_status_string(-3)
+    assert b"BAD_INPUT" in lib.mla_status_string(-6)
 
 
 def test_workspace_bytes():
@@ -146,3 +147,50 @@ def test_absorb_rejects_invalid_arguments():
     assert lib.mla_absorb_o(FAKE, None, FAKE, 4, 128, None) == -1
     assert lib.mla_absorb_o(FAKE, FAKE, FAKE + 2, 4, 128, None) == -2
     assert lib.mla_absorb_o(FAKE, FAKE, FAKE, 4, 0, None) == -1
+
+
+def test_check_inputs_rejects_invalid_arguments():
+    lib = _lib()
+    ok = dict(bt=FAKE, max_pages=4, num_pages=8, L=FAKE, batch=2, result=FAKE, stream=None)
+    for kw, status in [(dict(bt=None), -1), (dict(L=None), -1), (dict(result=None), -1), (dict(batch=0), -1),
+                       (dict(max_pages=0), -1), (dict(num_pages=0), -1), (dict(bt=FAKE + 2), -2),
+                       (dict(L=FAKE + 1), -2), (dict(result=FAKE + 2), -2)]:
+        args = dict(ok, **kw)
+        assert lib.mla_check_inputs(*args.values()) == status, kw
+
+
+def _cpu_buffers(B, s_q, h_q, W, o_shape=None, lse_shape=None, ws_bytes=None):
+    from paged_mla_decode_03_amd import binding
+    buf = binding.DecodeBuffers.__new__(binding.DecodeBuffers)
+    buf.o = torch.empty(o_shape or (B, s_q, h_q, 512), dtype=torch.bfloat16)
+    buf.lse = torch.empty(lse_shape or (B, h_q, s_q), dtype=torch.float32)
+    need = binding.workspace_bytes(B, s_q, h_q, 1, 512, W)
+    buf.workspace = torch.empty(need if ws_bytes is None else ws_bytes, dtype=torch.uint8)
+    return buf
+
+
+def test_decode_buffers_must_match_the_call():
+    """The library writes o and lse for every (b, i, h) of a call, so
+    caller-supplied buffers of another shape are refused before any launch."""
+    from paged_mla_decode_03_amd import binding
+    _lib()
+    cpu = torch.device("cpu")
+    binding._check_buffers(_cpu_buffers(4, 2, 16, 8), 4, 2, 16, 1, 512, 8, cpu)   # matching: accepted
+    for kw in (dict(o_shape=(3, 2, 16, 512)), dict(o_shape=(4, 1, 16, 512)), dict(o_shape=(4, 2, 8, 512)),
+               dict(lse_shape=(4, 2, 16)), dict(lse_shape=(4, 16, 1)), dict(ws_bytes=256)):
+        with pytest.raises(ValueError):
+            binding._check_buffers(_cpu_buffers(4, 2, 16, 8, **kw), 4, 2, 16, 1, 512, 8, cpu)
+
+
+def test_absorb_outputs_must_match_the_call():
+    from paged_mla_decode_03_amd import absorb_o, absorb_q
+    _lib()
+    qn = torch.zeros((3, 4, 128), dtype=torch.bfloat16)
+    qr = torch.zeros((3, 4, 64), dtype=torch.bfloat16)
+    w = torch.zeros((4, 512, 128), dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        absorb_q(qn, qr, w, out=torch.zeros((2, 4, 576), dtype=torch.bfloat16))
+    o = torch.zeros((3, 4, 512), dtype=torch.bfloat16)
+    wv = torch.zeros((4, 128, 512), dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        absorb_o(o, wv, out=torch.zeros((3, 4, 64), dtype=torch.bfloat16))
