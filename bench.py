@@ -1,19 +1,25 @@
-"""Benchmark of one paged MLA decode step on one MI355X.
+"""Benchmark of the paged MLA decode hot path on one MI355X.
 
-A step is the whole hot path over one batch: the split-KV decode kernel and
-the log-sum-exp combine (the scheduler metadata is computed once per batch of
-sequence lengths and timed separately).  Inputs are seeded synthetic bf16
-tensors resident in HBM before timing starts.  Successive steps alternate
-between independent KV pools whose total exceeds the 256 MB Infinity Cache,
-so every step streams its cache from HBM.
+A step is the whole hot path over one batch of sequences: the split-KV
+decode kernel and the log-sum-exp combine (the scheduler metadata is
+computed once per batch of sequence lengths; a "full step" that recomputes
+it is timed too).  Inputs are seeded synthetic bf16 tensors resident in HBM
+before timing starts.  Successive steps alternate between independent KV
+pools whose total exceeds the 256 MB Infinity Cache, so every step streams
+its cache from HBM.
 
-Prints one JSON line.  `value` is achieved algorithmic bandwidth (GB/s) of the
-whole step; `roofline` rates the dominant kernel (the decode kernel) against
-MI355X's 8 TB/s HBM or 2.5 PFLOP/s dense bf16 MFMA peak, with its duration
-measured by HIP events that the kernel's dispatch records at its start and
-end (mla_decode_splitkv_timed).
+The headline is the largest single-GPU workload, causal_sq2 (B=132, s_q=2
+causal, h_q=128, L=8192), which the bf16 matrix cores bound: `value` is its
+whole-step throughput in TFLOP/s, and `roofline` rates its decode kernel
+against the 2.5 PFLOP/s dense bf16 MFMA peak, the kernel's duration taken
+from HIP events that its own dispatches record (mla_decode_splitkv_timed)
+in the timed steps.  `per_config` holds the same measurements for all five
+workloads, each with both roofline fractions (HBM 8 TB/s and MFMA).
 
-    python bench.py [--steps K] [--warmup W] [--workload mem_bound] [--no-cpu-baseline]
+Prints one JSON line.
+
+    python bench.py [--steps K] [--warmup W] [--workload causal_sq2] [--configs all|none]
+                    [--no-cpu-baseline]
 """
 from __future__ import annotations
 
@@ -32,6 +38,9 @@ HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 MALL_BYTES = 256 << 20
 BOUND = {"mem_bound": "hbm", "var_len": "hbm", "skewed": "hbm", "causal_sq2": "mfma", "tiny": "hbm"}
+# Workloads kept off the GPU (an input that faulted an earlier decode kernel;
+# see the design notes' fault history) until the cause is shown on the CPU.
+OFF_GPU = {"tiny"}
 
 
 def parse():
@@ -44,11 +53,14 @@ def parse():
     # kernels' own durations do not change), so the default warmup is 300
     # steps (about 30 ms).
     ap.add_argument("--warmup", type=int, default=300)
-    ap.add_argument("--workload", default="mem_bound")
+    ap.add_argument("--workload", default="causal_sq2",
+                    help="the headline workload (the largest one by default)")
+    ap.add_argument("--configs", default="all",
+                    help="'all': also measure the other workloads into per_config; 'none': the headline only")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=15.0)
-    ap.add_argument("--op", choices=["decode", "append", "absorb"], default="decode",
+    ap.add_argument("--op", choices=["decode", "append", "absorb", "outproj"], default="decode",
                     help="append: time the cache append of the workload's new tokens instead; absorb: the "
                          "per-head projections before and after the decode (each prints its own JSON line)")
     ap.add_argument("--append-tokens", type=int, default=0,
@@ -64,6 +76,7 @@ KERNEL_SOURCES = {
     "mla_decode_wide_kernel": ("mla_decode_wide.hip", "mla_decode_common.h", "mla_kernels.h"),
     "mla_append_kernel": ("mla_append.hip", "mla_append.h", "mla_kernels.h"),
     "mla_absorb_kernel": ("mla_absorb.hip", "mla_absorb.h"),
+    "mla_outproj_kernel": ("mla_outproj.hip", "mla_outproj.h"),
 }
 
 
@@ -269,6 +282,263 @@ def bench_absorb(args):
     print(json.dumps(out), flush=True)
 
 
+def bench_outproj(args):
+    """The output projection over all heads, u = W^O [o_1; ...; o_h], for
+    the workload's B * s_q tokens, h_q = 128 heads of d_h = 128 and
+    d_model = h_q * d_h = 16384 (the multi-head convention that each head is
+    d_model / n_h wide), random bf16 weights; 20 launches captured into a
+    HIP graph and replayed.  Algorithmic bytes: W^O and the per-head outputs
+    read once, u written once; flops 2 * tokens * d_model * h_q * d_h."""
+    import torch
+
+    sys.path.insert(0, ROOT)
+    from paged_mla_decode_03_amd import outproj
+    from paged_mla_decode_03_amd.binding import library
+    from workloads import WORKLOADS, bf16_normal
+
+    dev = torch.device("cuda", 0)
+    w = WORKLOADS[args.workload]
+    T, H = w.batch * w.s_q, w.h_q
+    K, N = H * 128, H * 128
+    rng = np.random.Generator(np.random.PCG64(args.seed))
+    o = bf16_normal(rng, (T, H, 128)).to(dev)
+    wo = bf16_normal(rng, (N, K)).to(dev)
+    out = torch.empty((T, N), dtype=torch.bfloat16, device=dev)
+    need = int(library().mla_outproj_workspace_bytes(T, K, N))
+    ws = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    nbytes = 2 * (N * K + T * K + T * N)
+    flops = 2 * T * N * K
+    fn = lambda: outproj(o, wo, out, ws)
+    for _ in range(args.warmup):
+        fn()
+    torch.cuda.synchronize()
+    if args.copy_mb > 0:
+        src = torch.empty(args.copy_mb << 20, dtype=torch.uint8, device=dev)
+        torch.empty_like(src).copy_(src)
+        torch.cuda.synchronize()
+        del src
+    graph, n_graph = torch.cuda.CUDAGraph(), 20
+    with torch.cuda.graph(graph):
+        for _ in range(n_graph):
+            fn()
+    reps = max(1, args.steps // n_graph)
+    graph.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / (reps * n_graph)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    print(f"[bench] outproj: {ms * 1e3:.2f} us per call ({gbs:.0f} GB/s, {flops / ms / 1e9:.0f} TFLOP/s), "
+          f"split-K workspace {need} B", file=sys.stderr, flush=True)
+    out_line = {"metric": "MLA output projection over all heads: achieved HBM GB/s", "value": round(gbs, 2),
+                "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+                "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+                "dtype": "bf16", "data": "synthetic",
+                "config": {"workload": f"{args.workload} outproj", "tokens": T, "h_q": H, "d_h": 128,
+                           "d_model": N, "seed": args.seed},
+                "tflops": round(flops / (ms * 1e-3) / 1e12, 2),
+                "roofline": {"kernel": "mla_outproj_kernel", "bound": "hbm", "achieved": round(gbs, 2),
+                             "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                             "traffic": measured_traffic(w, "mla_outproj_kernel", f"{args.workload}_outproj"),
+                             "per_launch": {"bytes": nbytes, "flops": flops}}}
+    print(json.dumps(out_line), flush=True)
+
+
+def _pct(a, q):
+    return float(np.percentile(np.asarray(a), q))
+
+
+def gpu_clock_mhz():
+    """Current shader clock from sysfs (the entry marked '*' of
+    pp_dpm_sclk), or None where it cannot be read."""
+    import glob
+    import re
+    for path in sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk")):
+        try:
+            for line in open(path).read().splitlines():
+                if line.strip().endswith("*"):
+                    m = re.search(r"(\d+)\s*Mhz", line, re.I)
+                    if m:
+                        return int(m.group(1))
+        except OSError:
+            continue
+    return None
+
+
+def achievable_bandwidth(dev, mib: int = 1024) -> dict:
+    """Measured HBM rates beside the 8 TB/s spec: a plain device copy of
+    `mib` MiB (read + write) and a read-only reduction over the same buffer,
+    each the median of 10 event-timed runs after warmup."""
+    import torch
+    n = mib << 20
+    src = torch.ones(n // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    out = {}
+    for name, fn, nbytes in (("copy_gbs", lambda: dst.copy_(src), 2 * n),
+                             ("read_gbs", lambda: torch.sum(src), n)):
+        for _ in range(3):
+            fn()
+        ts = []
+        for _ in range(10):
+            a, z = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            z.record()
+            z.synchronize()
+            ts.append(a.elapsed_time(z))
+        out[name] = round(nbytes / (float(np.median(ts)) * 1e-3) / 1e9, 1)
+    del src, dst
+    torch.cuda.empty_cache()
+    return out
+
+
+def measure_workload(name: str, args, dev, want_cpu: bool) -> dict:
+    """All measurements of one workload (see the module docstring)."""
+    import torch
+
+    from paged_mla_decode_03_amd import (DecodeBuffers, get_mla_metadata, mla_combine_splits, mla_decode_paged,
+                                         mla_decode_splitkv_timed)
+    from workloads import WORKLOADS, algorithmic_counts, make_inputs
+
+    w = WORKLOADS[name]
+    print(f"[bench] generating {name} (seed {args.seed})", file=sys.stderr, flush=True)
+    inp = make_inputs(w, args.seed)
+    L = inp.cache_seqlens.numpy()
+    counts = algorithmic_counts(w, L, inp.block_table.shape[1])
+    q = inp.q.to(dev)
+    bt = inp.block_table.to(dev)
+    seqlens = inp.cache_seqlens.to(dev)
+    kv_bytes = inp.kvcache.numel() * 2
+    n_pools = max(2, -(-2 * MALL_BYTES // kv_bytes) + 1)
+    pools = [inp.kvcache.to(dev)]
+    for _ in range(1, n_pools):
+        pools.append(pools[0].clone())
+    rows = w.s_q * w.h_q // w.h_kv
+
+    # Scheduler metadata (once per batch of lengths), timed on its own.
+    torch.cuda.synchronize()
+    meta, ns = get_mla_metadata(seqlens, rows, w.h_kv)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(20):
+        meta, ns = get_mla_metadata(seqlens, rows, w.h_kv)
+    e1.record()
+    torch.cuda.synchronize()
+    metadata_us = e0.elapsed_time(e1) / 20 * 1e3
+    W = meta.shape[0]
+    buf = DecodeBuffers(q, pools[0], 512, W)
+    splits = np.diff(ns.cpu().numpy())
+    # Bytes per kernel: the combine writes o and lse of split sequences.
+    split_rows = int((splits > 1).sum()) * w.s_q * w.h_q
+    combine_bytes = split_rows * (512 * 2 + 4)
+    decode_bytes = counts["total_bytes"] - combine_bytes
+
+    # One step: the decode kernel (its dispatch records two events, so the
+    # kernel's own duration comes from the timed steps themselves) and the
+    # combine, on torch's current stream.
+    def step(i, evs=None):
+        kv = pools[i % n_pools]
+        if evs is None:
+            mla_decode_paged(q, kv, bt, seqlens, 512, meta, ns, causal=w.causal, buffers=buf)
+        else:
+            mla_decode_splitkv_timed(q, kv, bt, seqlens, 512, meta, ns, evs[0], evs[1], causal=w.causal,
+                                     buffers=buf)
+            mla_combine_splits(ns, w.s_q, w.h_q, w.h_kv, 512, W, buf)
+
+    K = args.steps
+    kev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    print(f"[bench] {name}: warmup {args.warmup}", file=sys.stderr, flush=True)
+    for i in range(args.warmup):
+        step(i, kev[i % K])
+    torch.cuda.synchronize()
+    if args.copy_mb > 0:
+        src = torch.empty(args.copy_mb << 20, dtype=torch.uint8, device=dev)
+        torch.empty_like(src).copy_(src)
+        torch.cuda.synchronize()
+        del src
+
+    # The timed steps, launches only, between a synchronize and a pair of
+    # events on each side.
+    g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    g0.record()
+    for i in range(K):
+        step(i, kev[i])
+    g1.record()
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3
+    ms_per_step = wall_ms / K
+    event_ms_per_step = g0.elapsed_time(g1) / K
+    kernel_ms = np.array([a.elapsed_time(z) for a, z in kev])
+
+    # Step-time distribution: each step bracketed by events on the stream
+    # (plain mla_decode_paged); then the full step with the metadata.
+    def timed_loop(fn):
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+        torch.cuda.synchronize()
+        for i in range(K):
+            evs[i][0].record()
+            fn(i)
+            evs[i][1].record()
+        torch.cuda.synchronize()
+        return np.array([a.elapsed_time(z) for a, z in evs]) * 1e3
+
+    step_us = timed_loop(lambda i: step(i))
+
+    def full(i):
+        m, n = get_mla_metadata(seqlens, rows, w.h_kv)
+        mla_decode_paged(q, pools[i % n_pools], bt, seqlens, 512, m, n, causal=w.causal, buffers=buf)
+
+    full_us = timed_loop(full)
+    clock = gpu_clock_mhz()
+
+    kernel_mean_s = float(kernel_ms.mean()) * 1e-3
+    res = {
+        "config": {"workload": name, "batch": w.batch, "s_q": w.s_q, "h_q": w.h_q, "h_kv": w.h_kv, "d_qk": 576,
+                   "dv": 512, "page_size": 64, "causal": w.causal, "seqlen_total": int(L.sum()),
+                   "seqlen_max": int(L.max()), "seed": args.seed, "kv_pools": n_pools, "num_workers": W,
+                   "max_splits": int(splits.max())},
+        "us_per_step": round(ms_per_step * 1e3, 2),
+        "step_event_us": round(event_ms_per_step * 1e3, 2),
+        "step_us": {"median": round(float(np.median(step_us)), 2), "p10": round(_pct(step_us, 10), 2),
+                    "p90": round(_pct(step_us, 90), 2)},
+        "full_step_with_metadata_us": {"median": round(float(np.median(full_us)), 2),
+                                       "p10": round(_pct(full_us, 10), 2), "p90": round(_pct(full_us, 90), 2)},
+        "metadata_us": round(metadata_us, 2),
+        "decode_kernel_us": {"mean": round(kernel_mean_s * 1e6, 2), "median": round(float(np.median(kernel_ms)) * 1e3, 2),
+                             "p10": round(_pct(kernel_ms, 10) * 1e3, 2), "p90": round(_pct(kernel_ms, 90) * 1e3, 2)},
+        "step": {"gbs": round(counts["total_bytes"] / (ms_per_step * 1e-3) / 1e9, 2),
+                 "tflops": round(counts["flops"] / (ms_per_step * 1e-3) / 1e12, 2),
+                 "hbm_frac": round(counts["total_bytes"] / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                 "mfma_frac": round(counts["flops"] / (ms_per_step * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)},
+        "decode_kernel": {"kernel": decode_kernel_name(w), "bytes": decode_bytes, "flops": counts["flops"],
+                          "gbs": round(decode_bytes / kernel_mean_s / 1e9, 2),
+                          "tflops": round(counts["flops"] / kernel_mean_s / 1e12, 2),
+                          "hbm_frac": round(decode_bytes / kernel_mean_s / 1e9 / HBM_PEAK_GBS, 4),
+                          "mfma_frac": round(counts["flops"] / kernel_mean_s / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+                          "traffic": measured_traffic(w)},
+        "algorithmic_bytes": counts["total_bytes"],
+        "algorithmic_flops": counts["flops"],
+        "combine_bytes": combine_bytes,
+        "gpu_clock_mhz_after": clock,
+    }
+    print(f"[bench] {name}: {res['us_per_step']} us/step (wall), step median {res['step_us']['median']} us, "
+          f"decode kernel mean {res['decode_kernel_us']['mean']} us ({res['decode_kernel']['hbm_frac']:.3f} HBM, "
+          f"{res['decode_kernel']['mfma_frac']:.3f} MFMA), full step {res['full_step_with_metadata_us']['median']} us",
+          file=sys.stderr, flush=True)
+    if want_cpu:
+        print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
+        res["cpu_baseline"] = cpu_baseline(inp, args.cpu_budget_s)
+    del pools, q, bt, seqlens, buf, inp
+    torch.cuda.empty_cache()
+    return res
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -282,186 +552,64 @@ def main():
     if args.op == "absorb":
         bench_absorb(args)
         return
+    if args.op == "outproj":
+        bench_outproj(args)
+        return
 
     import torch
 
     sys.path.insert(0, ROOT)
-    from paged_mla_decode_03_amd import (DecodeBuffers, get_mla_metadata, mla_combine_splits, mla_decode_paged,
-                                         mla_decode_splitkv, mla_decode_splitkv_timed)
-    from workloads import WORKLOADS, algorithmic_counts, make_inputs
+    from workloads import WORKLOADS
 
+    if args.workload in OFF_GPU:
+        print(json.dumps({"error": f"workload {args.workload} is kept off the GPU (see the design notes)"}))
+        sys.exit(2)
     dev = torch.device("cuda", 0)
-    w = WORKLOADS[args.workload]
-    print(f"[bench] generating {args.workload} (seed {args.seed})", file=sys.stderr, flush=True)
-    inp = make_inputs(w, args.seed)
-    L = inp.cache_seqlens.numpy()
-    counts = algorithmic_counts(w, L, inp.block_table.shape[1])
-
-    q = inp.q.to(dev)
-    bt = inp.block_table.to(dev)
-    seqlens = inp.cache_seqlens.to(dev)
-    kv_bytes = inp.kvcache.numel() * 2
-    n_pools = max(2, -(-2 * MALL_BYTES // kv_bytes) + 1)
-    pools = [inp.kvcache.to(dev)]
-    for i in range(1, n_pools):
-        pools.append(pools[0].clone())
-    rows = w.s_q * w.h_q // w.h_kv
-
-    # Scheduler metadata (once per batch of lengths), timed on its own.
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    meta, ns = get_mla_metadata(seqlens, rows, w.h_kv)
-    e0.record()
-    for _ in range(10):
-        meta, ns = get_mla_metadata(seqlens, rows, w.h_kv)
-    e1.record()
-    torch.cuda.synchronize()
-    metadata_us = e0.elapsed_time(e1) / 10 * 1e3
-    W = meta.shape[0]
-    buf = DecodeBuffers(q, pools[0], 512, W)
-
-    # One step: mla_decode_paged, one call that launches the decode and the
-    # combine kernel on torch's current stream (which the binding launches on).
-    def step(i):
-        mla_decode_paged(q, pools[i % n_pools], bt, seqlens, 512, meta, ns, causal=w.causal, buffers=buf)
-
-    # The same two launches through their own entry points, each bracketed by
-    # events (used only outside the timed loop: an event between launches
-    # widens the gap).
-    def split_step(i, evs):
-        kv = pools[i % n_pools]
-        evs[0].record()
-        mla_decode_splitkv(q, kv, bt, seqlens, 512, meta, ns, causal=w.causal, buffers=buf)
-        evs[1].record()
-        mla_combine_splits(ns, w.s_q, w.h_q, w.h_kv, 512, W, buf)
-        evs[2].record()
-
-    print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-    if args.copy_mb > 0:
-        src = torch.empty(args.copy_mb << 20, dtype=torch.uint8, device=dev)
-        dst = torch.empty_like(src)
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
-
-    # The timed steps: launches only, between a synchronize and a pair of
-    # events on each side.
-    g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t_start = time.perf_counter()
-    g0.record()
-    for i in range(args.steps):
-        step(i)
-    g1.record()
-    launch_ms = (time.perf_counter() - t_start) * 1e3      # host time to issue the steps
-    torch.cuda.synchronize()
-    wall_ms = (time.perf_counter() - t_start) * 1e3
-    ms_per_step = wall_ms / args.steps
-    event_ms_per_step = g0.elapsed_time(g1) / args.steps
-
-    # Per-launch split of a step, from separate steps with events between the
-    # launches (outside the timed loop).
-    n_split = min(args.steps, 10)
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n_split)]
-    for i in range(n_split):
-        split_step(i, evs[i])
-    torch.cuda.synchronize()
-    decode_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
-    combine_ms = np.array([e[1].elapsed_time(e[2]) for e in evs])
-
-    # The decode kernel alone, launched back to back between two events on
-    # its stream: the average is the kernel's own duration plus one dispatch
-    # gap, the closest event-based match to a profiler's per-kernel time.
-    n_dec = max(args.steps, 10)
-    d0, d1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    d0.record()
-    for i in range(n_dec):
-        mla_decode_splitkv(q, pools[i % n_pools], bt, seqlens, 512, meta, ns, causal=w.causal, buffers=buf)
-    d1.record()
-    torch.cuda.synchronize()
-    decode_b2b_ms = d0.elapsed_time(d1) / n_dec
-
-    # The decode kernel alone, each launch bracketed by its own pair of
-    # events recorded on the stream with the stream idle before it.
-    iso_ms = []
-    for i in range(n_dec):
-        a, z = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        a.record()
-        mla_decode_splitkv(q, pools[i % n_pools], bt, seqlens, 512, meta, ns, causal=w.causal, buffers=buf)
-        z.record()
-        z.synchronize()
-        iso_ms.append(a.elapsed_time(z))
-    decode_iso_ms = float(np.mean(iso_ms))
-
-    # The decode kernel's own duration: HIP events that the dispatch records
-    # at the kernel's start and end, back-to-back launches.  This is the
-    # duration the roofline uses.
-    kev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_dec)]
-    torch.cuda.synchronize()
-    for i in range(n_dec):
-        mla_decode_splitkv_timed(q, pools[i % n_pools], bt, seqlens, 512, meta, ns, kev[i][0], kev[i][1],
-                                 causal=w.causal, buffers=buf)
-    torch.cuda.synchronize()
-    kernel_ms = np.array([a.elapsed_time(z) for a, z in kev])
-    decode_kernel_ms = float(kernel_ms.mean())
-    print(f"[bench] {args.steps} steps: {ms_per_step * 1e3:.1f} us/step (wall), "
-          f"{event_ms_per_step * 1e3:.1f} us/step (events), host issue {launch_ms / args.steps * 1e3:.1f} us/step, decode kernel "
-          f"{decode_ms.mean() * 1e3:.1f} us in step, {decode_b2b_ms * 1e3:.1f} us back to back, "
-          f"{decode_iso_ms * 1e3:.1f} us launched alone, {decode_kernel_ms * 1e3:.1f} us kernel (dispatch events), "
-          f"combine {combine_ms.mean() * 1e3:.1f} us", file=sys.stderr, flush=True)
-
-    gbs = counts["total_bytes"] / (ms_per_step * 1e-3) / 1e9
-    tflops = counts["flops"] / (ms_per_step * 1e-3) / 1e12
-    dec_s = decode_kernel_ms * 1e-3
+    head = measure_workload(args.workload, args, dev, not args.no_cpu_baseline)
+    per_config = {args.workload: head}
+    if args.configs == "all":
+        for name in WORKLOADS:
+            if name != args.workload and name not in OFF_GPU:
+                per_config[name] = measure_workload(name, args, dev, False)
+    achievable = achievable_bandwidth(dev)
     bound = BOUND.get(args.workload, "hbm")
+    dk = head["decode_kernel"]
     if bound == "hbm":
-        achieved, peak, unit = counts["total_bytes"] / dec_s / 1e9, HBM_PEAK_GBS, "GB/s"
+        achieved, peak, unit = dk["gbs"], HBM_PEAK_GBS, "GB/s"
+        value, vunit = head["step"]["gbs"], "GB/s"
     else:
-        achieved, peak, unit = counts["flops"] / dec_s / 1e12, MFMA_BF16_PEAK_TFLOPS, "TFLOP/s"
-    traffic = measured_traffic(w)
+        achieved, peak, unit = dk["tflops"], MFMA_BF16_PEAK_TFLOPS, "TFLOP/s"
+        value, vunit = head["step"]["tflops"], "TFLOP/s"
     out = {
         "metric": METRIC,
-        "value": round(gbs, 2),
-        "unit": "GB/s",
+        "value": value,
+        "unit": vunit,
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 5),
+        "ms_per_step": round(head["us_per_step"] / 1e3, 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": args.workload, "batch": w.batch, "s_q": w.s_q, "h_q": w.h_q, "h_kv": w.h_kv,
-                   "d_qk": 576, "dv": 512, "page_size": 64, "causal": w.causal,
-                   "seqlen_total": int(L.sum()), "seqlen_max": int(L.max()), "seed": args.seed,
-                   "kv_pools": n_pools, "num_workers": W},
-        "tflops": round(tflops, 2),
-        "us_per_step": round(ms_per_step * 1e3, 2),
-        "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
-        "mfma_frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
-        "decode_kernel_us": round(decode_kernel_ms * 1e3, 2),
-        "decode_launched_alone_us": round(decode_iso_ms * 1e3, 2),
-        "decode_back_to_back_us": round(decode_b2b_ms * 1e3, 2),
-        "decode_in_step_us": round(decode_ms.mean() * 1e3, 2),
-        "combine_kernel_us": round(combine_ms.mean() * 1e3, 2),
-        "step_event_us": round(event_ms_per_step * 1e3, 2),
-        "metadata_us": round(metadata_us, 2),
-        "algorithmic_bytes": counts["total_bytes"],
-        "algorithmic_flops": counts["flops"],
-        "roofline": {"kernel": decode_kernel_name(w), "bound": bound, "achieved": round(achieved, 2),
-                     "peak": peak, "unit": unit, "frac": round(achieved / peak, 4),
-                     "traffic": traffic,
-                     "per_launch": {"bytes": counts["total_bytes"], "flops": counts["flops"]}},
+        "config": head["config"],
+        "gbs": head["step"]["gbs"],
+        "tflops": head["step"]["tflops"],
+        "us_per_step": head["us_per_step"],
+        "hbm_frac": head["step"]["hbm_frac"],
+        "mfma_frac": head["step"]["mfma_frac"],
+        "roofline": {"kernel": dk["kernel"], "bound": bound, "achieved": achieved, "peak": peak, "unit": unit,
+                     "frac": round(achieved / peak, 4), "traffic": dk["traffic"],
+                     "duration": "mean of the kernel's dispatch-recorded durations over the timed steps",
+                     "kernel_us": head["decode_kernel_us"]["mean"],
+                     "per_launch": {"bytes": dk["bytes"], "flops": dk["flops"]},
+                     "hbm_frac": dk["hbm_frac"], "mfma_frac": dk["mfma_frac"]},
+        "achievable_hbm": achievable,
+        "per_config": {k: {kk: vv for kk, vv in v.items() if kk != "cpu_baseline"} for k, v in per_config.items()},
     }
-    if not args.no_cpu_baseline:
-        print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
-        out["cpu_baseline"] = cpu_baseline(inp, args.cpu_budget_s)
+    if "cpu_baseline" in head:
+        out["cpu_baseline"] = head["cpu_baseline"]
     print(json.dumps(out), flush=True)
 
 

@@ -255,6 +255,28 @@ int mla_absorb_q(const void* q_nope, const void* q_rope, const void* w_uk_t, voi
                  void* stream);
 int mla_absorb_o(const void* o_latent, const void* w_uv, void* out, int tokens, int h_q, void* stream);
 
+/* The output projection over all heads (deepseek.csdn.net FlashMLA article,
+ * section 2.2, second output equation): u_t = W^O [o_{t,1}; ...; o_{t,n_h}],
+ * the per-head outputs (d_h = 128 each, the result of mla_absorb_o)
+ * concatenated in head order and mapped by one matrix.  bf16 in and out,
+ * fp32 accumulation.
+ *   o_heads  [dev] bf16 [tokens][k]: row t = [o_{t,1}; ...; o_{t,n_h}],
+ *            k = n_h * 128 (mla_absorb_o's output [tokens][h_q][128] is this
+ *            layout)
+ *   w_o      [dev] bf16 [n][k]: W^O, row-major (output column n's weights
+ *            contiguous)
+ *   out      [dev] bf16 [tokens][n]
+ *   workspace [dev] fp32 scratch of mla_outproj_workspace_bytes(tokens, k, n)
+ *            bytes (0 when the call needs none; then it may be NULL): the
+ *            split-K partials, written before they are read.
+ * k must be a multiple of 128 and n of 128; pointers 16-byte aligned.  The
+ * result is deterministic (fixed summation order).  Errors:
+ * MLA_ERR_INVALID_ARG (null pointers, non-positive sizes),
+ * MLA_ERR_UNSUPPORTED (sizes or alignment), MLA_ERR_WORKSPACE. */
+size_t mla_outproj_workspace_bytes(int tokens, int k, int n);
+int mla_outproj(const void* o_heads, const void* w_o, void* out, int tokens, int k, int n, void* workspace,
+                size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -20,6 +20,8 @@ What it computes (deepseek.csdn.net, "FlashMLA ... 详解", section 2.2 "DeepSee
 * Appending new tokens to the paged cache (:func:`kvcache_append_ref`): the
   cache keeps every earlier token's latent row, and a new token's row goes to
   the page and slot its logical position maps to.
+* The output projection over all heads (:func:`out_proj_ref`), the second
+  output equation of section 2.2: u_t = W^O [o_{t,1}; ...; o_{t,n_h}].
 * The call on the dolphin-ai.jp FlashMLA page ("FlashMLA の使用方法", step 4):
   ``flash_mla_with_kvcache(q, kvcache, block_table, cache_seqlens, dv, ...,
   causal)`` returns the output and the log-sum-exp.
@@ -238,3 +240,17 @@ def absorb_o_ref(o_latent, w_uv):
     for h in range(H):
         out[:, h, :] = o[:, h, :] @ w[h].T
     return out
+
+
+def out_proj_ref(o_heads, w_o):
+    """The output projection over all heads (deepseek.csdn.net FlashMLA
+    article, section 2.2, second output equation): the per-head outputs
+    o_{t,i} are stacked in head order, [o_{t,1}; o_{t,2}; ...; o_{t,n_h}],
+    and mapped by one matrix, u_t = W^O [o_{t,1}; ...; o_{t,n_h}].
+
+    o_heads [T][h][d_h], w_o [d_model][h * d_h].  Returns [T][d_model] in
+    float64."""
+    o, w = as_f64(o_heads), as_f64(w_o)
+    T, H, D = o.shape
+    stacked = o.reshape(T, H * D)          # row t = o_{t,1} followed by o_{t,2}, ...
+    return stacked @ w.T

@@ -72,6 +72,10 @@ def _load():
     lib.mla_kvcache_append.argtypes = [vp, vp, vp, c_int, c_int, vp, c_int, c_int, c_int, c_int, vp, vp]
     lib.mla_absorb_q.argtypes = [vp, vp, vp, vp, c_int, c_int, vp]
     lib.mla_absorb_o.argtypes = [vp, vp, vp, c_int, c_int, vp]
+    lib.mla_outproj_workspace_bytes.restype = c_size_t
+    lib.mla_outproj_workspace_bytes.argtypes = [c_int, c_int, c_int]
+    lib.mla_outproj.restype = c_int
+    lib.mla_outproj.argtypes = [vp, vp, vp, c_int, c_int, c_int, vp, c_size_t, vp]
     lib.mla_check_inputs.restype = c_int
     lib.mla_check_inputs.argtypes = [vp, c_int, c_int, vp, c_int, vp, vp]
     lib.mla_set_debug_checks.restype = None
@@ -352,3 +356,36 @@ def set_debug_checks(enable: bool) -> None:
     """Turn the checker in front of every decode call on or off (overrides
     MLA_DEBUG_CHECKS for the process)."""
     _load().mla_set_debug_checks(int(bool(enable)))
+
+
+def outproj(o_heads: torch.Tensor, w_o: torch.Tensor, out: Optional[torch.Tensor] = None,
+            workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """u = W^O [o_1; ...; o_h] for every token: o_heads [..., h, 128] (or
+    [..., h * 128]) bf16, w_o [d_model, h * 128] bf16.  Returns [..., d_model]
+    bf16.  The split-K workspace is allocated here unless given."""
+    device = o_heads.device
+    _require(o_heads, "o_heads", torch.bfloat16, device)
+    _require(w_o, "w_o", torch.bfloat16, device)
+    n, k = w_o.shape
+    lead = o_heads.shape[:-2] if (o_heads.dim() >= 2 and o_heads.shape[-1] == 128
+                                  and o_heads.shape[-2] * 128 == k) else o_heads.shape[:-1]
+    tokens = o_heads.numel() // k
+    if o_heads.numel() != tokens * k or tokens == 0:
+        raise ValueError(f"o_heads {tuple(o_heads.shape)} does not hold rows of {k} = h * 128 values")
+    if out is None:
+        out = torch.empty(tuple(lead) + (n,), dtype=torch.bfloat16, device=device)
+    _require(out, "out", torch.bfloat16, device)
+    if out.numel() != tokens * n:
+        raise ValueError(f"out has shape {tuple(out.shape)}, expected {tokens} x {n}")
+    need = int(_load().mla_outproj_workspace_bytes(tokens, k, n))
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=device)
+    if workspace is not None:
+        _require(workspace, "workspace", torch.uint8, device)
+        if workspace.numel() < need:
+            raise ValueError(f"workspace holds {workspace.numel()} bytes, the call needs {need}")
+    _check("mla_outproj", _load().mla_outproj(
+        o_heads.data_ptr(), w_o.data_ptr(), out.data_ptr(), tokens, k, n,
+        workspace.data_ptr() if workspace is not None else None,
+        workspace.numel() if workspace is not None else 0, _stream_handle(device)))
+    return out

@@ -14,6 +14,7 @@
 #include "mla_kernels.h"
 #include "mla_append.h"
 #include "mla_absorb.h"
+#include "mla_outproj.h"
 
 namespace {
 
@@ -451,6 +452,88 @@ int mla_absorb_o(const void* o_latent, const void* w_uv, void* out, int tokens, 
   p.c_t = (long long)h_q * mla::kDh;
   p.c_h = mla::kDh;
   return launch_absorb(p, false, (hipStream_t)stream);
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// Output projection over all heads.
+// ---------------------------------------------------------------------------
+namespace {
+
+// K slices per column tile: the fewest (1, 2, 4, 8) that give the launch at
+// least one workgroup per compute unit, each wave keeping whole 32-wide k
+// steps.
+int outproj_splits(int T, int K, int N, int cus) {
+  const long long tiles = (long long)(N / mla::kOutProjTileN) * ((T + mla::kOutProjTileT - 1) / mla::kOutProjTileT);
+  int best = 1;
+  for (int s = 1; s <= mla::kOutProjMaxSplits; s *= 2) {
+    if (K % (128 * s) != 0) break;
+    best = s;
+    if (tiles * s >= cus) break;
+  }
+  return best;
+}
+
+int check_outproj(int T, int K, int N) {
+  if (T <= 0 || K <= 0 || N <= 0) return MLA_ERR_INVALID_ARG;
+  if (K % 128 != 0 || N % mla::kOutProjTileN != 0) return MLA_ERR_UNSUPPORTED;
+  if ((long long)T * K >= (1LL << 40) || (long long)N * K >= (1LL << 40) || (long long)T * N >= (1LL << 40))
+    return MLA_ERR_UNSUPPORTED;
+  return MLA_OK;
+}
+
+size_t outproj_workspace(int T, int K, int N, int cus) {
+  const int s = outproj_splits(T, K, N, cus);
+  return s > 1 ? (size_t)s * T * N * sizeof(float) : 0;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t mla_outproj_workspace_bytes(int tokens, int k, int n) {
+  if (check_outproj(tokens, k, n) != MLA_OK) return 0;
+  int cus = 0;
+  if (cu_count(-1, &cus) != MLA_OK) return 0;
+  return outproj_workspace(tokens, k, n, cus);
+}
+
+int mla_outproj(const void* o_heads, const void* w_o, void* out, int tokens, int k, int n, void* workspace,
+                size_t workspace_bytes_given, void* stream) {
+  if (!o_heads || !w_o || !out) return MLA_ERR_INVALID_ARG;
+  int st = check_outproj(tokens, k, n);
+  if (st != MLA_OK) return st;
+  if (!aligned(o_heads, 16) || !aligned(w_o, 16) || !aligned(out, 16) || !aligned(workspace, 16))
+    return MLA_ERR_UNSUPPORTED;
+  int cus = 0;
+  if ((st = cu_count(-1, &cus)) != MLA_OK) return st;
+  const size_t need = outproj_workspace(tokens, k, n, cus);
+  if (need > 0 && (!workspace || workspace_bytes_given < need)) return MLA_ERR_WORKSPACE;
+  mla::OutProjParams p;
+  p.a = (const uint16_t*)o_heads;
+  p.w = (const uint16_t*)w_o;
+  p.out = (uint16_t*)out;
+  p.partial = (float*)workspace;
+  p.T = tokens;
+  p.K = k;
+  p.N = n;
+  p.ntiles = n / mla::kOutProjTileN;
+  p.tchunks = (tokens + mla::kOutProjTileT - 1) / mla::kOutProjTileT;
+  p.splits = outproj_splits(tokens, k, n, cus);
+  const long long groups = (long long)p.ntiles * p.splits;
+  const long long blocks = (groups + mla::kNumXcdOutProj - 1) / mla::kNumXcdOutProj * mla::kNumXcdOutProj * p.tchunks;
+  if (blocks >= (1LL << 31)) return MLA_ERR_UNSUPPORTED;
+  hipLaunchKernelGGL(mla::mla_outproj_kernel, dim3((unsigned)blocks), dim3(mla::kOutProjThreads), 0,
+                     (hipStream_t)stream, p);
+  if (hipGetLastError() != hipSuccess) return MLA_ERR_HIP;
+  if (p.splits > 1) {
+    const long long groups4 = (long long)tokens * n / 4;
+    hipLaunchKernelGGL(mla::mla_outproj_reduce_kernel, dim3((unsigned)((groups4 + 255) / 256)), dim3(256), 0,
+                       (hipStream_t)stream, p);
+    if (hipGetLastError() != hipSuccess) return MLA_ERR_HIP;
+  }
+  return MLA_OK;
 }
 
 }  // extern "C"

@@ -224,7 +224,7 @@ __device__ __forceinline__ void decode_role(const DecodeParams& p, DecodeShared&
     const int n_vis_min = p.causal ? L - p.s_q + row_tok(0) + 1 : L;
     float m_ref = kNegInf;
     bool second_pass = false;
-    float m_seen, l_run;
+    float m_seen, l_run, l_bf;   // l_run: exact sum of the weights (for lse); l_bf: of their bf16 roundings (for O)
     int overflow;
     f32x4 acc[8][4];
 
@@ -232,6 +232,7 @@ __device__ __forceinline__ void decode_role(const DecodeParams& p, DecodeShared&
       // ---------------- one pass over the segment's half pages ----------------
       m_seen = kNegInf;
       l_run = 0.f;
+      l_bf = 0.f;
       overflow = 0;
       if constexpr (!scorer) {
         const bf16x8 zero8 = __builtin_bit_cast(bf16x8, u32x4{0, 0, 0, 0});
@@ -327,8 +328,9 @@ __device__ __forceinline__ void decode_role(const DecodeParams& p, DecodeShared&
               for (int h = 0; h < 2; ++h) {
                 const float w0 = __builtin_amdgcn_exp2f(__builtin_fmaf(x[i][2 * h], p.scale_log2, -mu));
                 const float w1 = __builtin_amdgcn_exp2f(__builtin_fmaf(x[i][2 * h + 1], p.scale_log2, -mu));
+                l_run += w0 + w1;
                 pk[i][h] = pack_bf16x2(w0, w1);
-                l_run += sum_bf16x2(pk[i][h]);
+                l_bf += sum_bf16x2(pk[i][h]);
               }
             // Slot 8*grp4 + 4*i + e holds key 16i + 4*grp4 + e of the half page.
             *(__attribute__((address_space(3))) u32x4*)(p_base + (uint32_t)((hp & 1) * kPBytes) + pw_off) =
@@ -389,7 +391,8 @@ __device__ __forceinline__ void decode_role(const DecodeParams& p, DecodeShared&
       // overflow vote in LDS.  (A second pass cannot overflow.)
       if constexpr (scorer) {
         const float l_row = row_sum4(l_run);
-        if (grp4 == 0) sh.l[srow] = l_row;
+        const float l_norm = row_sum4(l_bf);
+        if (grp4 == 0) sh.l[srow] = l_norm;
         const bool wave_overflow = __builtin_amdgcn_ballot_w64(overflow != 0) != 0;
         if (lane == 0) sh.flags[wave] = wave_overflow;
         if (grp4 == 0) {

@@ -153,11 +153,12 @@ __device__ inline uint32_t pack_bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){a, b}, bf16x2));
 }
 
-// Sum of the two bf16 values packed by pack_bf16x2, in fp32 (exact).  The
-// row sums are accumulated from the rounded weights that the PV product
-// actually uses, so that each output row is a convex combination of cached
-// values: the rounding of a weight then moves O only by that weight's share
-// of (v_j - O), never by a mismatch between the weights and their sum.
+// Sum of the two bf16 values packed by pack_bf16x2, in fp32 (exact).  Each
+// row keeps two sums: the exact one, for its log-sum-exp, and one over the
+// rounded weights that the PV product actually uses, which normalises O, so
+// that each output row is a convex combination of cached values: the
+// rounding of a weight then moves O only by that weight's share of
+// (v_j - O), never by a mismatch between the weights and their sum.
 __device__ inline float sum_bf16x2(uint32_t packed) {
   return __builtin_bit_cast(float, packed << 16) + __builtin_bit_cast(float, packed & 0xFFFF0000u);
 }

@@ -192,6 +192,7 @@ __device__ __forceinline__ void wide_worker(const DecodeParams& p, char (*lds_pa
     float m_ref[2] = {kNegInf, kNegInf};   // the score rows' reference points (log2 units)
     bool second_pass = false;   // rerun with m_ref = the row's maximum over the segment
     float m_seen[2], l_run[2];  // largest score this lane has seen; its share of sum_j 2^(s_j - m_ref)
+    float l_bf[2];              // its share of the same sum over the bf16-rounded weights (O's normaliser)
     float l_row[2];             // the rows' sums sum_j 2^(s_j - m_ref) at the end of a pass
     int overflow;               // a score rose more than kOverflowThreshold above the reference
     f32x4 acc[8][8];
@@ -202,6 +203,7 @@ __device__ __forceinline__ void wide_worker(const DecodeParams& p, char (*lds_pa
       for (int j = 0; j < 2; ++j) {
         m_seen[j] = kNegInf;
         l_run[j] = 0.f;
+        l_bf[j] = 0.f;
       }
       overflow = 0;
       {
@@ -353,8 +355,9 @@ __device__ __forceinline__ void wide_worker(const DecodeParams& p, char (*lds_pa
               for (int h = 0; h < 2; ++h) {
                 const float w0 = __builtin_amdgcn_exp2f(__builtin_fmaf(x[2 * kk + i][2 * h], p.scale_log2, -mu));
                 const float w1 = __builtin_amdgcn_exp2f(__builtin_fmaf(x[2 * kk + i][2 * h + 1], p.scale_log2, -mu));
+                l_run[j] += w0 + w1;
                 pk[i][h] = pack_bf16x2(w0, w1);
-                l_run[j] += sum_bf16x2(pk[i][h]);
+                l_bf[j] += sum_bf16x2(pk[i][h]);
               }
             // Slot 8*grp4 + 4*i + e of k-step kk holds key 32kk + 16i + 4*grp4 + e.
             *(__attribute__((address_space(3))) u32x4*)(pr_off[kk] + pw_base + (uint32_t)(j * 16 * kWidePRowBytes)) =
@@ -403,7 +406,8 @@ __device__ __forceinline__ void wide_worker(const DecodeParams& p, char (*lds_pa
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         l_row[j] = row_sum4(l_run[j]);
-        if (grp4 == 0) sx[srow[j]] = l_row[j];
+        const float l_norm = row_sum4(l_bf[j]);
+        if (grp4 == 0) sx[srow[j]] = l_norm;
       }
       const bool wave_overflow = __builtin_amdgcn_ballot_w64(overflow != 0) != 0;
       if (lane == 0) flags[wave] = wave_overflow;

@@ -23,6 +23,7 @@ from oracle.mla_oracle import (DEFAULT_SCALE, PAGE_SIZE, attend_range, lse_combi
 
 D_C, D_H, D_HR = 512, 128, 64
 D_QK = D_C + D_HR
+D_MODEL = 24          # output width of W^O in the brute-force cases (any width works)
 
 
 def _paged(rows_per_seq, rng, h_kv=1, extra_pages=2):
@@ -57,6 +58,7 @@ def _brute_force_case(seqlens, s_q, h_q, h_kv, causal, seed):
     w_uv = rng.standard_normal((h_q, D_H, D_C)) / math.sqrt(D_C)
     qc = rng.standard_normal((B, s_q, h_q, D_H))
     qr = rng.standard_normal((B, s_q, h_q, D_HR))
+    w_o = rng.standard_normal((D_MODEL, h_q * D_H)) / math.sqrt(h_q * D_H)
 
     # Un-absorbed: per head i, k_{j,i} = [W^UK_i c_j ; k^R_j], v_{j,i} = W^UV_i c_j,
     # q_{t,i} = [q^C ; q^R], o = sum_{j<=t} softmax(q.k / sqrt(d_h + d_h^R)) v.
@@ -82,6 +84,13 @@ def _brute_force_case(seqlens, s_q, h_q, h_kv, causal, seed):
                 z = math.fsum(math.exp(s - m) for s in scores)
                 lse_ref[b, i, t] = m + math.log(z)
                 o_ref[b, t, i] = sum(math.exp(s - m) / z * v for s, v in zip(scores, vals))
+    # Second output equation, head by head: W^O [o_1; ...; o_n] is the sum over
+    # heads i of W^O's column block i (columns i*d_h .. i*d_h + d_h - 1) times o_i.
+    u_ref = np.zeros((B, s_q, D_MODEL))
+    for b in range(B):
+        for t in range(s_q):
+            for i in range(h_q):
+                u_ref[b, t] += w_o[:, i * D_H:(i + 1) * D_H] @ o_ref[b, t, i]
 
     # Absorbed: q~ = [W^UK^T q^C ; q^R], cached rows [c^KV ; k^R] in pages.
     T = B * s_q
@@ -91,15 +100,17 @@ def _brute_force_case(seqlens, s_q, h_q, h_kv, causal, seed):
     kv, bt = _paged(rows, rng, h_kv)
     O, LSE = mla_decode_ref(q_abs, kv, bt, np.asarray(seqlens), dv=D_C, causal=causal)
     o_from_latent = mo.absorb_o_ref(O.reshape(T, h_q, D_C), w_uv).reshape(B, s_q, h_q, D_H)
-    return o_ref, lse_ref, o_from_latent, LSE
+    u_abs = mo.out_proj_ref(o_from_latent.reshape(T, h_q, D_H), w_o).reshape(B, s_q, D_MODEL)
+    return o_ref, lse_ref, o_from_latent, LSE, u_ref, u_abs
 
 
 def _p1_error(seqlens, s_q, h_q, h_kv, causal, seed):
-    o_ref, lse_ref, o_abs, lse_abs = _brute_force_case(seqlens, s_q, h_q, h_kv, causal, seed)
+    o_ref, lse_ref, o_abs, lse_abs, u_ref, u_abs = _brute_force_case(seqlens, s_q, h_q, h_kv, causal, seed)
     scale = max(1.0, np.abs(o_ref).max())
     fin = np.isfinite(lse_ref)
     assert (np.isfinite(lse_abs) == fin).all()
-    return max(np.abs(o_abs - o_ref).max() / scale, np.abs(lse_abs[fin] - lse_ref[fin]).max())
+    return max(np.abs(o_abs - o_ref).max() / scale, np.abs(lse_abs[fin] - lse_ref[fin]).max(),
+               np.abs(u_abs - u_ref).max() / max(1.0, np.abs(u_ref).max()))
 
 
 @pytest.mark.parametrize("seqlens,s_q,h_kv,causal", [
@@ -337,4 +348,20 @@ def test_planted_absorption_mistakes_are_caught(kind, monkeypatch):
         monkeypatch.setattr(mo, "absorb_q_ref", lambda qn, qr, w: aq(qn, qr, np.roll(w, 1, axis=0)))
     else:
         monkeypatch.setattr(mo, "absorb_o_ref", lambda o, w: np.roll(ao(o, w), 1, axis=1))
+    assert _p1_error((5, 70), 1, 4, 1, False, seed=3) > 1e-3
+
+
+@pytest.mark.parametrize("kind", ["heads_reversed", "head_dims_interleaved", "weight_blocks_rolled"])
+def test_planted_output_projection_mistakes_are_caught(kind, monkeypatch):
+    """P-1 also runs the absorbed side through out_proj_ref and compares it
+    with W^O applied head block by head block to the un-absorbed outputs, so
+    a wrong stacking order of the heads, or of W^O's column blocks, fails."""
+    op = mo.out_proj_ref
+    if kind == "heads_reversed":
+        monkeypatch.setattr(mo, "out_proj_ref", lambda o, w: op(np.asarray(o)[:, ::-1, :], w))
+    elif kind == "head_dims_interleaved":
+        monkeypatch.setattr(mo, "out_proj_ref",
+                            lambda o, w: op(np.ascontiguousarray(np.asarray(o).transpose(0, 2, 1)).reshape(np.shape(o)), w))
+    else:
+        monkeypatch.setattr(mo, "out_proj_ref", lambda o, w: op(o, np.roll(np.asarray(w), D_H, axis=1)))
     assert _p1_error((5, 70), 1, 4, 1, False, seed=3) > 1e-3
