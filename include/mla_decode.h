@@ -175,6 +175,31 @@ int mla_combine_splits(const int32_t* num_splits, int batch, int s_q, int h_q, i
                        int num_workers, void* o, float* lse, const void* workspace,
                        size_t workspace_bytes, void* stream);
 
+/* Maximum bytes of split partials mla_decode_paged_noalloc can hold: the
+ * size of the library's static device scratch array. */
+#define MLA_NOALLOC_SCRATCH_BYTES (64u << 20)
+
+/* mla_decode_paged for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same launches and results, with the split partials in a
+ * static device array of MLA_NOALLOC_SCRATCH_BYTES (64 MiB) that the library
+ * holds on each GPU it runs on until the process ends, instead of a caller
+ * workspace.  The caller still passes every input and the outputs o and lse.
+ * The call allocates nothing; its first call on a device looks up the array's
+ * address there.  Returns MLA_ERR_WORKSPACE, launching nothing, when
+ * mla_workspace_bytes() of the call exceeds the array (e.g. 256 query rows per
+ * latent head over more than ~250 workers plus sequences).  Every call on one
+ * GPU shares that GPU's array: calls that may overlap on one GPU (different
+ * streams, or host threads) race and must be serialised by the caller.
+ * Nothing in the array needs clearing: each call writes every partial it
+ * reads.  Other arguments, checks and errors as mla_decode_paged. */
+int mla_decode_paged_noalloc(const void* q, const void* kvcache, const int32_t* block_table,
+                             int max_pages_per_seq, int num_pages, const int32_t* cache_seqlens,
+                             int batch, int s_q, int h_q, int h_kv, int d_qk, int dv,
+                             const int32_t* tile_scheduler_metadata, const int32_t* num_splits,
+                             int num_workers, int causal, float softmax_scale, void* o, float* lse,
+                             void* stream);
+
 /* Checker of the tables a decode reads (the paging contract of the
  * deepseek.csdn.net FlashMLA article, section 4.2(1): logical block j of
  * sequence b is physical page block_table[b][j]; the arguments of the call on

@@ -76,6 +76,8 @@ def _load():
     lib.mla_outproj_workspace_bytes.argtypes = [c_int, c_int, c_int]
     lib.mla_outproj.restype = c_int
     lib.mla_outproj.argtypes = [vp, vp, vp, c_int, c_int, c_int, vp, c_size_t, vp]
+    lib.mla_decode_paged_noalloc.restype = c_int
+    lib.mla_decode_paged_noalloc.argtypes = decode_args[:19] + [vp]
     lib.mla_check_inputs.restype = c_int
     lib.mla_check_inputs.argtypes = [vp, c_int, c_int, vp, c_int, vp, vp]
     lib.mla_set_debug_checks.restype = None
@@ -356,6 +358,34 @@ def set_debug_checks(enable: bool) -> None:
     """Turn the checker in front of every decode call on or off (overrides
     MLA_DEBUG_CHECKS for the process)."""
     _load().mla_set_debug_checks(int(bool(enable)))
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def mla_decode_paged_noalloc(q: torch.Tensor, kvcache: torch.Tensor, block_table: torch.Tensor,
+                             cache_seqlens: torch.Tensor, dv: int, tile_scheduler_metadata: torch.Tensor,
+                             num_splits: torch.Tensor, o: torch.Tensor, lse: torch.Tensor, causal: bool = False,
+                             softmax_scale: Optional[float] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """mla_decode_paged with the split partials in the library's static
+    device scratch (no workspace, nothing allocated by the call): the
+    caller passes the outputs o bf16 [B][s_q][h_q][dv] and lse fp32
+    [B][h_q][s_q].  Calls that overlap on one GPU race on the scratch."""
+    _validate(q, kvcache, block_table, cache_seqlens, tile_scheduler_metadata, num_splits)
+    device = q.device
+    B, s_q, h_q, d_qk = q.shape
+    P, page, h_kv, _ = kvcache.shape
+    _require(o, "o", torch.bfloat16, device)
+    _require(lse, "lse", torch.float32, device)
+    if tuple(o.shape) != (B, s_q, h_q, dv) or tuple(lse.shape) != (B, h_q, s_q):
+        raise ValueError(f"o must be {(B, s_q, h_q, dv)} and lse {(B, h_q, s_q)}")
+    W = tile_scheduler_metadata.shape[0]
+    _check("mla_decode_paged_noalloc", _load().mla_decode_paged_noalloc(
+        q.data_ptr(), kvcache.data_ptr(), block_table.data_ptr(), block_table.shape[1], P,
+        cache_seqlens.data_ptr(), B, s_q, h_q, h_kv, d_qk, dv, tile_scheduler_metadata.data_ptr(),
+        num_splits.data_ptr(), W, int(bool(causal)), float(softmax_scale or 0.0), o.data_ptr(), lse.data_ptr(),
+        _stream_handle(device)))
+    return o, lse
 
 
 def outproj(o_heads: torch.Tensor, w_o: torch.Tensor, out: Optional[torch.Tensor] = None,

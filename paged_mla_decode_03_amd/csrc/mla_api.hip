@@ -359,6 +359,62 @@ int mla_decode_paged(const void* q, const void* kvcache, const int32_t* block_ta
   return launch_combine(p, (hipStream_t)stream);
 }
 
+// ---------------------------------------------------------------------------
+// Decode without a caller workspace: the split partials go to `scratch`, a
+// file-scope device array of kScratchBytes that every GPU the library runs on
+// holds until the process ends.  On the host the array's name is only a
+// stand-in for the device symbol, so its device address on each GPU is looked
+// up once (hipGetSymbolAddress, with that GPU current) and only that address
+// is passed to kernels or copies.
+// ---------------------------------------------------------------------------
+}  // extern "C"
+
+constexpr size_t kScratchBytes = (size_t)MLA_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+namespace {
+
+void* g_scratch_ptr[64];
+std::mutex g_scratch_mutex;
+
+// The current device's address of `scratch` (nullptr if the lookup failed).
+void* scratch_on_current_device() {
+  int device = 0;
+  if (hipGetDevice(&device) != hipSuccess || device < 0 || device >= 64) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[device]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return nullptr;
+    g_scratch_ptr[device] = ptr;
+  }
+  return g_scratch_ptr[device];
+}
+
+}  // namespace
+
+extern "C" {
+
+int mla_decode_paged_noalloc(const void* q, const void* kvcache, const int32_t* block_table, int max_pages_per_seq,
+                             int num_pages, const int32_t* cache_seqlens, int batch, int s_q, int h_q, int h_kv,
+                             int d_qk, int dv, const int32_t* meta, const int32_t* num_splits, int num_workers,
+                             int causal, float softmax_scale, void* o, float* lse, void* stream) {
+  // The host checks run first and need no device; the size check names the
+  // limit before the scratch address is looked up.
+  Shape s;
+  const void* fake_ws = (const void*)(uintptr_t)256;   // any 256-aligned non-null value: only checked, never used
+  int st = check_decode(q, kvcache, block_table, max_pages_per_seq, num_pages, cache_seqlens, batch, s_q, h_q, h_kv,
+                        d_qk, dv, meta, num_splits, num_workers, causal, o, lse, fake_ws, kScratchBytes, &s);
+  if (st != MLA_OK) return st;
+  void* ws = scratch_on_current_device();
+  if (!ws) return MLA_ERR_HIP;
+  const mla::DecodeParams p = decode_params(q, kvcache, block_table, max_pages_per_seq, num_pages, cache_seqlens, s, meta,
+                                            num_splits, num_workers, causal, softmax_scale, o, lse, ws);
+  if (debug_checks_on() && (st = debug_check_tables(p, num_pages, (hipStream_t)stream)) != MLA_OK) return st;
+  st = launch_decode(p, (hipStream_t)stream);
+  if (st != MLA_OK) return st;
+  return launch_combine(p, (hipStream_t)stream);
+}
+
 int mla_check_inputs(const int32_t* block_table, int max_pages_per_seq, int num_pages,
                      const int32_t* cache_seqlens, int batch, int32_t* result, void* stream) {
   if (!block_table || !cache_seqlens || !result) return MLA_ERR_INVALID_ARG;
