@@ -225,6 +225,44 @@ int mla_check_inputs(const int32_t* block_table, int max_pages_per_seq, int num_
  * MLA_ERR_BAD_INPUT without launching anything more if an entry is bad. */
 void mla_set_debug_checks(int enable);
 
+/* Whole-page allocator for the paged cache: memory goes out and comes back
+ * only in whole pages of 64 token slots (the lukefan.com talk on FlashMLA, on
+ * allocating and freeing in whole pages of 64; deepseek.csdn.net FlashMLA
+ * article, section 4.2(2), paged KV cache management), and every call runs on
+ * the stream with no host round trip.  Its state is caller memory:
+ *   free_pages [dev] int32 [num_pages]: a stack of free page ids,
+ *              free_pages[0 .. count) with the top at count - 1;
+ *   state      [dev] int32 [4]: count; status of the last call (0 done,
+ *              1 not enough free pages / the stack would overflow, 2 a
+ *              length or page id out of range); pages the last call moved
+ *              (or would have needed); 0.
+ * A call that cannot be satisfied changes nothing but state[1..2]; the
+ * caller reads state after synchronising.  Calls on one state must be
+ * stream-ordered.
+ *
+ * mla_pages_init: every page free, free_pages[i] = num_pages - 1 - i (the
+ *   first pages handed out are 0, 1, 2, ...).
+ * mla_pages_reserve: before s_new tokens are appended to every sequence of
+ *   lengths cache_seqlens (tokens cached now), sequence b needs
+ *   ceil((L_b + s_new) / 64) - ceil(L_b / 64) more pages; sequences in batch
+ *   order, and each one's blocks in ascending order, take pages popped from
+ *   the top of the stack into block_table[b][ceil(L_b/64) ..].  Refused (1)
+ *   if the free pages do not suffice, (2) if some L_b < 0 or
+ *   ceil((L_b + s_new)/64) > max_pages_per_seq.
+ * mla_pages_release: every sequence b with release[b] != 0 gives back its
+ *   ceil(L_b / 64) mapped pages, pushed in the same order, and its entries
+ *   become -1.  Refused (2) if a length or one of those page ids is out of
+ *   range, (1) if the stack would hold more than num_pages (pages given back
+ *   twice).  cache_seqlens is not changed by either call.
+ * Errors (returned, nothing launched): MLA_ERR_INVALID_ARG for null pointers
+ * or non-positive sizes (s_new may be 0), MLA_ERR_UNSUPPORTED for misaligned
+ * pointers. */
+int mla_pages_init(int32_t* free_pages, int32_t* state, int num_pages, void* stream);
+int mla_pages_reserve(int32_t* free_pages, int32_t* state, int num_pages, const int32_t* cache_seqlens, int batch,
+                      int s_new, int32_t* block_table, int max_pages_per_seq, void* stream);
+int mla_pages_release(int32_t* free_pages, int32_t* state, int num_pages, const int32_t* cache_seqlens,
+                      const int32_t* release, int batch, int32_t* block_table, int max_pages_per_seq, void* stream);
+
 /* The step before decode: write the latent rows of new tokens into the
  * paged cache.  The cache keeps the [c^KV (512); k^R (64)] row of every
  * token already seen, and a step computes only the new token's row and adds

@@ -22,6 +22,11 @@ What it computes (deepseek.csdn.net, "FlashMLA ... 详解", section 2.2 "DeepSee
   the page and slot its logical position maps to.
 * The output projection over all heads (:func:`out_proj_ref`), the second
   output equation of section 2.2: u_t = W^O [o_{t,1}; ...; o_{t,n_h}].
+* Whole-page allocation for the paged cache (:func:`pages_init_ref`,
+  :func:`pages_reserve_ref`, :func:`pages_release_ref`): memory is handed
+  out and taken back only in whole 64-token pages (the lukefan.com talk on
+  FlashMLA, on allocating and freeing in whole pages of 64; the
+  deepseek.csdn.net article, section 4.2(2), paged KV cache management).
 * The call on the dolphin-ai.jp FlashMLA page ("FlashMLA の使用方法", step 4):
   ``flash_mla_with_kvcache(q, kvcache, block_table, cache_seqlens, dv, ...,
   causal)`` returns the output and the log-sum-exp.
@@ -254,3 +259,88 @@ def out_proj_ref(o_heads, w_o):
     T, H, D = o.shape
     stacked = o.reshape(T, H * D)          # row t = o_{t,1} followed by o_{t,2}, ...
     return stacked @ w.T
+
+
+# ----------------------------------------------------------------------------
+# Whole-page allocation.
+#
+# The pool holds num_pages pages of 64 token slots; a sequence's cache is
+# always a whole number of pages, mapped through its block_table row.  The
+# free pages form a stack: free_pages[0 .. count) with the top at count - 1.
+# The order in which pages are handed out is this implementation's own rule
+# (the pages only ask for whole pages):
+#   * init: free_pages[i] = num_pages - 1 - i, so the first pages handed out
+#     are 0, 1, 2, ...;
+#   * reserve (before appending s_new tokens to every sequence of lengths L):
+#     sequence b needs ceil((L_b + s_new) / 64) - ceil(L_b / 64) more pages;
+#     sequences in batch order, and each one's blocks in ascending order, take
+#     pages popped from the top of the stack;
+#   * release (sequences whose flag is set): each one's ceil(L_b / 64) mapped
+#     pages are pushed, sequences in batch order and blocks in ascending
+#     order, and its block_table entries become -1.
+# A call that cannot be satisfied changes nothing and reports why: status 1
+# when the free pages do not suffice (reserve) or the stack would overflow
+# (release: pages given back twice), status 2 when a table or length is out
+# of range (a length past 64 * max_pages, a page id outside the pool).
+# ----------------------------------------------------------------------------
+
+def _pages(n_tokens: int) -> int:
+    return (n_tokens + PAGE_SIZE - 1) // PAGE_SIZE if n_tokens > 0 else 0
+
+
+def pages_init_ref(num_pages: int):
+    """A pool with every page free.  Returns (free_pages int64 [num_pages],
+    count)."""
+    return np.arange(num_pages - 1, -1, -1, dtype=np.int64), num_pages
+
+
+def pages_reserve_ref(free_pages, count: int, cache_seqlens, s_new: int, block_table):
+    """Map the pages the next s_new tokens of every sequence need.  Returns
+    (free_pages, count, block_table, status, pages handed out); on a status
+    other than 0 the inputs come back unchanged."""
+    fp = np.array(free_pages, dtype=np.int64, copy=True)
+    bt = np.array(block_table, copy=True)
+    L = np.asarray(cache_seqlens).astype(np.int64)
+    B, max_pages = bt.shape
+    needs = []
+    for b in range(B):
+        if L[b] < 0 or _pages(int(L[b]) + s_new) > max_pages:
+            return np.array(free_pages, copy=True), count, np.array(block_table, copy=True), 2, 0
+        needs.append((_pages(int(L[b])), _pages(int(L[b]) + s_new)))
+    total = sum(want - have for have, want in needs)
+    if total > count:
+        return np.array(free_pages, copy=True), count, np.array(block_table, copy=True), 1, total
+    top = count
+    for b, (have, want) in enumerate(needs):
+        for j in range(have, want):
+            top -= 1
+            bt[b, j] = fp[top]
+    return fp, top, bt, 0, total
+
+
+def pages_release_ref(free_pages, count: int, cache_seqlens, release, block_table, num_pages: int):
+    """Give back the pages of every sequence whose release flag is set.
+    Returns (free_pages, count, block_table, status, pages taken back)."""
+    fp = np.array(free_pages, dtype=np.int64, copy=True)
+    bt = np.array(block_table, copy=True)
+    L = np.asarray(cache_seqlens).astype(np.int64)
+    B, max_pages = bt.shape
+    total = 0
+    for b in range(B):
+        if not release[b]:
+            continue
+        n = _pages(int(L[b]))
+        if L[b] < 0 or n > max_pages or any(not 0 <= int(bt[b, j]) < num_pages for j in range(n)):
+            return np.array(free_pages, copy=True), count, np.array(block_table, copy=True), 2, 0
+        total += n
+    if count + total > num_pages:
+        return np.array(free_pages, copy=True), count, np.array(block_table, copy=True), 1, total
+    top = count
+    for b in range(B):
+        if not release[b]:
+            continue
+        for j in range(_pages(int(L[b]))):
+            fp[top] = bt[b, j]
+            top += 1
+            bt[b, j] = -1
+    return fp, top, bt, 0, total

@@ -72,12 +72,17 @@ def _load():
     lib.mla_kvcache_append.argtypes = [vp, vp, vp, c_int, c_int, vp, c_int, c_int, c_int, c_int, vp, vp]
     lib.mla_absorb_q.argtypes = [vp, vp, vp, vp, c_int, c_int, vp]
     lib.mla_absorb_o.argtypes = [vp, vp, vp, c_int, c_int, vp]
+    lib.mla_decode_paged_noalloc.restype = c_int
+    lib.mla_decode_paged_noalloc.argtypes = decode_args[:19] + [vp]
     lib.mla_outproj_workspace_bytes.restype = c_size_t
     lib.mla_outproj_workspace_bytes.argtypes = [c_int, c_int, c_int]
     lib.mla_outproj.restype = c_int
     lib.mla_outproj.argtypes = [vp, vp, vp, c_int, c_int, c_int, vp, c_size_t, vp]
-    lib.mla_decode_paged_noalloc.restype = c_int
-    lib.mla_decode_paged_noalloc.argtypes = decode_args[:19] + [vp]
+    for name in ("mla_pages_init", "mla_pages_reserve", "mla_pages_release"):
+        getattr(lib, name).restype = c_int
+    lib.mla_pages_init.argtypes = [vp, vp, c_int, vp]
+    lib.mla_pages_reserve.argtypes = [vp, vp, c_int, vp, c_int, c_int, vp, c_int, vp]
+    lib.mla_pages_release.argtypes = [vp, vp, c_int, vp, vp, c_int, vp, c_int, vp]
     lib.mla_check_inputs.restype = c_int
     lib.mla_check_inputs.argtypes = [vp, c_int, c_int, vp, c_int, vp, vp]
     lib.mla_set_debug_checks.restype = None
@@ -419,3 +424,46 @@ def outproj(o_heads: torch.Tensor, w_o: torch.Tensor, out: Optional[torch.Tensor
         workspace.data_ptr() if workspace is not None else None,
         workspace.numel() if workspace is not None else 0, _stream_handle(device)))
     return out
+
+
+class PagePool:
+    """Whole-page allocator state on the GPU (mla_pages_* in the C header):
+    a stack of free page ids and a 4-int state (free count, status of the
+    last call, pages it moved, 0).  Every call is stream-ordered and does not
+    synchronise; ``status()`` reads the state back."""
+
+    def __init__(self, num_pages: int, device: Optional[torch.device] = None):
+        device = device or torch.device("cuda", torch.cuda.current_device())
+        self.num_pages = int(num_pages)
+        self.free_pages = torch.empty(self.num_pages, dtype=torch.int32, device=device)
+        self.state = torch.empty(4, dtype=torch.int32, device=device)
+        _check("mla_pages_init", _load().mla_pages_init(self.free_pages.data_ptr(), self.state.data_ptr(),
+                                                        self.num_pages, _stream_handle(device)))
+
+    def reserve(self, cache_seqlens: torch.Tensor, s_new: int, block_table: torch.Tensor) -> None:
+        device = self.free_pages.device
+        _require(cache_seqlens, "cache_seqlens", torch.int32, device)
+        _require(block_table, "block_table", torch.int32, device)
+        if block_table.dim() != 2 or cache_seqlens.numel() != block_table.shape[0]:
+            raise ValueError("block_table must be [B][max_pages] and cache_seqlens [B]")
+        _check("mla_pages_reserve", _load().mla_pages_reserve(
+            self.free_pages.data_ptr(), self.state.data_ptr(), self.num_pages, cache_seqlens.data_ptr(),
+            block_table.shape[0], int(s_new), block_table.data_ptr(), block_table.shape[1], _stream_handle(device)))
+
+    def release(self, cache_seqlens: torch.Tensor, release: torch.Tensor, block_table: torch.Tensor) -> None:
+        device = self.free_pages.device
+        _require(cache_seqlens, "cache_seqlens", torch.int32, device)
+        _require(release, "release", torch.int32, device)
+        _require(block_table, "block_table", torch.int32, device)
+        if block_table.dim() != 2 or cache_seqlens.numel() != block_table.shape[0] \
+                or release.numel() != block_table.shape[0]:
+            raise ValueError("block_table must be [B][max_pages], cache_seqlens and release [B]")
+        _check("mla_pages_release", _load().mla_pages_release(
+            self.free_pages.data_ptr(), self.state.data_ptr(), self.num_pages, cache_seqlens.data_ptr(),
+            release.data_ptr(), block_table.shape[0], block_table.data_ptr(), block_table.shape[1],
+            _stream_handle(device)))
+
+    def status(self):
+        """(free count, status of the last call, pages it moved) read back (synchronises)."""
+        s = self.state.cpu().tolist()
+        return s[0], s[1], s[2]

@@ -5,6 +5,7 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <algorithm>
 #include <atomic>
 #include <mutex>
 
@@ -175,8 +176,8 @@ int launch_combine(const mla::DecodeParams& d, hipStream_t stream) {
   p.rows = d.rows;
   p.group = d.group;
   const long long tasks = (long long)d.batch * d.h_kv * d.rows;
-  const int blocks = (int)((tasks + mla::kCombineRowsPerBlock - 1) / mla::kCombineRowsPerBlock);
-  hipLaunchKernelGGL(mla::mla_combine_kernel, dim3(blocks), dim3(mla::kCombineRowsPerBlock * 64), 0, stream, p);
+  if (tasks >= (1LL << 31)) return MLA_ERR_UNSUPPORTED;
+  hipLaunchKernelGGL(mla::mla_combine_kernel, dim3((unsigned)tasks), dim3(mla::kCombineThreads), 0, stream, p);
   return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
 
@@ -426,6 +427,57 @@ int mla_check_inputs(const int32_t* block_table, int max_pages_per_seq, int num_
 }
 
 void mla_set_debug_checks(int enable) { g_debug_checks.store(enable ? 1 : 0); }
+
+int mla_pages_init(int32_t* free_pages, int32_t* state, int num_pages, void* stream) {
+  if (!free_pages || !state || num_pages <= 0) return MLA_ERR_INVALID_ARG;
+  if (!aligned(free_pages, 4) || !aligned(state, 4)) return MLA_ERR_UNSUPPORTED;
+  mla::PagesParams p{};
+  p.free_pages = free_pages;
+  p.state = state;
+  p.num_pages = num_pages;
+  const int blocks = (int)std::min<long long>(1024, ((long long)num_pages + 255) / 256);
+  hipLaunchKernelGGL(mla::mla_pages_init_kernel, dim3(blocks), dim3(256), 0, (hipStream_t)stream, p);
+  return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+int mla_pages_reserve(int32_t* free_pages, int32_t* state, int num_pages, const int32_t* cache_seqlens, int batch,
+                      int s_new, int32_t* block_table, int max_pages_per_seq, void* stream) {
+  if (!free_pages || !state || !cache_seqlens || !block_table) return MLA_ERR_INVALID_ARG;
+  if (num_pages <= 0 || batch <= 0 || s_new < 0 || max_pages_per_seq <= 0) return MLA_ERR_INVALID_ARG;
+  if (!aligned(free_pages, 4) || !aligned(state, 4) || !aligned(cache_seqlens, 4) || !aligned(block_table, 4))
+    return MLA_ERR_UNSUPPORTED;
+  mla::PagesParams p{};
+  p.free_pages = free_pages;
+  p.state = state;
+  p.block_table = block_table;
+  p.seqlens = cache_seqlens;
+  p.num_pages = num_pages;
+  p.batch = batch;
+  p.max_pages = max_pages_per_seq;
+  p.s_new = s_new;
+  hipLaunchKernelGGL(mla::mla_pages_reserve_kernel, dim3(1), dim3(mla::kPagesThreads), 0, (hipStream_t)stream, p);
+  return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+int mla_pages_release(int32_t* free_pages, int32_t* state, int num_pages, const int32_t* cache_seqlens,
+                      const int32_t* release, int batch, int32_t* block_table, int max_pages_per_seq, void* stream) {
+  if (!free_pages || !state || !cache_seqlens || !release || !block_table) return MLA_ERR_INVALID_ARG;
+  if (num_pages <= 0 || batch <= 0 || max_pages_per_seq <= 0) return MLA_ERR_INVALID_ARG;
+  if (!aligned(free_pages, 4) || !aligned(state, 4) || !aligned(cache_seqlens, 4) || !aligned(release, 4) ||
+      !aligned(block_table, 4))
+    return MLA_ERR_UNSUPPORTED;
+  mla::PagesParams p{};
+  p.free_pages = free_pages;
+  p.state = state;
+  p.block_table = block_table;
+  p.seqlens = cache_seqlens;
+  p.release = release;
+  p.num_pages = num_pages;
+  p.batch = batch;
+  p.max_pages = max_pages_per_seq;
+  hipLaunchKernelGGL(mla::mla_pages_release_kernel, dim3(1), dim3(mla::kPagesThreads), 0, (hipStream_t)stream, p);
+  return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
 
 int mla_kvcache_append(const void* kv_new, void* kvcache, const int32_t* block_table, int max_pages_per_seq,
                        int num_pages, const int32_t* cache_seqlens, int batch, int s_new, int h_kv, int d_qk,

@@ -20,7 +20,7 @@ constexpr int kNumXcd = 8;                         // MI355X: 8 XCDs, round-robi
 constexpr int kMetaInts = 8;
 constexpr int kMaxWorkers = 4096;
 constexpr int kSchedThreads = 256;
-constexpr int kCombineRowsPerBlock = 4;            // one wave per (sequence, head, query row)
+constexpr int kCombineThreads = 256;               // one 4-wave workgroup per (sequence, head, query row)
 
 // Wide decode workgroup: 128 query rows of a head, 4 waves (one per SIMD, 512
 // registers each), used when a head has more than 128 query rows.  Its two
@@ -77,6 +77,17 @@ struct SchedParams {
 };
 
 constexpr int kCheckThreads = 1024;
+constexpr int kPagesThreads = 1024;
+
+// Whole-page allocator: a stack of free page ids in device memory.
+struct PagesParams {
+  int32_t* free_pages;          // [num_pages]
+  int32_t* state;               // [4]: free count, status of the last call, pages it moved, 0
+  int32_t* block_table;         // [B][max_pages]
+  const int32_t* seqlens;       // [B]
+  const int32_t* release;       // [B] (release only)
+  int num_pages, batch, max_pages, s_new;
+};
 
 struct CheckParams {
   const int32_t* block_table;   // [B][max_pages]
@@ -92,5 +103,8 @@ __global__ void mla_decode_wide_kernel(DecodeParams p);
 __global__ void mla_combine_kernel(CombineParams p);
 __global__ void mla_sched_kernel(SchedParams p);
 __global__ void mla_check_kernel(CheckParams p);
+__global__ void mla_pages_init_kernel(PagesParams p);
+__global__ void mla_pages_reserve_kernel(PagesParams p);
+__global__ void mla_pages_release_kernel(PagesParams p);
 
 }  // namespace mla

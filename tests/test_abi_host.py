@@ -194,3 +194,28 @@ def test_absorb_outputs_must_match_the_call():
     wv = torch.zeros((4, 128, 512), dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         absorb_o(o, wv, out=torch.zeros((3, 4, 64), dtype=torch.bfloat16))
+
+
+def test_pages_calls_reject_invalid_arguments():
+    lib = _lib()
+    assert lib.mla_pages_init(None, FAKE, 8, None) == -1
+    assert lib.mla_pages_init(FAKE, FAKE, 0, None) == -1
+    assert lib.mla_pages_init(FAKE + 2, FAKE, 8, None) == -2
+    ok = dict(fp=FAKE, st=FAKE, P=8, L=FAKE, B=2, s_new=1, bt=FAKE, mp=4, stream=None)
+    for kw, status in [(dict(fp=None), -1), (dict(bt=None), -1), (dict(P=0), -1), (dict(B=0), -1),
+                       (dict(s_new=-1), -1), (dict(mp=0), -1), (dict(L=FAKE + 1), -2), (dict(st=FAKE + 2), -2)]:
+        args = dict(ok, **kw)
+        assert lib.mla_pages_reserve(*args.values()) == status, kw
+    ok = dict(fp=FAKE, st=FAKE, P=8, L=FAKE, rel=FAKE, B=2, bt=FAKE, mp=4, stream=None)
+    for kw, status in [(dict(rel=None), -1), (dict(B=-1), -1), (dict(rel=FAKE + 1), -2), (dict(bt=FAKE + 2), -2)]:
+        args = dict(ok, **kw)
+        assert lib.mla_pages_release(*args.values()) == status, kw
+
+
+def test_outproj_rejects_invalid_arguments():
+    lib = _lib()
+    assert lib.mla_outproj(None, FAKE, FAKE, 4, 256, 128, FAKE, 1 << 30, None) == -1
+    assert lib.mla_outproj(FAKE, FAKE, FAKE, 0, 256, 128, FAKE, 1 << 30, None) == -1
+    assert lib.mla_outproj(FAKE, FAKE, FAKE, 4, 200, 128, FAKE, 1 << 30, None) == -2    # k % 128
+    assert lib.mla_outproj(FAKE, FAKE, FAKE, 4, 256, 100, FAKE, 1 << 30, None) == -2    # n % 128
+    assert lib.mla_outproj(FAKE + 8, FAKE, FAKE, 4, 256, 128, FAKE, 1 << 30, None) == -2

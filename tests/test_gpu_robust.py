@@ -59,13 +59,16 @@ def test_causal_single_token_equals_noncausal():
     assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
 
 
-@pytest.mark.parametrize("counts", [[1, 3, 36], [2, 19, 5], [7, 13, 0], [11, 8, 22]])
+@pytest.mark.parametrize("counts", [[1, 3, 36], [2, 19, 5], [7, 13, 0], [11, 8, 22], [300, 1, 17], [2, 257, 0]])
 def test_combine_kernel_alone_on_synthetic_partials(counts):
     """Write partials for 3 sequences straight into the workspace and check
-    the merge against the oracle's formula (a split left alone, an empty
-    split, many splits: the kernel takes splits 4 at first, then 4, 2 and 1
-    at a time, and these counts reach every such tail)."""
-    B, s_q, h_q, h_kv, dv, W = 3, 1, 64, 1, 512, 40
+    the merge against the oracle's formula: a split left alone, an empty
+    sequence, a split that saw no key, and many splits (four waves take
+    splits w, w + 4, ..., four at a time each, so 16 per round: these counts
+    end every round at a different place, and above 256 the threads'
+    strided reductions of the lse values wrap around)."""
+    B, s_q, h_q, h_kv, dv = 3, 1, 64, 1, 512
+    W = max(40, sum(counts))
     R = s_q * h_q // h_kv
     ns = torch.tensor(np.concatenate([[0], np.cumsum(counts)]), dtype=torch.int32, device=DEV)
     q = torch.zeros((B, s_q, h_q, 576), dtype=torch.bfloat16, device=DEV)
