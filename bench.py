@@ -369,17 +369,21 @@ def gpu_clock_mhz():
     return None
 
 
-def achievable_bandwidth(dev, mib: int = 1024) -> dict:
-    """Measured HBM rates beside the 8 TB/s spec: a plain device copy of
-    `mib` MiB (read + write) and a read-only reduction over the same buffer,
-    each the median of 10 event-timed runs after warmup."""
+def achievable_bandwidth(dev, mib: int = 2048) -> dict:
+    """Measured HBM rates beside the 8 TB/s spec: the library's plain
+    streaming read of `mib` MiB (mla_stream_read) and a plain device copy of
+    half of it (read + write), each the median of 10 event-timed runs after
+    warmup."""
     import torch
+    from paged_mla_decode_03_amd.binding import stream_read
     n = mib << 20
     src = torch.ones(n // 4, dtype=torch.float32, device=dev)
-    dst = torch.empty_like(src)
+    half = src[: n // 8]
+    dst = torch.empty_like(half)
+    sink = torch.empty(4, dtype=torch.int32, device=dev)
     out = {}
-    for name, fn, nbytes in (("copy_gbs", lambda: dst.copy_(src), 2 * n),
-                             ("read_gbs", lambda: torch.sum(src), n)):
+    for name, fn, nbytes in (("read_gbs", lambda: stream_read(src, sink), n),
+                             ("copy_gbs", lambda: dst.copy_(half), n)):
         for _ in range(3):
             fn()
         ts = []

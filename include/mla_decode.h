@@ -263,6 +263,14 @@ int mla_pages_reserve(int32_t* free_pages, int32_t* state, int num_pages, const 
 int mla_pages_release(int32_t* free_pages, int32_t* state, int num_pages, const int32_t* cache_seqlens,
                       const int32_t* release, int batch, int32_t* block_table, int max_pages_per_seq, void* stream);
 
+/* Measurement helper, not a step of the method: a plain streaming read of
+ * `bytes` bytes at src (device memory; 16-byte aligned, bytes a multiple of
+ * 16), eight 16-byte loads in flight per lane over eight workgroups per
+ * compute unit.  Timing it gives the achievable HBM read rate that the
+ * decode's rooflines are reported beside.  sink [dev] 16 bytes, written only
+ * in the (never expected) case that the folded data match a fixed pattern. */
+int mla_stream_read(const void* src, size_t bytes, void* sink, void* stream);
+
 /* The step before decode: write the latent rows of new tokens into the
  * paged cache.  The cache keeps the [c^KV (512); k^R (64)] row of every
  * token already seen, and a step computes only the new token's row and adds

@@ -83,6 +83,8 @@ def _load():
     lib.mla_pages_init.argtypes = [vp, vp, c_int, vp]
     lib.mla_pages_reserve.argtypes = [vp, vp, c_int, vp, c_int, c_int, vp, c_int, vp]
     lib.mla_pages_release.argtypes = [vp, vp, c_int, vp, vp, c_int, vp, c_int, vp]
+    lib.mla_stream_read.restype = c_int
+    lib.mla_stream_read.argtypes = [vp, c_size_t, vp, vp]
     lib.mla_check_inputs.restype = c_int
     lib.mla_check_inputs.argtypes = [vp, c_int, c_int, vp, c_int, vp, vp]
     lib.mla_set_debug_checks.restype = None
@@ -467,3 +469,15 @@ class PagePool:
         """(free count, status of the last call, pages it moved) read back (synchronises)."""
         s = self.state.cpu().tolist()
         return s[0], s[1], s[2]
+
+
+def stream_read(src: torch.Tensor, sink: Optional[torch.Tensor] = None) -> None:
+    """Launch the library's plain streaming read over src (a measurement
+    helper: the achievable HBM read rate)."""
+    device = src.device
+    if not src.is_contiguous() or (src.numel() * src.element_size()) % 16:
+        raise ValueError("src must be contiguous and a multiple of 16 bytes")
+    if sink is None:
+        sink = torch.empty(4, dtype=torch.int32, device=device)
+    _check("mla_stream_read", _load().mla_stream_read(src.data_ptr(), src.numel() * src.element_size(),
+                                                      sink.data_ptr(), _stream_handle(device)))

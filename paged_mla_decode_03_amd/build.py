@@ -21,7 +21,8 @@ LIB_NAME = "libmla_decode.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
 SOURCES = ["mla_api.hip", "mla_sched.hip", "mla_decode.hip", "mla_decode_wide.hip", "mla_combine.hip",
            "mla_append.hip", "mla_absorb.hip", "mla_check.hip",
-           "mla_outproj.hip", "mla_pages.hip"]
+           "mla_outproj.hip", "mla_pages.hip",
+           "mla_stream.hip"]
 ARCH = "gfx950"
 
 # Packed fp32 VALU forms are kept out of the generated code; -O3 would

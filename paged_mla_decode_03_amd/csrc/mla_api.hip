@@ -177,7 +177,16 @@ int launch_combine(const mla::DecodeParams& d, hipStream_t stream) {
   p.group = d.group;
   const long long tasks = (long long)d.batch * d.h_kv * d.rows;
   if (tasks >= (1LL << 31)) return MLA_ERR_UNSUPPORTED;
-  hipLaunchKernelGGL(mla::mla_combine_kernel, dim3((unsigned)tasks), dim3(mla::kCombineThreads), 0, stream, p);
+  // Few sequences over many workers: a sequence may split into as many
+  // pieces as there are workers, and one workgroup per row spreads a long
+  // row's splits over four waves.  Otherwise one wave per row.
+  if (d.num_workers > 2 * d.batch) {
+    hipLaunchKernelGGL(mla::mla_combine_wide_kernel, dim3((unsigned)tasks), dim3(mla::kCombineThreads), 0, stream, p);
+  } else {
+    const long long blocks = (tasks + mla::kCombineRowsPerWaveBlock - 1) / mla::kCombineRowsPerWaveBlock;
+    hipLaunchKernelGGL(mla::mla_combine_kernel, dim3((unsigned)blocks), dim3(mla::kCombineRowsPerWaveBlock * 64), 0,
+                       stream, p);
+  }
   return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
 
@@ -428,6 +437,18 @@ int mla_check_inputs(const int32_t* block_table, int max_pages_per_seq, int num_
 
 void mla_set_debug_checks(int enable) { g_debug_checks.store(enable ? 1 : 0); }
 
+int mla_stream_read(const void* src, size_t bytes, void* sink, void* stream) {
+  if (!src || !sink || bytes == 0) return MLA_ERR_INVALID_ARG;
+  if (!aligned(src, 16) || !aligned(sink, 16) || bytes % 16 != 0) return MLA_ERR_UNSUPPORTED;
+  int cus = 0;
+  const int st = cu_count(-1, &cus);
+  if (st != MLA_OK) return st;
+  // Eight workgroups of eight waves per compute unit.
+  hipLaunchKernelGGL(mla::mla_stream_read_kernel, dim3(cus * 8), dim3(mla::kStreamThreads), 0, (hipStream_t)stream,
+                     (const uint4*)src, bytes / 16, (uint4*)sink);
+  return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
 int mla_pages_init(int32_t* free_pages, int32_t* state, int num_pages, void* stream) {
   if (!free_pages || !state || num_pages <= 0) return MLA_ERR_INVALID_ARG;
   if (!aligned(free_pages, 4) || !aligned(state, 4)) return MLA_ERR_UNSUPPORTED;
@@ -570,13 +591,13 @@ int mla_absorb_o(const void* o_latent, const void* w_uv, void* out, int tokens, 
 namespace {
 
 // K slices per column tile: the fewest (1, 2, 4, 8) that give the launch at
-// least one workgroup per compute unit, each wave keeping whole 32-wide k
-// steps.
+// least one workgroup per compute unit, each of the workgroup's waves
+// keeping whole 32-wide k steps.
 int outproj_splits(int T, int K, int N, int cus) {
   const long long tiles = (long long)(N / mla::kOutProjTileN) * ((T + mla::kOutProjTileT - 1) / mla::kOutProjTileT);
   int best = 1;
   for (int s = 1; s <= mla::kOutProjMaxSplits; s *= 2) {
-    if (K % (128 * s) != 0) break;
+    if (K % (32 * (mla::kOutProjWaves / 2) * s) != 0) break;
     best = s;
     if (tiles * s >= cus) break;
   }

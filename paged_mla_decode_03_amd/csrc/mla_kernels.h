@@ -20,7 +20,8 @@ constexpr int kNumXcd = 8;                         // MI355X: 8 XCDs, round-robi
 constexpr int kMetaInts = 8;
 constexpr int kMaxWorkers = 4096;
 constexpr int kSchedThreads = 256;
-constexpr int kCombineThreads = 256;               // one 4-wave workgroup per (sequence, head, query row)
+constexpr int kCombineThreads = 256;               // wide combine: one 4-wave workgroup per (sequence, head, row)
+constexpr int kCombineRowsPerWaveBlock = 4;        // combine: one wave per (sequence, head, query row)
 
 // Wide decode workgroup: 128 query rows of a head, 4 waves (one per SIMD, 512
 // registers each), used when a head has more than 128 query rows.  Its two
@@ -77,6 +78,7 @@ struct SchedParams {
 };
 
 constexpr int kCheckThreads = 1024;
+constexpr int kStreamThreads = 512;
 constexpr int kPagesThreads = 1024;
 
 // Whole-page allocator: a stack of free page ids in device memory.
@@ -100,9 +102,12 @@ template <bool kSingleHead>
 __global__ void mla_decode_kernel(DecodeParams p);
 template <bool kSingleHead>
 __global__ void mla_decode_wide_kernel(DecodeParams p);
+
 __global__ void mla_combine_kernel(CombineParams p);
+__global__ void mla_combine_wide_kernel(CombineParams p);
 __global__ void mla_sched_kernel(SchedParams p);
 __global__ void mla_check_kernel(CheckParams p);
+__global__ void mla_stream_read_kernel(const uint4* __restrict__ src, size_t n16, uint4* sink);
 __global__ void mla_pages_init_kernel(PagesParams p);
 __global__ void mla_pages_reserve_kernel(PagesParams p);
 __global__ void mla_pages_release_kernel(PagesParams p);

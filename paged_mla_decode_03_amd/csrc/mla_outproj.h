@@ -5,7 +5,8 @@
 
 namespace mla {
 
-constexpr int kOutProjThreads = 256;   // 4 waves, each over a quarter of the workgroup's K slice
+constexpr int kOutProjWaves = 8;       // each over an eighth of the workgroup's K slice
+constexpr int kOutProjThreads = kOutProjWaves * 64;
 constexpr int kOutProjTileN = 128;     // output columns per workgroup
 constexpr int kOutProjTileT = 64;      // tokens per workgroup
 constexpr int kNumXcdOutProj = 8;      // MI355X: 8 XCDs, round-robin block dispatch

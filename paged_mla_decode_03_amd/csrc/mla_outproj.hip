@@ -13,20 +13,23 @@
 // (235 MB for d_model = 7168 and 128 heads) and every byte of it is used
 // once per token, so the aim is to stream W from HBM exactly once while the
 // token rows come from L2.  Work decomposition:
-//   * A workgroup (4 waves) owns 128 output columns and 64 tokens over a
+//   * A workgroup (8 waves) owns 128 output columns and 64 tokens over a
 //     slice of K: S slices per column tile (split K, S chosen on the host so
-//     that the grid fills the chip), and within the workgroup each wave takes
-//     a quarter of the slice, so no two waves load the same bytes.
-//   * Wave tile: D^T[n][t] = W[n][:] . A[t][:] as 8 column tiles x 4 token
+//     that the grid fills the chip).  Wave w takes the column half w % 2
+//     (64 columns) over the K quarter w / 2 of the slice, so no two waves
+//     load the same weight bytes (the token rows, a few MB, come from L2).
+//   * Wave tile: D^T[n][t] = W[n][:] . A[t][:] as 4 column tiles x 4 token
 //     tiles of v_mfma_f32_16x16x32_bf16 (W rows as the A operand, token rows
 //     as the B operand: both are 16-byte reads along K straight from memory
-//     into registers), the next k step's 12 fragments in flight while this
-//     one's 32 MFMAs run.
+//     into registers).  The stream is bound by how many bytes are in flight
+//     (HBM latency is a few microseconds), so every wave keeps the next two
+//     k steps' 16 fragments in flight while one step's 16 MFMAs run: 16 KB
+//     per wave, 128 KB per compute unit.
 //   * The workgroups of one (column tile, K slice) that differ only in their
 //     token chunk get consecutive ids on the same XCD, so W is fetched from
 //     HBM once and found in that XCD's L2 by the others.
-//   * End: the four waves' partial tiles are summed in LDS in a fixed order
-//     (two halves of 64 columns); with S = 1 the workgroup writes bf16
+//   * End: the four K quarters' partial tiles are summed in LDS in a fixed
+//     order; with S = 1 the workgroup writes bf16
 //     output, else fp32 partials that mla_outproj_reduce_kernel sums over the
 //     S slices in slice order, so the result does not depend on scheduling.
 #include <hip/hip_runtime.h>
@@ -50,12 +53,13 @@ __device__ inline uint32_t pack2(float a, float b) {
 
 __device__ inline bf16x8 load8(const uint16_t* p) { return __builtin_bit_cast(bf16x8, *(const u32x4*)p); }
 
-constexpr int kRedStride = kOutProjTileN / 2 + 4;   // floats per LDS row of a half tile (padded)
+constexpr int kKParts = kOutProjWaves / 2;           // K quarters per workgroup slice
+constexpr int kRedStride = kOutProjTileN / 2 + 4;    // floats per LDS row of a column half (padded)
 
 }  // namespace
 
-__global__ __launch_bounds__(kOutProjThreads, 2) void mla_outproj_kernel(OutProjParams p) {
-  __shared__ __attribute__((aligned(16))) float red[4][kOutProjTileT][kRedStride];
+__global__ __launch_bounds__(kOutProjThreads, 1) void mla_outproj_kernel(OutProjParams p) {
+  __shared__ __attribute__((aligned(16))) float red[kOutProjWaves][kOutProjTileT][kRedStride];
   // Block -> (column tile, K slice, token chunk): the token chunks of one
   // (column tile, K slice) are consecutive blocks on one XCD.
   const int xcd = blockIdx.x % kNumXcdOutProj;
@@ -68,81 +72,88 @@ __global__ __launch_bounds__(kOutProjThreads, 2) void mla_outproj_kernel(OutProj
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
+  const int half = wave & 1;                           // column half
+  const int part = wave >> 1;                          // K quarter
   const int col = lane & 15;
   const int kq = 8 * (lane >> 4);
-  const int n0 = nt * kOutProjTileN;
+  const int n0 = nt * kOutProjTileN + 64 * half;
   const int t0 = tc * kOutProjTileT;
-  const int kw = p.K / (p.splits * 4);                 // this wave's share of K
-  const int kbeg = s * (p.K / p.splits) + wave * kw;
+  const int kw = p.K / (p.splits * kKParts);           // this wave's share of K (a multiple of 32)
+  const int kbeg = s * (p.K / p.splits) + part * kw;
 
   // Fragment sources: W rows n0 + 16d + col, token rows t0 + 16r + col
   // (rows past T repeat row T-1; their outputs are never stored).
-  const uint16_t* wsrc[8];
+  const uint16_t* wsrc[4];
   const uint16_t* asrc[4];
 #pragma unroll
-  for (int d = 0; d < 8; ++d) wsrc[d] = p.w + (size_t)(n0 + 16 * d + col) * p.K + kbeg + kq;
+  for (int d = 0; d < 4; ++d) wsrc[d] = p.w + (size_t)(n0 + 16 * d + col) * p.K + kbeg + kq;
 #pragma unroll
   for (int r = 0; r < 4; ++r) asrc[r] = p.a + (size_t)min(t0 + 16 * r + col, p.T - 1) * p.K + kbeg + kq;
 
-  f32x4 acc[8][4];
+  f32x4 acc[4][4];
 #pragma unroll
-  for (int d = 0; d < 8; ++d)
+  for (int d = 0; d < 4; ++d)
 #pragma unroll
     for (int r = 0; r < 4; ++r) acc[d][r] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  bf16x8 wf[8], af[4];
-#pragma unroll
-  for (int d = 0; d < 8; ++d) wf[d] = load8(wsrc[d]);
-#pragma unroll
-  for (int r = 0; r < 4; ++r) af[r] = load8(asrc[r]);
+  // Two k steps in flight ahead of the one being multiplied.  Steps past
+  // the wave's share reload its last step (in bounds, never multiplied).
   const int steps = kw / 32;
-  for (int ks = 0; ks < steps; ++ks) {
-    bf16x8 wn[8], an[4];
-    const int nk = (ks + 1 < steps ? ks + 1 : ks) * 32;    // the last step reloads its own (unused) fragments
+  auto koff = [&](int ks) __attribute__((always_inline)) { return (ks < steps ? ks : steps - 1) * 32; };
+  bf16x8 wf[3][4], af[3][4];
 #pragma unroll
-    for (int d = 0; d < 8; ++d) wn[d] = load8(wsrc[d] + nk);
+  for (int j = 0; j < 2; ++j) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) an[r] = load8(asrc[r] + nk);
+    for (int d = 0; d < 4; ++d) wf[j][d] = load8(wsrc[d] + koff(j));
 #pragma unroll
-    for (int d = 0; d < 8; ++d)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) acc[d][r] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[d], af[r], acc[d][r], 0, 0, 0);
-#pragma unroll
-    for (int d = 0; d < 8; ++d) wf[d] = wn[d];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) af[r] = an[r];
+    for (int r = 0; r < 4; ++r) af[j][r] = load8(asrc[r] + koff(j));
   }
-
-  // acc[d][r][i] = partial D^T[n0 + 16d + 4*(lane/16) + i][t0 + 16r + col].
-  // Sum the four waves' partials in LDS, 64 columns at a time.
+  auto step = [&]<int J>(int ks) __attribute__((always_inline)) {
+    constexpr int L = (J + 2) % 3;
 #pragma unroll
-  for (int hf = 0; hf < 2; ++hf) {
+    for (int d = 0; d < 4; ++d) wf[L][d] = load8(wsrc[d] + koff(ks + 2));
+#pragma unroll
+    for (int r = 0; r < 4; ++r) af[L][r] = load8(asrc[r] + koff(ks + 2));
 #pragma unroll
     for (int d = 0; d < 4; ++d)
 #pragma unroll
       for (int r = 0; r < 4; ++r)
-        *(f32x4*)&red[wave][16 * r + col][16 * d + 4 * (lane >> 4)] = acc[4 * hf + d][r];
-    __syncthreads();
-    // Thread i sums 4 consecutive columns of one token row, 4 rows apart.
+        acc[d][r] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[J][d], af[J][r], acc[d][r], 0, 0, 0);
+  };
+  int ks = 0;
+  for (; ks + 3 <= steps; ks += 3) {
+    step.template operator()<0>(ks);
+    step.template operator()<1>(ks + 1);
+    step.template operator()<2>(ks + 2);
+  }
+  if (ks < steps) step.template operator()<0>(ks);
+  if (ks + 1 < steps) step.template operator()<1>(ks + 1);
+
+  // acc[d][r][i] = partial D^T[n0 + 16d + 4*(lane/16) + i][t0 + 16r + col].
 #pragma unroll
-    for (int j = 0; j < (kOutProjTileT * kOutProjTileN / 2) / (4 * kOutProjThreads); ++j) {
-      const int e = threadIdx.x + j * kOutProjThreads;       // index of a 4-column group
-      const int t = e / (kOutProjTileN / 8);
-      const int c4 = 4 * (e % (kOutProjTileN / 8));
-      f32x4 v = *(const f32x4*)&red[0][t][c4];
-      v += *(const f32x4*)&red[1][t][c4];
-      v += *(const f32x4*)&red[2][t][c4];
-      v += *(const f32x4*)&red[3][t][c4];
-      const int tt = t0 + t;
-      const int n = n0 + 64 * hf + c4;
-      if (tt < p.T) {
-        if (p.splits == 1)
-          *(u32x2*)(p.out + (size_t)tt * p.N + n) = u32x2{pack2(v[0], v[1]), pack2(v[2], v[3])};
-        else
-          *(f32x4*)(p.partial + ((size_t)s * p.T + tt) * p.N + n) = v;
-      }
+  for (int d = 0; d < 4; ++d)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) *(f32x4*)&red[wave][16 * r + col][16 * d + 4 * (lane >> 4)] = acc[d][r];
+  __syncthreads();
+  // Thread i sums 4 consecutive columns of one token row over the K quarters
+  // (waves half, half + 2, half + 4, half + 6), in that order.
+#pragma unroll
+  for (int j = 0; j < (kOutProjTileT * kOutProjTileN) / (4 * kOutProjThreads); ++j) {
+    const int e = threadIdx.x + j * kOutProjThreads;    // 2048 groups: 64 rows x 128 columns / 4
+    const int t = e / (kOutProjTileN / 4);
+    const int c = 4 * (e % (kOutProjTileN / 4));         // column within the tile
+    const int h = c / 64, c4 = c % 64;
+    f32x4 v = *(const f32x4*)&red[h][t][c4];
+#pragma unroll
+    for (int q = 1; q < kKParts; ++q) v += *(const f32x4*)&red[h + 2 * q][t][c4];
+    const int tt = t0 + t;
+    const int n = nt * kOutProjTileN + c;
+    if (tt < p.T) {
+      if (p.splits == 1)
+        *(u32x2*)(p.out + (size_t)tt * p.N + n) = u32x2{pack2(v[0], v[1]), pack2(v[2], v[3])};
+      else
+        *(f32x4*)(p.partial + ((size_t)s * p.T + tt) * p.N + n) = v;
     }
-    __syncthreads();
   }
 }
 

@@ -59,18 +59,30 @@ def test_causal_single_token_equals_noncausal():
     assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
 
 
+@pytest.mark.parametrize("variant", ["wave", "wide"])
 @pytest.mark.parametrize("counts", [[1, 3, 36], [2, 19, 5], [7, 13, 0], [11, 8, 22], [300, 1, 17], [2, 257, 0]])
-def test_combine_kernel_alone_on_synthetic_partials(counts):
-    """Write partials for 3 sequences straight into the workspace and check
-    the merge against the oracle's formula: a split left alone, an empty
-    sequence, a split that saw no key, and many splits (four waves take
-    splits w, w + 4, ..., four at a time each, so 16 per round: these counts
-    end every round at a different place, and above 256 the threads'
-    strided reductions of the lse values wrap around)."""
-    B, s_q, h_q, h_kv, dv = 3, 1, 64, 1, 512
-    W = max(40, sum(counts))
+def test_combine_kernel_alone_on_synthetic_partials(counts, variant):
+    """Write partials straight into the workspace and check the merge of the
+    first three sequences against the oracle's formula: a split left alone,
+    an empty sequence, a split that saw no key, and many splits.  Both
+    variants: one wave per row (chosen when workers <= 2 x sequences; its
+    first four splits load together, then four, two, one at a time) and one
+    workgroup per row (chosen when there are more workers; four waves take
+    splits w, w + 4, ..., four at a time each, so 16 per round, and above 256
+    splits the threads' strided reductions of the lse values wrap around).
+    These counts end every round at a different place."""
+    s_q, h_q, h_kv, dv = 1, 64, 1, 512
+    if variant == "wide":
+        full = list(counts)
+        W = max(40, sum(full))
+    else:
+        pad = max(0, sum(counts) - 6)                # enough one-split sequences that W <= 2 B
+        full = list(counts) + [1] * pad
+        W = sum(full)
+    B = len(full)
+    assert (W > 2 * B) == (variant == "wide")
     R = s_q * h_q // h_kv
-    ns = torch.tensor(np.concatenate([[0], np.cumsum(counts)]), dtype=torch.int32, device=DEV)
+    ns = torch.tensor(np.concatenate([[0], np.cumsum(full)]), dtype=torch.int32, device=DEV)
     q = torch.zeros((B, s_q, h_q, 576), dtype=torch.bfloat16, device=DEV)
     kv = torch.zeros((1, 64, h_kv, 576), dtype=torch.bfloat16, device=DEV)
     buf = DecodeBuffers(q, kv, dv, W)
@@ -81,7 +93,7 @@ def test_combine_kernel_alone_on_synthetic_partials(counts):
     rng = np.random.default_rng(0)
     po = rng.standard_normal((slots, h_kv, R, dv)).astype(np.float32)
     pl = rng.normal(3.0, 2.0, (slots, h_kv, R)).astype(np.float32)
-    pl[int(np.cumsum(counts)[0]) + 1] = -np.inf  # sequence 1: its second split saw no key
+    pl[int(np.cumsum(counts)[0]) + 1] = -np.inf  # a split that saw no key
     ws_o.copy_(torch.from_numpy(po))
     ws_l.copy_(torch.from_numpy(pl))
     buf.o.fill_(7.0)
@@ -90,8 +102,8 @@ def test_combine_kernel_alone_on_synthetic_partials(counts):
     torch.cuda.synchronize()
     o = buf.o.float().cpu().numpy()
     lse = buf.lse.cpu().numpy()
-    for b in range(B):
-        s0, n = int(ns[b]), counts[b]
+    for b in range(3):
+        s0, n = int(ns[b]), full[b]
         if n == 1:                               # single split: left to the decode kernel
             assert (o[b] == 7.0).all() and (lse[b] == 7.0).all()
             continue
