@@ -60,7 +60,7 @@ def parse():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=15.0)
-    ap.add_argument("--op", choices=["decode", "append", "absorb", "outproj"], default="decode",
+    ap.add_argument("--op", choices=["decode", "append", "absorb", "outproj", "fp8"], default="decode",
                     help="append: time the cache append of the workload's new tokens instead; absorb: the "
                          "per-head projections before and after the decode (each prints its own JSON line)")
     ap.add_argument("--append-tokens", type=int, default=0,
@@ -348,6 +348,87 @@ def bench_outproj(args):
     print(json.dumps(out_line), flush=True)
 
 
+def _fp8_codes(latents, kv_scale):
+    """E4M3 codes of latents / kv_scale by torch's float8 cast (round to
+    nearest even; the values are clamped to +-448 first): the fp8 cache a
+    quantising append would leave for the benchmark's latents."""
+    import torch
+    x = (latents.float() * (1.0 / kv_scale)).clamp_(-448.0, 448.0)
+    return x.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def bench_fp8(args):
+    """The decode over an fp8 cache (one byte per cached value, OCP E4M3 codes
+    with one scale) against the same step over the bf16 cache, on the
+    workloads with up to 128 query rows per head (mem_bound, var_len,
+    skewed): median step time (decode + combine, events around each step,
+    pools rotated past the Infinity Cache) and the step's algorithmic rate,
+    the fp8 cache counted at one byte per value."""
+    import torch
+
+    sys.path.insert(0, ROOT)
+    from paged_mla_decode_03_amd import DecodeBuffers, get_mla_metadata, mla_decode_paged, mla_decode_paged_fp8
+    from workloads import FP8_KV_SCALE, WORKLOADS, algorithmic_counts, make_fp8_inputs, make_inputs
+
+    dev = torch.device("cuda", 0)
+    res = {}
+    for name in ("mem_bound", "var_len", "skewed"):
+        w = WORKLOADS[name]
+        out = {}
+        for kind in ("bf16", "fp8"):
+            print(f"[bench] fp8 op: {name} {kind}", file=sys.stderr, flush=True)
+            inp = make_fp8_inputs(w, args.seed, encode=_fp8_codes) if kind == "fp8" else make_inputs(w, args.seed)
+            L = inp.cache_seqlens.numpy()
+            counts = algorithmic_counts(w, L, inp.block_table.shape[1])
+            nbytes = counts["total_bytes"] - (counts["kv_bytes"] // 2 if kind == "fp8" else 0)
+            q, bt, sl = inp.q.to(dev), inp.block_table.to(dev), inp.cache_seqlens.to(dev)
+            kv_bytes = inp.kvcache.numel() * inp.kvcache.element_size()
+            n_pools = max(2, -(-2 * MALL_BYTES // kv_bytes) + 1)
+            pools = [inp.kvcache.to(dev)]
+            for _ in range(1, n_pools):
+                pools.append(pools[0].clone())
+            meta, ns = get_mla_metadata(sl, w.s_q * w.h_q // w.h_kv, w.h_kv)
+            buf = DecodeBuffers(q, pools[0] if kind == "bf16" else torch.empty((1, 64, w.h_kv, 576), device=dev,
+                                                                                dtype=torch.bfloat16),
+                                512, meta.shape[0])
+            if kind == "fp8":
+                sc = inp.extra["kv_scale"]
+                fn = lambda i: mla_decode_paged_fp8(q, pools[i % n_pools], sc, bt, sl, 512, meta, ns, buffers=buf)
+            else:
+                fn = lambda i: mla_decode_paged(q, pools[i % n_pools], bt, sl, 512, meta, ns, buffers=buf)
+            for i in range(args.warmup):
+                fn(i)
+            torch.cuda.synchronize()
+            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+            for i in range(args.steps):
+                evs[i][0].record()
+                fn(i)
+                evs[i][1].record()
+            torch.cuda.synchronize()
+            us = np.array([a.elapsed_time(z) for a, z in evs]) * 1e3
+            med = float(np.median(us))
+            out[kind] = {"step_us_median": round(med, 2), "p10": round(_pct(us, 10), 2), "p90": round(_pct(us, 90), 2),
+                         "algorithmic_bytes": int(nbytes), "gbs": round(nbytes / (med * 1e-6) / 1e9, 2),
+                         "hbm_frac": round(nbytes / (med * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+            del pools, q, bt, sl, buf, inp
+            torch.cuda.empty_cache()
+        out["speedup_vs_bf16"] = round(out["bf16"]["step_us_median"] / out["fp8"]["step_us_median"], 3)
+        print(f"[bench] fp8 op: {name}: bf16 {out['bf16']['step_us_median']} us, fp8 {out['fp8']['step_us_median']} us "
+              f"({out['speedup_vs_bf16']}x)", file=sys.stderr, flush=True)
+        res[name] = out
+    head = res["mem_bound"]["fp8"]
+    line = {"metric": "paged MLA decode over an fp8 cache: achieved HBM GB/s (fp8 bytes)", "value": head["gbs"],
+            "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "ms_per_step": round(head["step_us_median"] / 1e3, 5), "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": "fp8 cache, bf16 compute", "data": "synthetic",
+            "config": {"workload": "mem_bound fp8 cache", "kv_scale": FP8_KV_SCALE, "seed": args.seed},
+            "roofline": {"kernel": "mla_decode_fp8_kernel", "bound": "hbm", "achieved": head["gbs"],
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": head["hbm_frac"], "traffic": None,
+                         "duration": "median step (decode + combine)"},
+            "per_config": res}
+    print(json.dumps(line), flush=True)
+
+
 def _pct(a, q):
     return float(np.percentile(np.asarray(a), q))
 
@@ -558,6 +639,9 @@ def main():
         return
     if args.op == "outproj":
         bench_outproj(args)
+        return
+    if args.op == "fp8":
+        bench_fp8(args)
         return
 
     import torch

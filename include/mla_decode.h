@@ -200,6 +200,35 @@ int mla_decode_paged_noalloc(const void* q, const void* kvcache, const int32_t* 
                              int num_workers, int causal, float softmax_scale, void* o, float* lse,
                              void* stream);
 
+/* fp8 latent cache (the ruibaoantu.com page's outlook: BF16 mixed with
+ * FP8; read here as fp8 storage of the cached rows with bf16 queries, bf16
+ * MFMA products, fp32 accumulation and bf16 outputs).  The cache holds one
+ * byte per value, OCP FP8 E4M3 ("E4M3FN": sign, 4 exponent bits with bias 7,
+ * 3 mantissa bits, no infinities, 0x7F/0xFF NaN, largest finite 448), and
+ * one fp32 scale kv_scale > 0 for the whole cache: a cached value is
+ * e4m3_value(code) * kv_scale.
+ *
+ * mla_kvcache_append_fp8: mla_kvcache_append into such a cache
+ *   (kvcache_fp8 [dev] uint8 [num_pages][64][h_kv][576], 16-byte aligned):
+ *   each new bf16 value x is stored as the nearest E4M3 code, ties to even,
+ *   of float(x) * (1 / kv_scale) (the reciprocal and the product in fp32)
+ *   clamped to [-448, 448]; a NaN stays NaN (code 0xFF).  Other arguments,
+ *   the bad_rows rule and errors as mla_kvcache_append; kv_scale must be a
+ *   positive finite float (else MLA_ERR_INVALID_ARG).
+ * mla_decode_paged_fp8: mla_decode_paged over such a cache, the result that
+ *   of the cache's values e4m3_value(code) * kv_scale.  Heads of up to 128
+ *   query rows (rows_per_kv = s_q*h_q/h_kv <= 128; MLA_ERR_UNSUPPORTED
+ *   above).  The same metadata, workspace, outputs and errors as
+ *   mla_decode_paged. */
+int mla_kvcache_append_fp8(const void* kv_new, void* kvcache_fp8, float kv_scale, const int32_t* block_table,
+                           int max_pages_per_seq, int num_pages, const int32_t* cache_seqlens, int batch, int s_new,
+                           int h_kv, int d_qk, int32_t* bad_rows, void* stream);
+int mla_decode_paged_fp8(const void* q, const void* kvcache_fp8, float kv_scale, const int32_t* block_table,
+                         int max_pages_per_seq, int num_pages, const int32_t* cache_seqlens, int batch, int s_q,
+                         int h_q, int h_kv, int d_qk, int dv, const int32_t* tile_scheduler_metadata,
+                         const int32_t* num_splits, int num_workers, int causal, float softmax_scale, void* o,
+                         float* lse, void* workspace, size_t workspace_bytes, void* stream);
+
 /* Checker of the tables a decode reads (the paging contract of the
  * deepseek.csdn.net FlashMLA article, section 4.2(1): logical block j of
  * sequence b is physical page block_table[b][j]; the arguments of the call on

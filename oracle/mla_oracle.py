@@ -27,6 +27,11 @@ What it computes (deepseek.csdn.net, "FlashMLA ... 详解", section 2.2 "DeepSee
   out and taken back only in whole 64-token pages (the lukefan.com talk on
   FlashMLA, on allocating and freeing in whole pages of 64; the
   deepseek.csdn.net article, section 4.2(2), paged KV cache management).
+* An fp8 cache (:func:`fp8_e4m3_encode_ref`, :func:`fp8_e4m3_decode_ref`,
+  :func:`kvcache_append_fp8_ref`, :func:`mla_decode_fp8_ref`): the
+  ruibaoantu.com page's outlook on mixing BF16 with FP8; read here as a
+  cache whose latent rows are stored in fp8 while queries, the arithmetic
+  and the outputs stay bf16/fp32.
 * The call on the dolphin-ai.jp FlashMLA page ("FlashMLA の使用方法", step 4):
   ``flash_mla_with_kvcache(q, kvcache, block_table, cache_seqlens, dv, ...,
   causal)`` returns the output and the log-sum-exp.
@@ -344,3 +349,69 @@ def pages_release_ref(free_pages, count: int, cache_seqlens, release, block_tabl
             top += 1
             bt[b, j] = -1
     return fp, top, bt, 0, total
+
+
+# ----------------------------------------------------------------------------
+# fp8 cache: OCP E4M3 ("E4M3FN": 1 sign, 4 exponent bits with bias 7, 3
+# mantissa bits; no infinities; 0x7F / 0xFF are NaN; largest finite 448;
+# subnormals k * 2^-9).  The cache holds e4m3(clamp(x * inv_scale)) for one
+# fp32 scale per cache, x * inv_scale computed in fp32 and clamped to
+# [-448, 448] before rounding to nearest even, so every finite input maps to
+# a finite code; an element's value is decode(code) * scale.
+# ----------------------------------------------------------------------------
+
+FP8_E4M3_MAX = 448.0
+
+
+def fp8_e4m3_decode_ref(codes) -> np.ndarray:
+    """Value of each E4M3FN byte (NaN for 0x7F / 0xFF), from the format's
+    definition: sign * 2^(e - 7) * (1 + m / 8) for e > 0, sign * 2^-6 * m / 8
+    for e = 0."""
+    c = np.asarray(codes).astype(np.int64) & 0xFF
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = c & 0x7
+    val = np.where(e > 0, np.ldexp(1.0 + m / 8.0, (e - 7).astype(np.int64)), np.ldexp(m / 8.0, -6))
+    val = sign * val
+    return np.where((c & 0x7F) == 0x7F, np.nan, val)
+
+
+_E4M3_POS = fp8_e4m3_decode_ref(np.arange(0x7F))      # the 127 non-negative finite codes, ascending
+
+
+def fp8_e4m3_encode_ref(x) -> np.ndarray:
+    """Nearest E4M3FN code to each value (ties to the even code), after
+    clamping to [-448, 448]; a NaN maps to the NaN code 0xFF."""
+    v = np.asarray(x, dtype=np.float64)
+    nan = np.isnan(v)
+    a = np.clip(np.abs(np.where(nan, 0.0, v)), 0.0, FP8_E4M3_MAX)
+    hi = np.searchsorted(_E4M3_POS, a, side="left")          # first code with value >= a
+    hi = np.minimum(hi, len(_E4M3_POS) - 1)
+    lo = np.maximum(hi - 1, 0)
+    d_lo = a - _E4M3_POS[lo]
+    d_hi = _E4M3_POS[hi] - a
+    pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0))
+    code = np.where(pick_hi, hi, lo)
+    code = np.where(a == 0.0, 0, code)
+    neg = np.signbit(v) & ~nan
+    code = np.where(neg, code | 0x80, code)
+    code = np.where(nan, 0xFF, code)                       # NaN in, NaN code out (0xFF)
+    return code.astype(np.uint8)
+
+
+def kvcache_append_fp8_ref(kvcache_fp8, block_table, cache_seqlens, kv_new, inv_scale):
+    """:func:`kvcache_append_ref` into an fp8 cache: each new value x (bf16)
+    becomes e4m3(clamp(float32(x) * float32(inv_scale))), the product in fp32.
+    Returns (new cache codes, rows not written)."""
+    new = np.asarray(as_f64(kv_new), dtype=np.float32)
+    codes = fp8_e4m3_encode_ref((new * np.float32(inv_scale)).astype(np.float32))
+    return kvcache_append_ref(kvcache_fp8, block_table, cache_seqlens, codes)
+
+
+def mla_decode_fp8_ref(q, kvcache_fp8, kv_scale, block_table, cache_seqlens, dv: int = 512, causal: bool = False,
+                       softmax_scale: float | None = None, batch_subset=None):
+    """:func:`mla_decode_ref` over the fp8 cache's values, decode(code) *
+    kv_scale, exactly as the cache defines them."""
+    vals = fp8_e4m3_decode_ref(kvcache_fp8) * float(kv_scale)
+    return mla_decode_ref(q, vals, block_table, cache_seqlens, dv, causal=causal, softmax_scale=softmax_scale,
+                          batch_subset=batch_subset)

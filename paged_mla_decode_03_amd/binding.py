@@ -85,6 +85,10 @@ def _load():
     lib.mla_pages_release.argtypes = [vp, vp, c_int, vp, vp, c_int, vp, c_int, vp]
     lib.mla_stream_read.restype = c_int
     lib.mla_stream_read.argtypes = [vp, c_size_t, vp, vp]
+    lib.mla_decode_paged_fp8.restype = c_int
+    lib.mla_decode_paged_fp8.argtypes = [vp, vp, c_float] + decode_args[2:]
+    lib.mla_kvcache_append_fp8.restype = c_int
+    lib.mla_kvcache_append_fp8.argtypes = [vp, vp, c_float, vp, c_int, c_int, vp, c_int, c_int, c_int, c_int, vp, vp]
     lib.mla_check_inputs.restype = c_int
     lib.mla_check_inputs.argtypes = [vp, c_int, c_int, vp, c_int, vp, vp]
     lib.mla_set_debug_checks.restype = None
@@ -481,3 +485,65 @@ def stream_read(src: torch.Tensor, sink: Optional[torch.Tensor] = None) -> None:
         sink = torch.empty(4, dtype=torch.int32, device=device)
     _check("mla_stream_read", _load().mla_stream_read(src.data_ptr(), src.numel() * src.element_size(),
                                                       sink.data_ptr(), _stream_handle(device)))
+
+
+def kvcache_append_fp8(kv_new: torch.Tensor, kvcache_fp8: torch.Tensor, kv_scale: float, block_table: torch.Tensor,
+                       cache_seqlens: torch.Tensor, bad_rows: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """kvcache_append into an fp8 cache (uint8 codes [P][64][h_kv][576], OCP
+    E4M3 with one scale): each new value becomes the nearest code of
+    x / kv_scale clamped to +-448.  Returns kvcache_fp8."""
+    device = kvcache_fp8.device
+    _require(kv_new, "kv_new", torch.bfloat16, device)
+    _require(kvcache_fp8, "kvcache_fp8", torch.uint8, device)
+    _require(block_table, "block_table", torch.int32, device)
+    _require(cache_seqlens, "cache_seqlens", torch.int32, device)
+    if bad_rows is not None:
+        _require(bad_rows, "bad_rows", torch.int32, device)
+    if kv_new.dim() != 4 or kvcache_fp8.dim() != 4 or block_table.dim() != 2:
+        raise ValueError("kv_new must be [B][s_new][h_kv][576], kvcache_fp8 [P][64][h_kv][576], block_table [B][max_pages]")
+    B, s_new, h_kv, d = kv_new.shape
+    if kvcache_fp8.shape[1] != PAGE_SIZE or kvcache_fp8.shape[2] != h_kv or kvcache_fp8.shape[3] != d:
+        raise ValueError("kvcache_fp8 must be [P][64][h_kv][576] with the h_kv of kv_new")
+    if block_table.shape[0] != B or cache_seqlens.numel() != B:
+        raise ValueError("block_table / cache_seqlens batch does not match kv_new")
+    _check("mla_kvcache_append_fp8", _load().mla_kvcache_append_fp8(
+        kv_new.data_ptr(), kvcache_fp8.data_ptr(), float(kv_scale), block_table.data_ptr(), block_table.shape[1],
+        kvcache_fp8.shape[0], cache_seqlens.data_ptr(), B, s_new, h_kv, d,
+        bad_rows.data_ptr() if bad_rows is not None else None, _stream_handle(device)))
+    return kvcache_fp8
+
+
+def mla_decode_paged_fp8(q: torch.Tensor, kvcache_fp8: torch.Tensor, kv_scale: float, block_table: torch.Tensor,
+                         cache_seqlens: torch.Tensor, dv: int, tile_scheduler_metadata: torch.Tensor,
+                         num_splits: torch.Tensor, causal: bool = False, softmax_scale: Optional[float] = None,
+                         buffers: Optional[DecodeBuffers] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """mla_decode_paged over an fp8 cache (uint8 E4M3 codes [P][64][h_kv][576]
+    whose values are code * kv_scale); heads of up to 128 query rows."""
+    device = q.device
+    if device.type != "cuda":
+        raise ValueError("mla_decode_paged_fp8 runs on a GPU; q is on " + str(device))
+    _require(q, "q", torch.bfloat16, device)
+    _require(kvcache_fp8, "kvcache_fp8", torch.uint8, device)
+    for t, name in ((block_table, "block_table"), (cache_seqlens, "cache_seqlens"),
+                    (tile_scheduler_metadata, "tile_scheduler_metadata"), (num_splits, "num_splits")):
+        _require(t, name, torch.int32, device)
+    if q.dim() != 4 or kvcache_fp8.dim() != 4 or block_table.dim() != 2 or kvcache_fp8.shape[1] != PAGE_SIZE:
+        raise ValueError("q must be [B][s_q][h_q][576], kvcache_fp8 [P][64][h_kv][576], block_table [B][max_pages]")
+    if block_table.shape[0] != q.shape[0] or cache_seqlens.numel() != q.shape[0] or num_splits.numel() != q.shape[0] + 1:
+        raise ValueError("block_table / cache_seqlens / num_splits do not match the batch of q")
+    B, s_q, h_q, d_qk = q.shape
+    P, page, h_kv, _ = kvcache_fp8.shape
+    W = tile_scheduler_metadata.shape[0]
+    if buffers is None:
+        buffers = DecodeBuffers.__new__(DecodeBuffers)
+        buffers.o = torch.empty((B, s_q, h_q, dv), dtype=torch.bfloat16, device=device)
+        buffers.lse = torch.empty((B, h_q, s_q), dtype=torch.float32, device=device)
+        buffers.workspace = torch.empty(max(workspace_bytes(B, s_q, h_q, h_kv, dv, W), 256), dtype=torch.uint8,
+                                        device=device)
+    _check_buffers(buffers, B, s_q, h_q, h_kv, dv, W, device)
+    _check("mla_decode_paged_fp8", _load().mla_decode_paged_fp8(
+        q.data_ptr(), kvcache_fp8.data_ptr(), float(kv_scale), block_table.data_ptr(), block_table.shape[1], P,
+        cache_seqlens.data_ptr(), B, s_q, h_q, h_kv, d_qk, dv, tile_scheduler_metadata.data_ptr(),
+        num_splits.data_ptr(), W, int(bool(causal)), float(softmax_scale or 0.0), buffers.o.data_ptr(),
+        buffers.lse.data_ptr(), buffers.workspace.data_ptr(), buffers.workspace.numel(), _stream_handle(device)))
+    return buffers.o, buffers.lse

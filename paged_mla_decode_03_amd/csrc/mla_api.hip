@@ -131,6 +131,7 @@ mla::DecodeParams decode_params(const void* q, const void* kvcache, const int32_
   p.causal = causal;
   const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf(192.0f);
   p.scale_log2 = scale * 1.4426950408889634f;
+  p.out_scale = 1.0f;
   return p;
 }
 
@@ -146,10 +147,15 @@ void launch_one(Kernel kernel, int blocks, int threads, const mla::DecodeParams&
 }
 
 int launch_decode(const mla::DecodeParams& p, hipStream_t stream, hipEvent_t start = nullptr,
-                  hipEvent_t stop = nullptr) {
+                  hipEvent_t stop = nullptr, bool fp8 = false) {
   const int groups = p.num_workers * p.h_kv;
   const int blocks = (groups + mla::kNumXcd - 1) / mla::kNumXcd * mla::kNumXcd * p.row_blocks;
-  if (mla::rows_per_block(p.rows) == mla::kWideRows) {
+  if (fp8) {   // the fp8 cache runs the 64-row kernel (heads of up to 128 query rows)
+    if (p.h_kv == 1)
+      launch_one(mla::mla_decode_fp8_kernel<true>, blocks, mla::kThreads, p, stream, start, stop);
+    else
+      launch_one(mla::mla_decode_fp8_kernel<false>, blocks, mla::kThreads, p, stream, start, stop);
+  } else if (mla::rows_per_block(p.rows) == mla::kWideRows) {
     if (p.h_kv == 1)
       launch_one(mla::mla_decode_wide_kernel<true>, blocks, mla::kWideThreads, p, stream, start, stop);
     else
@@ -423,6 +429,53 @@ int mla_decode_paged_noalloc(const void* q, const void* kvcache, const int32_t* 
   st = launch_decode(p, (hipStream_t)stream);
   if (st != MLA_OK) return st;
   return launch_combine(p, (hipStream_t)stream);
+}
+
+int mla_decode_paged_fp8(const void* q, const void* kvcache_fp8, float kv_scale, const int32_t* block_table,
+                         int max_pages_per_seq, int num_pages, const int32_t* cache_seqlens, int batch, int s_q,
+                         int h_q, int h_kv, int d_qk, int dv, const int32_t* meta, const int32_t* num_splits,
+                         int num_workers, int causal, float softmax_scale, void* o, float* lse, void* workspace,
+                         size_t workspace_bytes_given, void* stream) {
+  Shape s;
+  int st = check_decode(q, kvcache_fp8, block_table, max_pages_per_seq, num_pages, cache_seqlens, batch, s_q, h_q,
+                        h_kv, d_qk, dv, meta, num_splits, num_workers, causal, o, lse, workspace,
+                        workspace_bytes_given, &s);
+  if (st != MLA_OK) return st;
+  if (!(kv_scale > 0.f) || !(kv_scale < 3.0e38f)) return MLA_ERR_INVALID_ARG;
+  if (mla::rows_per_block(s.rows) != mla::kRowsPerBlock) return MLA_ERR_UNSUPPORTED;
+  mla::DecodeParams p = decode_params(q, kvcache_fp8, block_table, max_pages_per_seq, num_pages, cache_seqlens, s, meta,
+                                      num_splits, num_workers, causal, softmax_scale, o, lse, workspace);
+  p.scale_log2 *= kv_scale;
+  p.out_scale = kv_scale;
+  if (debug_checks_on() && (st = debug_check_tables(p, num_pages, (hipStream_t)stream)) != MLA_OK) return st;
+  st = launch_decode(p, (hipStream_t)stream, nullptr, nullptr, true);
+  if (st != MLA_OK) return st;
+  return launch_combine(p, (hipStream_t)stream);
+}
+
+int mla_kvcache_append_fp8(const void* kv_new, void* kvcache_fp8, float kv_scale, const int32_t* block_table,
+                           int max_pages_per_seq, int num_pages, const int32_t* cache_seqlens, int batch, int s_new,
+                           int h_kv, int d_qk, int32_t* bad_rows, void* stream) {
+  const int st = check_append(kv_new, kvcache_fp8, block_table, max_pages_per_seq, num_pages, cache_seqlens, batch,
+                              s_new, h_kv, d_qk, bad_rows);
+  if (st != MLA_OK) return st;
+  if (!(kv_scale > 0.f) || !(kv_scale < 3.0e38f)) return MLA_ERR_INVALID_ARG;
+  mla::AppendParams p;
+  p.kv_new = (const uint16_t*)kv_new;
+  p.kv = kvcache_fp8;
+  p.block_table = block_table;
+  p.seqlens = cache_seqlens;
+  p.bad_rows = bad_rows;
+  p.inv_scale = 1.0f / kv_scale;
+  p.batch = batch;
+  p.s_new = s_new;
+  p.h_kv = h_kv;
+  p.max_pages = max_pages_per_seq;
+  p.num_pages = num_pages;
+  p.chunks = batch * s_new * h_kv * mla::kChunksPerRow;
+  const int blocks = (p.chunks + mla::kAppendThreads - 1) / mla::kAppendThreads;
+  hipLaunchKernelGGL(mla::mla_append_fp8_kernel, dim3(blocks), dim3(mla::kAppendThreads), 0, (hipStream_t)stream, p);
+  return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
 
 int mla_check_inputs(const int32_t* block_table, int max_pages_per_seq, int num_pages,

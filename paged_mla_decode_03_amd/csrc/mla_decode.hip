@@ -105,7 +105,16 @@ struct DecodeShared {
 // One role's loop over the worker's segments.  Both roles run the same
 // sequence of steps and barriers; each is compiled on its own so that the
 // score waves' Q and the output waves' accumulators never share registers.
-template <bool kSingleHead, bool scorer>
+//
+// kFp8: the cache holds fp8 codes (OCP E4M3, one fp32 scale for the cache).
+// A half page then moves HBM -> registers (each lane loads 8-byte chunks of
+// 8 codes, the same chunks every time: 5 per lane in the score waves, 4 in
+// the output waves, 2304 per half page) one step before it is needed, and in
+// the next step it is converted, exactly, to bf16 and written into its ring
+// slot in the same swizzled layout the DMAs fill, so the scores, softmax and
+// outputs are unchanged.  The cache's scale is folded into the score scale
+// and the output normaliser (p.scale_log2 and p.out_scale).
+template <bool kSingleHead, bool scorer, bool kFp8>
 __device__ __forceinline__ void decode_role(const DecodeParams& p, DecodeShared& sh, const int32_t* meta, int g, int rb) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -119,10 +128,12 @@ __device__ __forceinline__ void decode_role(const DecodeParams& p, DecodeShared&
   if (cpage >= cend) return;
   const int nrb = p.row_blocks;
 
-  const int row_stride_bytes = kSingleHead ? kRowBytes : p.h_kv * kRowBytes;
+  constexpr int kElemBytes = kFp8 ? 1 : 2;              // bytes per cached value
+  constexpr int kRowBytesIn = kDqk * kElemBytes;          // one latent row of one head in the cache
+  const int row_stride_bytes = kSingleHead ? kRowBytesIn : p.h_kv * kRowBytesIn;
   const size_t page_stride_bytes = (size_t)kPage * row_stride_bytes;
   const uint32_t page_span = (uint32_t)(kPage * row_stride_bytes);
-  const char* kv_head = (const char*)p.kv + (size_t)g * kRowBytes;
+  const char* kv_head = (const char*)p.kv + (size_t)g * kRowBytesIn;
   const uint32_t lane_src_off = (lane >> 3) * row_stride_bytes + ((lane & 7) ^ (lane >> 3)) * 16;
   const uint32_t ring_base = (uint32_t)(uintptr_t)&sh.ring[0][0];
   const uint32_t p_base = (uint32_t)(uintptr_t)&sh.p[0][0];
@@ -160,10 +171,75 @@ __device__ __forceinline__ void decode_role(const DecodeParams& p, DecodeShared&
   // End of a step: wait for this wave's share of the half page the score
   // waves read next (all but the DMAs just issued, if any).
   auto wait_next = [&](bool issued) __attribute__((always_inline)) {
+    if constexpr (kFp8) return;   // plain loads: the compiler waits for them where they are used
     if (issued)
       wait_dma_keep<kDma>();
     else
       wait_dma_all();
+  };
+
+  // fp8 staging: this lane's chunks c = tid + 512 i (i < kF8Chunks) of a half
+  // page, chunk c = 8 codes of row c / 72 at byte 8 * (c % 72) of that row.
+  constexpr int kF8Chunks = scorer ? 5 : 4;
+  static_assert(kThreads * 4 + kThreads / 2 == kHalfRows * (kDqk / 8), "every chunk: 5 per score lane, 4 per output lane");
+  uint32_t f8[kF8Chunks][2];
+  int f8_idx = -1;   // global half-page index whose chunks f8 holds (-1: none)
+  auto load_half = [&]() __attribute__((always_inline)) {
+    if (!lvalid) return false;
+    const bool ok = (unsigned)lpid < (unsigned)p.num_pages;   // a bad page id reads as zeros
+    const char* base = kv_head + (ok ? (size_t)lpid * page_stride_bytes : (size_t)0) +
+                       (size_t)(kHalfRows * lhalf) * row_stride_bytes;
+#pragma unroll
+    for (int i = 0; i < kF8Chunks; ++i) {
+      const int c = tid + kThreads * i;
+      const int r = c / kChunksPerRow, q = c - (c / kChunksPerRow) * kChunksPerRow;
+      const uint2 v = ok ? *(const uint2*)(base + (size_t)r * row_stride_bytes + q * 8) : uint2{0u, 0u};
+      f8[i][0] = v.x;
+      f8[i][1] = v.y;
+    }
+    f8_idx = gq;
+    ++gq;
+    if (lhalf == 0) {
+      lhalf = 1;
+    } else {
+      lhalf = 0;
+      lvalid = next_page(meta, p.seqlens, lb, lpage, lend, lp0);
+      if (lvalid) lpid = page_id(p, lb, page_in_order(lpage, lp0, lend, rb, nrb));
+    }
+    return true;
+  };
+  // Codes -> bf16 (exact: every E4M3 value is a bf16 value) into the ring
+  // slot of half page f8_idx.
+  auto convert_half = [&]() __attribute__((always_inline)) {
+    char* half = &sh.ring[f8_idx & (kRingSlots - 1)][0];
+#pragma unroll
+    for (int i = 0; i < kF8Chunks; ++i) {
+      const int c = tid + kThreads * i;
+      const int r = c / kChunksPerRow, q = c - (c / kChunksPerRow) * kChunksPerRow;
+      u32x4 o;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        typedef float f32x2 __attribute__((ext_vector_type(2)));
+        const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)f8[i][h], false);
+        const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)f8[i][h], true);
+        o[2 * h] = pack_bf16x2(lo[0], lo[1]);
+        o[2 * h + 1] = pack_bf16x2(hi[0], hi[1]);
+      }
+      *(u32x4*)(half + lds_tile_offset(r, q)) = o;
+    }
+    f8_idx = -1;
+  };
+  // One step's staging: bf16 issues its DMAs of half page gbase+k+3; fp8
+  // converts half page gbase+k+2 (loaded in the previous step) and loads
+  // half page gbase+k+3.  Returns whether DMAs were issued.
+  auto stage_step = [&](int target) __attribute__((always_inline)) {
+    if constexpr (kFp8) {
+      if (f8_idx == target - 1) convert_half();
+      if (gq == target) load_half();
+      return false;
+    } else {
+      return gq == target && issue_half();
+    }
   };
 
   // Score waves: per-lane offsets.  K: row col (+16 per key tile), 16-byte
@@ -190,8 +266,13 @@ __device__ __forceinline__ void decode_role(const DecodeParams& p, DecodeShared&
     return qrow < p.rows ? g * p.group + (qrow - (qrow / p.group) * p.group) : 0;
   };
 
-  // Prologue of the worker: half pages 0 and 1 in flight, wait for 0.
-  {
+  // Prologue of the worker: half pages 0 and 1 in flight, wait for 0 (fp8:
+  // half page 0 converted, half page 1 in registers).
+  if constexpr (kFp8) {
+    load_half();
+    convert_half();
+    load_half();
+  } else {
     issue_half();
     const bool issued = issue_half();
     wait_next(issued);
@@ -338,7 +419,7 @@ __device__ __forceinline__ void decode_role(const DecodeParams& p, DecodeShared&
           }
           // This wave's share of half page gbase+k+3, then wait for its share
           // of half page gbase+k+2 (see the output waves).
-          const bool issued = gq == gbase + k + 3 && issue_half();
+          const bool issued = stage_step(gbase + k + 3);
           wait_next(issued);
         } else {
           // ---- output waves: DMAs of half page gbase+k+3, outputs of half page k ----
@@ -346,7 +427,7 @@ __device__ __forceinline__ void decode_role(const DecodeParams& p, DecodeShared&
           // segment's half page gbase+2: a step issues only when the load
           // cursor stands at gbase+k+3, so the ring slot it fills, that of
           // half page k-1, is free.)
-          const bool issued = gq == gbase + k + 3 && issue_half();
+          const bool issued = stage_step(gbase + k + 3);
           if (k >= 0) {
             const uint32_t half_base = ring_base + (uint32_t)(((gbase + k) & (kRingSlots - 1)) * kHalfBytes);
             uint32_t vb[4];
@@ -424,9 +505,16 @@ __device__ __forceinline__ void decode_role(const DecodeParams& p, DecodeShared&
         lvalid = true;
         gq = gbase;
         lpid = page_id(p, lb, page_in_order(lpage, lp0, lend, rb, nrb));
-        issue_half();
-        const bool issued = issue_half();
-        wait_next(issued);
+        if constexpr (kFp8) {
+          f8_idx = -1;   // drop what was loaded ahead; the pass reloads from its start
+          load_half();
+          convert_half();
+          load_half();
+        } else {
+          issue_half();
+          const bool issued = issue_half();
+          wait_next(issued);
+        }
       }
     }
 
@@ -438,7 +526,7 @@ __device__ __forceinline__ void decode_role(const DecodeParams& p, DecodeShared&
         const int r = 16 * t + col;
         const int qrow = rb * kRowsPerBlock + r;
         const float l = sh.l[r];
-        const float inv = l == 0.f ? 0.f : 1.f / l;
+        const float inv = l == 0.f ? 0.f : p.out_scale / l;
         if (qrow < p.rows) {
           if (nsplit == 1) {
             uint16_t* op = p.o + ((size_t)(b * p.s_q + row_tok(r)) * p.h_q + row_head(r)) * kDv + 128 * ow + 4 * grp4;
@@ -486,12 +574,32 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(DecodeParams p)
   const int g = grp - worker * p.h_kv;
   const int32_t* meta = p.meta + (size_t)worker * kMetaInts;
   if (__builtin_amdgcn_readfirstlane(threadIdx.x >> 6) < 4)
-    decode_role<kSingleHead, true>(p, sh, meta, g, rb);
+    decode_role<kSingleHead, true, false>(p, sh, meta, g, rb);
   else
-    decode_role<kSingleHead, false>(p, sh, meta, g, rb);
+    decode_role<kSingleHead, false, false>(p, sh, meta, g, rb);
+}
+
+// The same kernel over an fp8 cache (see decode_role's kFp8).
+template <bool kSingleHead>
+__global__ __launch_bounds__(kThreads, 1) void mla_decode_fp8_kernel(DecodeParams p) {
+  __shared__ __attribute__((aligned(1024))) DecodeShared sh;
+  const int xcd = blockIdx.x % kNumXcd;
+  const int k = blockIdx.x / kNumXcd;
+  const int rb = k % p.row_blocks;
+  const int grp = (k / p.row_blocks) * kNumXcd + xcd;
+  if (grp >= p.num_workers * p.h_kv) return;
+  const int worker = grp / p.h_kv;
+  const int g = grp - worker * p.h_kv;
+  const int32_t* meta = p.meta + (size_t)worker * kMetaInts;
+  if (__builtin_amdgcn_readfirstlane(threadIdx.x >> 6) < 4)
+    decode_role<kSingleHead, true, true>(p, sh, meta, g, rb);
+  else
+    decode_role<kSingleHead, false, true>(p, sh, meta, g, rb);
 }
 
 template __global__ void mla_decode_kernel<true>(DecodeParams p);
 template __global__ void mla_decode_kernel<false>(DecodeParams p);
+template __global__ void mla_decode_fp8_kernel<true>(DecodeParams p);
+template __global__ void mla_decode_fp8_kernel<false>(DecodeParams p);
 
 }  // namespace mla

@@ -56,7 +56,8 @@ struct DecodeParams {
   int num_workers;
   int row_blocks;               // ceil(R / rows_per_block(R))
   int causal;
-  float scale_log2;             // softmax scale * log2(e)
+  float scale_log2;             // softmax scale * log2(e) (fp8 cache: times the cache's scale)
+  float out_scale;              // factor on the normalised outputs: 1, or the fp8 cache's scale
 };
 
 struct CombineParams {
@@ -100,6 +101,8 @@ struct CheckParams {
 
 template <bool kSingleHead>
 __global__ void mla_decode_kernel(DecodeParams p);
+template <bool kSingleHead>
+__global__ void mla_decode_fp8_kernel(DecodeParams p);
 template <bool kSingleHead>
 __global__ void mla_decode_wide_kernel(DecodeParams p);
 

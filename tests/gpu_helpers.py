@@ -11,7 +11,7 @@ from __future__ import annotations
 import numpy as np
 import torch
 
-from oracle.mla_oracle import mla_decode_ref
+from oracle.mla_oracle import fp8_e4m3_encode_ref, mla_decode_ref
 from paged_mla_decode_03_amd import get_mla_metadata, mla_decode_paged
 
 MAX_ABS_O = 1e-2
@@ -94,3 +94,16 @@ def compare(o, lse, O, LSE, batch_subset=None, scale=1.0, label=""):
     assert stats["mean_o"] <= MEAN_ABS_O * scale, f"{label}: {stats}"
     assert stats["max_lse"] <= MAX_ABS_LSE, f"{label}: {stats}"
     return stats
+
+
+def oracle_fp8_codes(latents, kv_scale):
+    """The oracle's E4M3 codes of latents / kv_scale (the product in fp32, as
+    a quantising append forms it), in chunks: the cache inputs of the fp8
+    decode tests."""
+    x = latents.float().numpy().reshape(-1)
+    inv = np.float32(1.0) / np.float32(kv_scale)
+    out = np.empty(x.size, dtype=np.uint8)
+    step = 1 << 24
+    for s in range(0, x.size, step):
+        out[s:s + step] = fp8_e4m3_encode_ref((x[s:s + step] * inv).astype(np.float32))
+    return out.reshape(tuple(latents.shape))

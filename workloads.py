@@ -215,3 +215,44 @@ def algorithmic_counts(w: Workload, seqlens: np.ndarray, max_pages_per_seq: int)
     flops = 2 * vis * w.h_q * (w.d_qk + w.d_v)
     return dict(kv_bytes=kv_bytes, total_bytes=kv_bytes + q_bytes + o_bytes + lse_bytes + table_bytes,
                 flops=flops, visible_pairs_per_head=vis)
+
+
+# fp8 cache inputs: one byte per cached value (OCP FP8 E4M3 codes) and one
+# scale for the whole cache.  The cache holds what a quantising append leaves
+# for the workload's N(0, 1) latents: with the scale 1/64 a latent of
+# magnitude up to 7 maps into the format's range (+-448), so the codes of
+# normal data are never clamped and sit in the format's upper binades, as a
+# scale fitted to the latents' range puts them.
+FP8_KV_SCALE = 1.0 / 64.0
+
+
+def make_fp8_inputs(w: Workload | str, seed: int = 0, *, encode, seqlens=None, poison: bool = False,
+                    extra_pages: int = 0) -> DecodeInputs:
+    """A decode step over an fp8 cache: the lengths, block table, q and bf16
+    latents of :func:`make_inputs` (same draws), with the cache replaced by
+    ``encode(latents, kv_scale)``: the caller's quantiser, returning uint8
+    codes [P][64][h_kv][576] of latents / kv_scale.  ``poison`` puts the NaN
+    code 0x7F into every slot no sequence may read.  The scale is in
+    ``extra["kv_scale"]``."""
+    if isinstance(w, str):
+        w = WORKLOADS[w]
+    base = make_inputs(w, seed, seqlens=seqlens, extra_pages=extra_pages)
+    shape = tuple(base.kvcache.shape)
+    codes = np.ascontiguousarray(np.asarray(encode(base.kvcache, FP8_KV_SCALE), dtype=np.uint8))
+    if codes.shape != shape:
+        raise ValueError(f"encoder returned shape {codes.shape}, expected {shape}")
+    if poison:
+        L = base.cache_seqlens.numpy()
+        bt = base.block_table.numpy()
+        referenced = np.zeros(shape[0], dtype=bool)
+        for b in range(len(L)):
+            npg = (int(L[b]) + PAGE_SIZE - 1) // PAGE_SIZE
+            pages = bt[b, :npg]
+            referenced[pages] = True
+            tail = int(L[b]) % PAGE_SIZE
+            if npg > 0 and tail:
+                codes[int(pages[-1]), tail:] = 0x7F
+        codes[~referenced] = 0x7F
+    base.kvcache = torch.from_numpy(codes)
+    base.extra["kv_scale"] = FP8_KV_SCALE
+    return base
