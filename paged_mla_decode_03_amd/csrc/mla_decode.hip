@@ -411,7 +411,7 @@ __device__ __forceinline__ void decode_role(const DecodeParams& p, DecodeShared&
                 const float w1 = __builtin_amdgcn_exp2f(__builtin_fmaf(x[i][2 * h + 1], p.scale_log2, -mu));
                 l_run += w0 + w1;
                 pk[i][h] = pack_bf16x2(w0, w1);
-                l_bf += sum_bf16x2(pk[i][h]);
+                l_bf = add_bf16x2(l_bf, pk[i][h]);
               }
             // Slot 8*grp4 + 4*i + e holds key 16i + 4*grp4 + e of the half page.
             *(__attribute__((address_space(3))) u32x4*)(p_base + (uint32_t)((hp & 1) * kPBytes) + pw_off) =

@@ -153,14 +153,18 @@ __device__ inline uint32_t pack_bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){a, b}, bf16x2));
 }
 
-// Sum of the two bf16 values packed by pack_bf16x2, in fp32 (exact).  Each
-// row keeps two sums: the exact one, for its log-sum-exp, and one over the
+// acc + the two bf16 values packed by pack_bf16x2, in fp32: one
+// v_dot2c_f32_bf16 against (1, 1) (on this chip vector ALU cycles add to
+// the matrix core's, so the sum takes one instruction, not four).  Each row
+// keeps two sums: the exact one, for its log-sum-exp, and one over the
 // rounded weights that the PV product actually uses, which normalises O, so
 // that each output row is a convex combination of cached values: the
 // rounding of a weight then moves O only by that weight's share of
 // (v_j - O), never by a mismatch between the weights and their sum.
-__device__ inline float sum_bf16x2(uint32_t packed) {
-  return __builtin_bit_cast(float, packed << 16) + __builtin_bit_cast(float, packed & 0xFFFF0000u);
+__device__ inline float add_bf16x2(float acc, uint32_t packed) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, packed), __builtin_bit_cast(bf16x2, 0x3F803F80u),
+                                          acc, false);
 }
 
 // Physical page of logical block j of sequence b.  A block past the end of
@@ -202,9 +206,16 @@ __device__ inline bool next_page(const int32_t* meta, const int32_t* seqlens, in
 // every block fetches a different page, and a page is fetched from memory by
 // one block and found in L2 by the others.  A last, partial group keeps its
 // order.  The result does not otherwise depend on the order.
+// Two row blocks (128 query rows per latent head) are the common case and
+// take shifts and masks instead of a division.
 __device__ inline int page_in_order(int page, int p0, int end, int rb, int nrb) {
   const int j = page - p0 - 1;
   if (j < 0 || nrb == 1) return page;
+  if (nrb == 2) {
+    const int base = p0 + 1 + (j & ~1);
+    if (base + 2 > end) return page;
+    return base + ((j & 1) ^ rb);
+  }
   const int base = p0 + 1 + (j / nrb) * nrb;
   if (base + nrb > end) return page;
   const int r = j - (j / nrb) * nrb + rb;

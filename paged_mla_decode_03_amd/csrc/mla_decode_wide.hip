@@ -227,8 +227,11 @@ __device__ __forceinline__ void wide_worker(const DecodeParams& p, char (*lds_pa
           zero_tail_rows<kWideThreads>(buf, valid, tid);
           __syncthreads();
         }
-        const bool dma = lvalid;
-        const __amdgpu_buffer_rsrc_t dma_rsrc = page_rsrc(kv_head, next_pid, p.num_pages, page_stride_bytes, page_span);
+        // The next page's DMAs go out in every step, so that the score stream
+        // holds no branch: with no page left they read from a resource of
+        // size 0 and write zeros into the free buffer.
+        const __amdgpu_buffer_rsrc_t dma_rsrc =
+            page_rsrc(kv_head, lvalid ? next_pid : -1, p.num_pages, page_stride_bytes, page_span);
         const uint32_t dma_dst = lds_base + ((it + 1) & 1) * kPageBytes;
 
         const uint32_t page_base = (uint32_t)(uintptr_t)buf;
@@ -275,7 +278,7 @@ __device__ __forceinline__ void wide_worker(const DecodeParams& p, char (*lds_pa
         static_assert(kDmaStart + kDmaEvery * (kWideDmaPerWave - 1) < kQk, "every DMA inside the score stream");
         auto dma_step = [&]<int G>() __attribute__((always_inline)) {
           if constexpr (G >= kDmaStart && (G - kDmaStart) % kDmaEvery == 0 && (G - kDmaStart) / kDmaEvery < kWideDmaPerWave) {
-            if (dma) stage_tile<kWideDmaPerWave>(dma_rsrc, lane_src_off, row_stride_bytes, dma_dst, wave, (G - kDmaStart) / kDmaEvery);
+            stage_tile<kWideDmaPerWave>(dma_rsrc, lane_src_off, row_stride_bytes, dma_dst, wave, (G - kDmaStart) / kDmaEvery);
           }
         };
         f32x4 s[4][2];
@@ -357,7 +360,7 @@ __device__ __forceinline__ void wide_worker(const DecodeParams& p, char (*lds_pa
                 const float w1 = __builtin_amdgcn_exp2f(__builtin_fmaf(x[2 * kk + i][2 * h + 1], p.scale_log2, -mu));
                 l_run[j] += w0 + w1;
                 pk[i][h] = pack_bf16x2(w0, w1);
-                l_bf[j] += sum_bf16x2(pk[i][h]);
+                l_bf[j] = add_bf16x2(l_bf[j], pk[i][h]);
               }
             // Slot 8*grp4 + 4*i + e of k-step kk holds key 32kk + 16i + 4*grp4 + e.
             *(__attribute__((address_space(3))) u32x4*)(pr_off[kk] + pw_base + (uint32_t)(j * 16 * kWidePRowBytes)) =
@@ -485,6 +488,9 @@ __device__ __forceinline__ void wide_worker(const DecodeParams& p, char (*lds_pa
     cpage = np;
     cend = ne;
   }
+  // The last page step issued DMAs (of zeros) into the free buffer: they
+  // land before the workgroup gives its LDS back.
+  wait_dma_all();
 }
 
 template <bool kSingleHead>
