@@ -12,9 +12,9 @@ from workloads import WORKLOADS, Workload, make_inputs
 pytestmark = pytest.mark.gpu
 
 
-TINY_SKIP = ("kept off the GPU: with the earlier decode kernel this input faulted the GPU twice; "
-             "that kernel is replaced, and this case returns once the replacement has passed "
-             "every other GPU test")
+TINY_SKIP = ("kept off the GPU: this input faulted the GPU twice with an earlier decode kernel, and the "
+             "cause of the second fault has not been shown; the case returns once that cause is shown "
+             "on the CPU")
 
 
 @pytest.mark.skip(reason=TINY_SKIP)
@@ -117,11 +117,14 @@ def _sample(inp, k, rng):
     return sorted(picks)
 
 
-@pytest.mark.parametrize("name,k", [("mem_bound", 3), ("var_len", 4), ("causal_sq2", 2), ("skewed", 3)])
-def test_full_size_workloads(name, k):
-    inp = make_inputs(name, 0)
+@pytest.mark.parametrize("name,k,seed", [("mem_bound", 3, 0), ("var_len", 4, 0), ("causal_sq2", 2, 0), ("skewed", 3, 0),
+                                         ("var_len", 4, 1), ("var_len", 4, 2), ("skewed", 3, 1), ("skewed", 3, 2)])
+def test_full_size_workloads(name, k, seed):
+    """Seeds 1 and 2 redraw the random lengths of var_len and skewed (and
+    every input value)."""
+    inp = make_inputs(name, seed)
     o, lse, _, ns = run_gpu(inp)
-    subset = _sample(inp, k, np.random.default_rng(1))
+    subset = _sample(inp, k, np.random.default_rng(1 + seed))
     O, LSE = oracle(inp, batch_subset=subset)
-    stats = compare(o, lse, O, LSE, batch_subset=subset, label=name)
-    print(name, "splits per sequence:", np.diff(ns).max(), stats)
+    stats = compare(o, lse, O, LSE, batch_subset=subset, label=f"{name} seed {seed}")
+    print(name, seed, "splits per sequence:", np.diff(ns).max(), stats)
