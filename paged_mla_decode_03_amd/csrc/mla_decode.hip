@@ -62,6 +62,8 @@ namespace {
 constexpr int kHalfRows = 32;                         // keys per half page
 constexpr int kHalfBytes = kHalfRows * kRowBytes;     // 36864 bytes per ring slot
 constexpr int kRingSlots = 4;
+constexpr int kRawHalfBytes = kHalfRows * kDqk;       // a half page of fp8 codes: 18432 bytes
+constexpr int kRawUnits = kRawHalfBytes / 1024;       // 18 wave-wide 1 KB DMAs
 constexpr int kPRowBytes = 2 * kHalfRows;           // one row of P: 32 bf16
 constexpr int kPBytes = kRowsPerBlock * kPRowBytes;   // 4 KB per P buffer
 // A half page is 36 wave-wide DMAs: tile row r (rows 8r..8r+7) x 9 tile
@@ -95,12 +97,27 @@ __device__ inline void wait_dma_keep() {
 
 }  // namespace
 
+// bf16 cache: a ring of four half-page slots.  fp8 cache: three bf16 slots
+// (each half page is converted into one a step before its first reader,
+// into the slot its predecessor's predecessor has left) and two slots of raw
+// fp8 codes that the DMAs fill a step ahead of the conversion.  Both fill
+// the same 155,920 bytes.
+template <bool kFp8>
 struct DecodeShared {
   char ring[kRingSlots][kHalfBytes];
   char p[2][kPBytes];
   float l[kRowsPerBlock];           // row sums at the end of a segment
   int flags[4];                     // overflow votes of the score waves
 };
+template <>
+struct DecodeShared<true> {
+  char ring[kRingSlots - 1][kHalfBytes];
+  char raw[2][kRawHalfBytes];
+  char p[2][kPBytes];
+  float l[kRowsPerBlock];
+  int flags[4];
+};
+static_assert(sizeof(DecodeShared<true>) == sizeof(DecodeShared<false>), "same LDS for both caches");
 
 // One role's loop over the worker's segments.  Both roles run the same
 // sequence of steps and barriers; each is compiled on its own so that the
@@ -115,7 +132,8 @@ struct DecodeShared {
 // outputs are unchanged.  The cache's scale is folded into the score scale
 // and the output normaliser (p.scale_log2 and p.out_scale).
 template <bool kSingleHead, bool scorer, bool kFp8>
-__device__ __forceinline__ void decode_role(const DecodeParams& p, DecodeShared& sh, const int32_t* meta, int g, int rb) {
+__device__ __forceinline__ void decode_role(const DecodeParams& p, DecodeShared<kFp8>& sh, const int32_t* meta, int g,
+                                            int rb) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
@@ -136,6 +154,8 @@ __device__ __forceinline__ void decode_role(const DecodeParams& p, DecodeShared&
   const char* kv_head = (const char*)p.kv + (size_t)g * kRowBytesIn;
   const uint32_t lane_src_off = (lane >> 3) * row_stride_bytes + ((lane & 7) ^ (lane >> 3)) * 16;
   const uint32_t ring_base = (uint32_t)(uintptr_t)&sh.ring[0][0];
+  // Ring slot of global half page i (i >= 0).
+  auto ring_slot = [](int i) __attribute__((always_inline)) { return kFp8 ? i % (kRingSlots - 1) : i & (kRingSlots - 1); };
   const uint32_t p_base = (uint32_t)(uintptr_t)&sh.p[0][0];
 
   // Load cursor over half pages (each wave keeps its own copy and issues its
@@ -154,7 +174,7 @@ __device__ __forceinline__ void decode_role(const DecodeParams& p, DecodeShared&
     if (!lvalid) return false;
     const __amdgpu_buffer_rsrc_t rsrc = page_rsrc(kv_head, lpid, p.num_pages, page_stride_bytes, page_span);
     const uint32_t dst =
-        ring_base + (uint32_t)((gq & (kRingSlots - 1)) * kHalfBytes) + (uint32_t)((trow * 9 + kCol0) * 1024);
+        ring_base + (uint32_t)(ring_slot(gq) * kHalfBytes) + (uint32_t)((trow * 9 + kCol0) * 1024);
     const int soff0 = (kHalfRows * lhalf + 8 * trow) * row_stride_bytes + kCol0 * 128;
 #pragma unroll
     for (int j = 0; j < kDma; ++j) lds_dma16(dst + (uint32_t)(j * 1024), lane_src_off, rsrc, (uint32_t)(soff0 + j * 128));
@@ -178,25 +198,39 @@ __device__ __forceinline__ void decode_role(const DecodeParams& p, DecodeShared&
       wait_dma_all();
   };
 
-  // fp8 staging: this lane's chunks c = tid + 512 i (i < kF8Chunks) of a half
-  // page, chunk c = 8 codes of row c / 72 at byte 8 * (c % 72) of that row.
-  constexpr int kF8Chunks = scorer ? 5 : 4;
-  static_assert(kThreads * 4 + kThreads / 2 == kHalfRows * (kDqk / 8), "every chunk: 5 per score lane, 4 per output lane");
-  uint32_t f8[kF8Chunks][2];
-  int f8_idx = -1;   // global half-page index whose chunks f8 holds (-1: none)
+  // fp8 staging.  A half page of codes is 18 wave-wide DMAs of 1 KB, unit u
+  // = bytes 1024u .. +1023 of its 32 x 576 codes in row order, landing at the
+  // same offset of a raw slot; this wave issues units s, s + 8 (and s + 16)
+  // for s = (wave + 4) % 8 (the output waves 4 and 5 take the last two), and
+  // in the next step each lane converts the 16 codes its own DMAs brought --
+  // so only the wave's own DMAs are waited for, and no barrier -- exactly to
+  // bf16 and writes them into the half page's ring slot in the swizzled
+  // layout the bf16 DMAs fill.
+  constexpr int kUnits = scorer ? 2 : 3;
+  const int unit0 = (wave + 4) & 7;
+  const int units = unit0 + 16 < kRawUnits ? 3 : 2;       // 3 for waves 4 and 5
+  uint32_t raw_base = 0;
+  uint32_t raw_voff[kUnits], raw_t0[kUnits], raw_t1[kUnits];
+  if constexpr (kFp8) {
+    raw_base = (uint32_t)(uintptr_t)&sh.raw[0][0];
+#pragma unroll
+    for (int i = 0; i < kUnits; ++i) {
+      const int b = 1024 * (unit0 + 8 * i) + 16 * lane;    // code index in the half page
+      const int r = b / kDqk, c = b - (b / kDqk) * kDqk;   // row and first column (a multiple of 16)
+      raw_voff[i] = (uint32_t)(r * row_stride_bytes + c);
+      raw_t0[i] = (uint32_t)lds_tile_offset(r, c / 8);
+      raw_t1[i] = (uint32_t)lds_tile_offset(r, c / 8 + 1);
+    }
+  }
+  int f8_idx = -1;   // global half-page index whose codes wait in a raw slot (-1: none)
   auto load_half = [&]() __attribute__((always_inline)) {
     if (!lvalid) return false;
-    const bool ok = (unsigned)lpid < (unsigned)p.num_pages;   // a bad page id reads as zeros
-    const char* base = kv_head + (ok ? (size_t)lpid * page_stride_bytes : (size_t)0) +
-                       (size_t)(kHalfRows * lhalf) * row_stride_bytes;
+    const __amdgpu_buffer_rsrc_t rsrc = page_rsrc(kv_head, lpid, p.num_pages, page_stride_bytes, page_span);
+    const uint32_t soff = (uint32_t)(kHalfRows * lhalf * row_stride_bytes);
+    const uint32_t dst = raw_base + (uint32_t)((gq & 1) * kRawHalfBytes) + (uint32_t)(unit0 * 1024);
 #pragma unroll
-    for (int i = 0; i < kF8Chunks; ++i) {
-      const int c = tid + kThreads * i;
-      const int r = c / kChunksPerRow, q = c - (c / kChunksPerRow) * kChunksPerRow;
-      const uint2 v = ok ? *(const uint2*)(base + (size_t)r * row_stride_bytes + q * 8) : uint2{0u, 0u};
-      f8[i][0] = v.x;
-      f8[i][1] = v.y;
-    }
+    for (int i = 0; i < kUnits; ++i)
+      if (i < 2 || units == 3) lds_dma16(dst + (uint32_t)(i * 8 * 1024), raw_voff[i], rsrc, soff);
     f8_idx = gq;
     ++gq;
     if (lhalf == 0) {
@@ -208,24 +242,28 @@ __device__ __forceinline__ void decode_role(const DecodeParams& p, DecodeShared&
     }
     return true;
   };
-  // Codes -> bf16 (exact: every E4M3 value is a bf16 value) into the ring
-  // slot of half page f8_idx.
+  // Codes of half page f8_idx -> bf16 (exact: every E4M3 value is a bf16
+  // value) into its ring slot, after this wave's own DMAs of it have landed.
   auto convert_half = [&]() __attribute__((always_inline)) {
-    char* half = &sh.ring[f8_idx & (kRingSlots - 1)][0];
+    wait_dma_all();
+    const uint32_t raw = raw_base + (uint32_t)((f8_idx & 1) * kRawHalfBytes) + (uint32_t)(unit0 * 1024 + 16 * lane);
+    char* half = &sh.ring[ring_slot(f8_idx)][0];
 #pragma unroll
-    for (int i = 0; i < kF8Chunks; ++i) {
-      const int c = tid + kThreads * i;
-      const int r = c / kChunksPerRow, q = c - (c / kChunksPerRow) * kChunksPerRow;
-      u32x4 o;
+    for (int i = 0; i < kUnits; ++i) {
+      if (i < 2 || units == 3) {
+        const u32x4 codes = *(const __attribute__((address_space(3))) u32x4*)(raw + (uint32_t)(i * 8 * 1024));
+        u32x4 o[2];
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        typedef float f32x2 __attribute__((ext_vector_type(2)));
-        const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)f8[i][h], false);
-        const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)f8[i][h], true);
-        o[2 * h] = pack_bf16x2(lo[0], lo[1]);
-        o[2 * h + 1] = pack_bf16x2(hi[0], hi[1]);
+        for (int h = 0; h < 4; ++h) {
+          typedef float f32x2 __attribute__((ext_vector_type(2)));
+          const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)codes[h], false);
+          const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)codes[h], true);
+          o[h >> 1][2 * (h & 1)] = pack_bf16x2(lo[0], lo[1]);
+          o[h >> 1][2 * (h & 1) + 1] = pack_bf16x2(hi[0], hi[1]);
+        }
+        *(u32x4*)(half + raw_t0[i]) = o[0];
+        *(u32x4*)(half + raw_t1[i]) = o[1];
       }
-      *(u32x4*)(half + lds_tile_offset(r, q)) = o;
     }
     f8_idx = -1;
   };
@@ -337,7 +375,7 @@ __device__ __forceinline__ void decode_role(const DecodeParams& p, DecodeShared&
           const int ppage = page_in_order(seg_page0 + hp / 2, seg_page0, cend, rb, nrb);
           const int valid = min(kHalfRows, L - ppage * kPage - kHalfRows * (hp & 1));
           if (valid < kHalfRows) {
-            char* half = &sh.ring[(gbase + hp) & (kRingSlots - 1)][0];
+            char* half = &sh.ring[ring_slot(gbase + hp)][0];
             for (int i = max(valid, 0) * kChunksPerRow + tid; i < kHalfRows * kChunksPerRow; i += kThreads) {
               const int r = i / kChunksPerRow;
               const int c = i - r * kChunksPerRow;
@@ -352,7 +390,7 @@ __device__ __forceinline__ void decode_role(const DecodeParams& p, DecodeShared&
             const int hp = k + 1;
             const int ppage = page_in_order(seg_page0 + hp / 2, seg_page0, cend, rb, nrb);
             const int key0 = ppage * kPage + kHalfRows * (hp & 1);
-            const uint32_t half_base = ring_base + (uint32_t)(((gbase + hp) & (kRingSlots - 1)) * kHalfBytes);
+            const uint32_t half_base = ring_base + (uint32_t)(ring_slot(gbase + hp) * kHalfBytes);
             uint32_t kb[2];
 #pragma unroll
             for (int par = 0; par < 2; ++par) kb[par] = half_base + kb_off[par];
@@ -429,7 +467,7 @@ __device__ __forceinline__ void decode_role(const DecodeParams& p, DecodeShared&
           // half page k-1, is free.)
           const bool issued = stage_step(gbase + k + 3);
           if (k >= 0) {
-            const uint32_t half_base = ring_base + (uint32_t)(((gbase + k) & (kRingSlots - 1)) * kHalfBytes);
+            const uint32_t half_base = ring_base + (uint32_t)(ring_slot(gbase + k) * kHalfBytes);
             uint32_t vb[4];
 #pragma unroll
             for (int m4 = 0; m4 < 4; ++m4) vb[m4] = half_base + vb_off[m4];
@@ -564,7 +602,7 @@ __device__ __forceinline__ void decode_role(const DecodeParams& p, DecodeShared&
 
 template <bool kSingleHead>
 __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(DecodeParams p) {
-  __shared__ __attribute__((aligned(1024))) DecodeShared sh;
+  __shared__ __attribute__((aligned(1024))) DecodeShared<false> sh;
   const int xcd = blockIdx.x % kNumXcd;
   const int k = blockIdx.x / kNumXcd;
   const int rb = k % p.row_blocks;
@@ -582,7 +620,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(DecodeParams p)
 // The same kernel over an fp8 cache (see decode_role's kFp8).
 template <bool kSingleHead>
 __global__ __launch_bounds__(kThreads, 1) void mla_decode_fp8_kernel(DecodeParams p) {
-  __shared__ __attribute__((aligned(1024))) DecodeShared sh;
+  __shared__ __attribute__((aligned(1024))) DecodeShared<true> sh;
   const int xcd = blockIdx.x % kNumXcd;
   const int k = blockIdx.x / kNumXcd;
   const int rb = k % p.row_blocks;
