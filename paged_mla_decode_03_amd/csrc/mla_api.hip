@@ -497,7 +497,7 @@ int mla_stream_read(const void* src, size_t bytes, void* sink, void* stream) {
   const int st = cu_count(-1, &cus);
   if (st != MLA_OK) return st;
   // Eight workgroups of eight waves per compute unit.
-  hipLaunchKernelGGL(mla::mla_stream_read_kernel, dim3(cus * 8), dim3(mla::kStreamThreads), 0, (hipStream_t)stream,
+  hipLaunchKernelGGL(mla::mla_stream_read_kernel, dim3(cus), dim3(mla::kStreamThreads), 0, (hipStream_t)stream,
                      (const uint4*)src, bytes / 16, (uint4*)sink);
   return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }

@@ -17,8 +17,13 @@
 // Sequence b's pages start at unit s_b + H (s_b = exclusive prefix sum of the
 // costs), so the workers meeting them are wf = (s_b+H)/Q .. wl = (s_b+H+n_b-1)/Q,
 // and b has wl - wf + 1 splits.  A worker's first segment is the sequence with
-// the smallest b that meets it, its last the largest; min/max over b are
-// found with LDS atomics, which makes the result independent of thread order.
+// the smallest b that meets it, its last the largest.  Only b's two end
+// workers wf and wl can meet other sequences (a worker strictly between them
+// lies inside b's pages), so min/max over b are found with LDS atomics at
+// those two, which makes the result independent of thread order, and the
+// interior workers' rows are written without a lookup (one thread per
+// sequence walks its workers: a long sequence split many ways costs a loop
+// of plain stores, not of dependent LDS reads).
 //
 // One workgroup, no host synchronisation: the kernel runs on the stream after
 // whatever wrote cache_seqlens.
@@ -90,9 +95,14 @@ __global__ __launch_bounds__(kSchedThreads) void mla_sched_kernel(SchedParams p)
     const long long cnt = n > 0 ? wl - wf + 1 : 0;
     const long long before = split_carry + block_exclusive_scan(cnt, scan_tmp, chunk_splits);
     if (b < B) p.num_splits[b] = (int32_t)before;
-    for (long long w = wf; w <= wl; ++w) {
-      atomicMin(&first_seq[w], b);
-      atomicMax(&last_seq[w], b);
+    // A worker strictly between wf and wl lies inside b's pages, so b is its
+    // only sequence: only the two end workers are contested.  The interior
+    // ones are written directly below.
+    if (n > 0) {
+      atomicMin(&first_seq[wf], b);
+      atomicMax(&last_seq[wf], b);
+      atomicMin(&first_seq[wl], b);
+      atomicMax(&last_seq[wl], b);
     }
     start_carry += chunk_cost;
     split_carry += chunk_splits;
@@ -120,13 +130,14 @@ __global__ __launch_bounds__(kSchedThreads) void mla_sched_kernel(SchedParams p)
     const long long wf = first_unit / Q, wl = (first_unit + n - 1) / Q;
     for (long long w = wf; w <= wl; ++w) {
       int32_t* row = p.meta + (size_t)w * kMetaInts;
-      if (first_seq[w] == b) {
+      const bool interior = w > wf && w < wl;
+      if (interior || first_seq[w] == b) {
         const long long lo = w * Q - first_unit;
         row[0] = b;
         row[1] = (int32_t)(lo > 0 ? lo : 0);
         row[4] = (int32_t)(w - wf);
       }
-      if (last_seq[w] == b) {
+      if (interior || last_seq[w] == b) {
         const long long hi = (w + 1) * Q - first_unit;
         row[2] = b;
         row[3] = (int32_t)(hi < n ? hi : n);

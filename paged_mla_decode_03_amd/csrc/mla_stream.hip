@@ -1,9 +1,12 @@
 // A plain streaming read of device memory (gfx950), for measurement: the
 // rate it reaches is the achievable HBM read bandwidth that the decode's
 // rooflines are set beside (the 8 TB/s of the specification is not reached
-// by any access pattern).  Every lane keeps eight 16-byte non-temporal loads
-// in flight, grid-strided over the buffer; the values are folded and stored
-// only if they match a pattern no test buffer holds, so the loads stay live.
+// by any access pattern).  One 512-thread workgroup per CU reads 64 KB
+// contiguous runs, each lane keeping eight 16-byte non-temporal loads in
+// flight (64 KB per CU: a probe of this chip reached 7.2 TB/s from 32 KB in
+// flight per CU, 4.2 TB/s at 8 KB, and less again with eight such
+// workgroups per CU).  The values are folded and stored only if they match
+// a pattern no test buffer holds, so the loads stay live.
 #include <hip/hip_runtime.h>
 
 #include "mla_kernels.h"
@@ -15,18 +18,22 @@ typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
 __global__ __launch_bounds__(kStreamThreads) void mla_stream_read_kernel(const uint4* __restrict__ src_, size_t n16,
                                                                       uint4* sink) {
   constexpr int kDepth = 8;
+  constexpr size_t kRun = (size_t)kDepth * kStreamThreads;      // 16-byte elements per run
   const u32x4v* src = (const u32x4v*)src_;
-  const size_t stride = (size_t)gridDim.x * kStreamThreads;
-  size_t i = (size_t)blockIdx.x * kStreamThreads + threadIdx.x;
+  const size_t runs = n16 / kRun;
   u32x4v acc = {0, 0, 0, 0};
-  for (; i + (kDepth - 1) * stride < n16; i += kDepth * stride) {
+  for (size_t r = blockIdx.x; r < runs; r += gridDim.x) {
+    const u32x4v* base = src + r * kRun + threadIdx.x;
     u32x4v v[kDepth];
 #pragma unroll
-    for (int k = 0; k < kDepth; ++k) v[k] = __builtin_nontemporal_load(src + i + k * stride);
+    for (int k = 0; k < kDepth; ++k) v[k] = __builtin_nontemporal_load(base + k * kStreamThreads);
 #pragma unroll
     for (int k = 0; k < kDepth; ++k) acc ^= v[k];
   }
-  for (; i < n16; i += stride) acc ^= src[i];
+  // The tail after the last whole run.
+  for (size_t i = runs * kRun + (size_t)blockIdx.x * kStreamThreads + threadIdx.x; i < n16;
+       i += (size_t)gridDim.x * kStreamThreads)
+    acc ^= src[i];
   if (acc[0] == 0x9E3779B9u && acc[1] == 0x7F4A7C15u) sink[0] = uint4{acc[0], acc[1], acc[2], acc[3]};
 }
 
