@@ -20,11 +20,12 @@
 //     load the same weight bytes (the token rows, a few MB, come from L2).
 //   * Wave tile: D^T[n][t] = W[n][:] . A[t][:] as 4 column tiles x 4 token
 //     tiles of v_mfma_f32_16x16x32_bf16 (W rows as the A operand, token rows
-//     as the B operand: both are 16-byte reads along K straight from memory
-//     into registers).  The stream is bound by how many bytes are in flight
-//     (HBM latency is a few microseconds), so every wave keeps the next two
-//     k steps' 16 fragments in flight while one step's 16 MFMAs run: 16 KB
-//     per wave, 128 KB per compute unit.
+//     as the B operand: both read along K straight from memory into
+//     registers, 32 contiguous bytes per lane for two k steps, so a row's
+//     128-byte line is read whole).  The stream is bound by how many bytes
+//     are in flight, so every wave keeps the next pair of k steps' 16
+//     fragments in flight while one pair's 32 MFMAs run: 16 KB per wave,
+//     128 KB per compute unit.
 //   * The workgroups of one (column tile, K slice) that differ only in their
 //     token chunk get consecutive ids on the same XCD, so W is fetched from
 //     HBM once and found in that XCD's L2 by the others.
@@ -75,20 +76,28 @@ __global__ __launch_bounds__(kOutProjThreads, 1) void mla_outproj_kernel(OutProj
   const int half = wave & 1;                           // column half
   const int part = wave >> 1;                          // K quarter
   const int col = lane & 15;
-  const int kq = 8 * (lane >> 4);
   const int n0 = nt * kOutProjTileN + 64 * half;
   const int t0 = tc * kOutProjTileT;
   const int kw = p.K / (p.splits * kKParts);           // this wave's share of K (a multiple of 32)
   const int kbeg = s * (p.K / p.splits) + part * kw;
 
-  // Fragment sources: W rows n0 + 16d + col, token rows t0 + 16r + col
-  // (rows past T repeat row T-1; their outputs are never stored).
+  // K goes in pairs of MFMA k steps (64 values): lane (col, g) loads the 16
+  // values 64p + 16g .. +15 of its rows, 32 contiguous bytes, so the four
+  // lanes of a row take one whole 128-byte line at once (read as two 64-byte
+  // halves in different k steps, a line was often fetched twice), and hands
+  // the first 8 to the MFMA of step 2p, the last 8 to step 2p + 1.  W and the
+  // token rows use the same arrangement, so every MFMA still pairs equal k
+  // and the sum over k is unchanged.  A wave's share with an odd number of
+  // 32-value steps ends with one step in the plain arrangement (lane g takes
+  // values 8g .. 8g + 7).  Rows past T repeat row T-1; their outputs are
+  // never stored.
+  const int g16 = 16 * (lane >> 4);
   const uint16_t* wsrc[4];
   const uint16_t* asrc[4];
 #pragma unroll
-  for (int d = 0; d < 4; ++d) wsrc[d] = p.w + (size_t)(n0 + 16 * d + col) * p.K + kbeg + kq;
+  for (int d = 0; d < 4; ++d) wsrc[d] = p.w + (size_t)(n0 + 16 * d + col) * p.K + kbeg;
 #pragma unroll
-  for (int r = 0; r < 4; ++r) asrc[r] = p.a + (size_t)min(t0 + 16 * r + col, p.T - 1) * p.K + kbeg + kq;
+  for (int r = 0; r < 4; ++r) asrc[r] = p.a + (size_t)min(t0 + 16 * r + col, p.T - 1) * p.K + kbeg;
 
   f32x4 acc[4][4];
 #pragma unroll
@@ -96,38 +105,55 @@ __global__ __launch_bounds__(kOutProjThreads, 1) void mla_outproj_kernel(OutProj
 #pragma unroll
     for (int r = 0; r < 4; ++r) acc[d][r] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // Two k steps in flight ahead of the one being multiplied.  Steps past
-  // the wave's share reload its last step (in bounds, never multiplied).
+  // One pair in flight ahead of the one being multiplied (16 KB per wave);
+  // a pair past the wave's share reloads its last pair (in bounds, never
+  // multiplied).
   const int steps = kw / 32;
-  auto koff = [&](int ks) __attribute__((always_inline)) { return (ks < steps ? ks : steps - 1) * 32; };
-  bf16x8 wf[3][4], af[3][4];
+  const int pairs = steps / 2;
+  auto poff = [&](int pp) __attribute__((always_inline)) { return (pp < pairs ? pp : pairs - 1) * 64 + g16; };
+  bf16x8 wf[2][2][4], af[2][2][4];   // [buffer][step of the pair][tile]
+  auto load_pair = [&]<int B>(int pp) __attribute__((always_inline)) {
+    const int o = poff(pp);
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
+    for (int h = 0; h < 2; ++h) {
 #pragma unroll
-    for (int d = 0; d < 4; ++d) wf[j][d] = load8(wsrc[d] + koff(j));
+      for (int d = 0; d < 4; ++d) wf[B][h][d] = load8(wsrc[d] + o + 8 * h);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) af[j][r] = load8(asrc[r] + koff(j));
+      for (int r = 0; r < 4; ++r) af[B][h][r] = load8(asrc[r] + o + 8 * h);
+    }
+  };
+  auto mma_pair = [&]<int B>() __attribute__((always_inline)) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int d = 0; d < 4; ++d)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          acc[d][r] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[B][h][d], af[B][h][r], acc[d][r], 0, 0, 0);
+  };
+  if (pairs > 0) {
+    load_pair.template operator()<0>(0);
+    int pp = 0;
+    for (; pp + 2 <= pairs; pp += 2) {
+      load_pair.template operator()<1>(pp + 1);
+      mma_pair.template operator()<0>();
+      load_pair.template operator()<0>(pp + 2);
+      mma_pair.template operator()<1>();
+    }
+    if (pp < pairs) mma_pair.template operator()<0>();   // the last pair of an odd count, in buffer 0
   }
-  auto step = [&]<int J>(int ks) __attribute__((always_inline)) {
-    constexpr int L = (J + 2) % 3;
+  if (steps & 1) {
+    const int o = 64 * pairs + 8 * (lane >> 4);
+    bf16x8 wt[4], at[4];
 #pragma unroll
-    for (int d = 0; d < 4; ++d) wf[L][d] = load8(wsrc[d] + koff(ks + 2));
+    for (int d = 0; d < 4; ++d) wt[d] = load8(wsrc[d] + o);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) af[L][r] = load8(asrc[r] + koff(ks + 2));
+    for (int r = 0; r < 4; ++r) at[r] = load8(asrc[r] + o);
 #pragma unroll
     for (int d = 0; d < 4; ++d)
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
-        acc[d][r] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[J][d], af[J][r], acc[d][r], 0, 0, 0);
-  };
-  int ks = 0;
-  for (; ks + 3 <= steps; ks += 3) {
-    step.template operator()<0>(ks);
-    step.template operator()<1>(ks + 1);
-    step.template operator()<2>(ks + 2);
+      for (int r = 0; r < 4; ++r) acc[d][r] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wt[d], at[r], acc[d][r], 0, 0, 0);
   }
-  if (ks < steps) step.template operator()<0>(ks);
-  if (ks + 1 < steps) step.template operator()<1>(ks + 1);
 
   // acc[d][r][i] = partial D^T[n0 + 16d + 4*(lane/16) + i][t0 + 16r + col].
 #pragma unroll
