@@ -75,6 +75,15 @@ constexpr int kScoreDma = 3;
 constexpr int kOutputDma = 6;
 static_assert(kScoreDma + kOutputDma == kHalfRows * kChunksPerRow / 64 / 4, "9 tile columns per tile row");
 
+// page_in_order for at most two row blocks, all this kernel meets (it
+// serves heads of up to 128 query rows in 64-row workgroups): no division.
+__device__ inline int page_in_order_le2(int page, int p0, int end, int rb, int nrb) {
+  const int j = page - p0 - 1;
+  if (j < 0 || nrb == 1) return page;
+  const int base = p0 + 1 + (j & ~1);
+  return base + 2 > end ? page : base + ((j & 1) ^ rb);
+}
+
 // Byte offset of 16-byte unit u (0..3) of row r of a P buffer: rows of 64
 // bytes, units XOR-swizzled by r / 4, so 16 consecutive rows read or write
 // 16 distinct 16-byte bank groups.
@@ -163,7 +172,7 @@ __device__ __forceinline__ void decode_role(const DecodeParams& p, DecodeShared<
   // gq counts half pages issued.
   int lb = cb, lpage = cpage, lend = cend, lp0 = cpage, lhalf = 0, gq = 0;
   bool lvalid = true;
-  int lpid = page_id(p, lb, page_in_order(lpage, lp0, lend, rb, nrb));
+  int lpid = page_id(p, lb, page_in_order_le2(lpage, lp0, lend, rb, nrb));
   const int ow = wave - 4;   // output wave index
   constexpr int kDma = scorer ? kScoreDma : kOutputDma;   // this wave's DMAs per half page
   constexpr int kCol0 = scorer ? kOutputDma : 0;          // its first tile column
@@ -184,7 +193,7 @@ __device__ __forceinline__ void decode_role(const DecodeParams& p, DecodeShared<
     } else {
       lhalf = 0;
       lvalid = next_page(meta, p.seqlens, lb, lpage, lend, lp0);
-      if (lvalid) lpid = page_id(p, lb, page_in_order(lpage, lp0, lend, rb, nrb));
+      if (lvalid) lpid = page_id(p, lb, page_in_order_le2(lpage, lp0, lend, rb, nrb));
     }
     return true;
   };
@@ -238,7 +247,7 @@ __device__ __forceinline__ void decode_role(const DecodeParams& p, DecodeShared<
     } else {
       lhalf = 0;
       lvalid = next_page(meta, p.seqlens, lb, lpage, lend, lp0);
-      if (lvalid) lpid = page_id(p, lb, page_in_order(lpage, lp0, lend, rb, nrb));
+      if (lvalid) lpid = page_id(p, lb, page_in_order_le2(lpage, lp0, lend, rb, nrb));
     }
     return true;
   };
@@ -370,10 +379,11 @@ __device__ __forceinline__ void decode_role(const DecodeParams& p, DecodeShared<
       for (int k = -1; k < nhalf; ++k) {
         // Tail of half page k+1 (read by the score waves now and the output
         // waves next step): rows past the sequence end hold anything.
+        // Page of half page k+1 (its tail here, its scores below).
+        const int ppage1 = page_in_order_le2(seg_page0 + (k + 1) / 2, seg_page0, cend, rb, nrb);
         if (k + 1 < nhalf) {
           const int hp = k + 1;
-          const int ppage = page_in_order(seg_page0 + hp / 2, seg_page0, cend, rb, nrb);
-          const int valid = min(kHalfRows, L - ppage * kPage - kHalfRows * (hp & 1));
+          const int valid = min(kHalfRows, L - ppage1 * kPage - kHalfRows * (hp & 1));
           if (valid < kHalfRows) {
             char* half = &sh.ring[ring_slot(gbase + hp)][0];
             for (int i = max(valid, 0) * kChunksPerRow + tid; i < kHalfRows * kChunksPerRow; i += kThreads) {
@@ -388,8 +398,7 @@ __device__ __forceinline__ void decode_role(const DecodeParams& p, DecodeShared<
           if (k + 1 < nhalf) {
             // ---- scores of half page hp = k+1: S^T = K Q^T, key tiles 0, 1 ----
             const int hp = k + 1;
-            const int ppage = page_in_order(seg_page0 + hp / 2, seg_page0, cend, rb, nrb);
-            const int key0 = ppage * kPage + kHalfRows * (hp & 1);
+            const int key0 = ppage1 * kPage + kHalfRows * (hp & 1);
             const uint32_t half_base = ring_base + (uint32_t)(ring_slot(gbase + hp) * kHalfBytes);
             uint32_t kb[2];
 #pragma unroll
@@ -542,7 +551,7 @@ __device__ __forceinline__ void decode_role(const DecodeParams& p, DecodeShared<
         lhalf = 0;
         lvalid = true;
         gq = gbase;
-        lpid = page_id(p, lb, page_in_order(lpage, lp0, lend, rb, nrb));
+        lpid = page_id(p, lb, page_in_order_le2(lpage, lp0, lend, rb, nrb));
         if constexpr (kFp8) {
           f8_idx = -1;   // drop what was loaded ahead; the pass reloads from its start
           load_half();
