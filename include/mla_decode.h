@@ -295,8 +295,8 @@ int mla_pages_release(int32_t* free_pages, int32_t* state, int num_pages, const 
 /* Measurement helper, not a step of the method: a plain streaming read of
  * `bytes` bytes at src (device memory; 16-byte aligned, bytes a multiple of
  * 16): one 512-thread workgroup per compute unit reading 64 KB runs, eight
- * 16-byte loads in flight per lane.  Timing it gives the achievable HBM read rate that the
- * decode's rooflines are reported beside.  sink [dev] 16 bytes, written only
+ * 16-byte loads in flight per lane.  Timing it gives the achievable HBM read
+ * rate that the decode's rooflines are reported beside.  sink [dev] 16 bytes, written only
  * in the (never expected) case that the folded data match a fixed pattern. */
 int mla_stream_read(const void* src, size_t bytes, void* sink, void* stream);
 

@@ -119,3 +119,31 @@ def test_fp8_append_bit_exact(h_kv, s_new, seqlens):
     assert int(bad_rows.item()) == bad and bad >= 1
     diff = np.argwhere(got != want)
     assert diff.size == 0, f"{len(diff)} codes differ, first at {diff[0].tolist()}: {got[tuple(diff[0])]} vs {want[tuple(diff[0])]}"
+
+
+def test_fp8_append_then_decode_end_to_end():
+    """bf16 latents appended into an empty fp8 cache on the GPU (three
+    sequences, 150 tokens each, over three pages), then decoded from it: the
+    codes equal the oracle's append of the same latents bit for bit, and the
+    decode matches the oracle's decode of its own cache."""
+    scale = 1.0 / 64
+    w = Workload("custom", batch=3, s_q=1, h_q=64, h_kv=1, causal=False, seqlens=(0, 0, 0), num_pages=None)
+    inp, kv_new = make_append_inputs(w, 21, 150, seqlens=[0, 0, 0], extra_pages=1)
+    P = inp.kvcache.shape[0]
+    L0 = inp.cache_seqlens.numpy().copy()
+    bt = inp.block_table.numpy().copy()
+    want, bad = mo.kvcache_append_fp8_ref(np.zeros((P, 64, 1, 576), dtype=np.uint8), bt, L0, kv_new,
+                                          np.float32(1.0) / np.float32(scale))
+    assert bad == 0
+    kv = torch.zeros((P, 64, 1, 576), dtype=torch.uint8, device=DEV)
+    bt_d = torch.from_numpy(bt).to(DEV)
+    bad_rows = torch.zeros(1, dtype=torch.int32, device=DEV)
+    kvcache_append_fp8(kv_new.to(DEV), kv, scale, bt_d, torch.from_numpy(L0).to(DEV), bad_rows)
+    torch.cuda.synchronize()
+    assert np.array_equal(kv.cpu().numpy(), want) and int(bad_rows.item()) == 0
+    L = torch.from_numpy((L0 + 150).astype(np.int32))
+    meta, ns = get_mla_metadata(L.to(DEV), 64, 1)
+    o, lse = mla_decode_paged_fp8(inp.q.to(DEV), kv, scale, bt_d, L.to(DEV), 512, meta, ns)
+    torch.cuda.synchronize()
+    O, LSE = mo.mla_decode_fp8_ref(inp.q, want, scale, bt, L.numpy(), 512)
+    compare(o.float().cpu().double().numpy(), lse.cpu().double().numpy(), O, LSE, label="fp8 append then decode")
