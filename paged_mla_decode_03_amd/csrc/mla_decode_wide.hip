@@ -119,14 +119,15 @@ __device__ __forceinline__ void wide_worker(const DecodeParams& p, char (*lds_pa
   //   V: row lane/4 (+16 per read), columns 128*wave + 16*d + 4*(lane%4); the
   //      offsets of column tiles d and d+4 differ by one LDS tile (1 KB).
   //   P: row col (+16 per row tile), unit 4*kk + grp4.
-  uint32_t kb_off[2], vb_off[4], pr_off[2];
-#pragma unroll
-  for (int par = 0; par < 2; ++par) kb_off[par] = lds_tile_offset(col, 4 * par + grp4);
-#pragma unroll
-  for (int d = 0; d < 4; ++d)
-    vb_off[d] = lds_tile_offset(lane >> 2, 16 * wave + 2 * d + ((lane & 3) >> 1)) + 8 * (lane & 1);
-#pragma unroll
-  for (int kk = 0; kk < 2; ++kk) pr_off[kk] = lds_p + p_unit_offset(col, 4 * kk + grp4);
+  // One register per operand: with the XOR swizzle, chunk 4 + c differs
+  // from chunk c by bit 6 of the byte offset, chunk 2d + c (c < 2) from c by
+  // bits 5-6 (d << 5), and P unit 4 + u from u by bit 6; the page and P
+  // buffers are 1 KB aligned and the added row and tile offsets are
+  // multiples of 1 KB or 2 KB, so the XOR applies to the full address.
+  const uint32_t kb_off = lds_tile_offset(col, grp4);
+  const uint32_t vb_off = lds_tile_offset(lane >> 2, 16 * wave + ((lane & 3) >> 1)) + 8 * (lane & 1);
+  const uint32_t pr_off0 = lds_p + p_unit_offset(col, grp4);
+  auto pr_off = [&](int kk) __attribute__((always_inline)) { return pr_off0 ^ (uint32_t)(64 * kk); };
   // Score rows of this wave: 32*wave + 16*j + col (the swizzle of a P row
   // depends on col only, so the write offset is the read offset plus whole rows).
   const uint32_t pw_base = (uint32_t)(2 * wave) * 16 * kWidePRowBytes;
@@ -235,11 +236,8 @@ __device__ __forceinline__ void wide_worker(const DecodeParams& p, char (*lds_pa
         const uint32_t dma_dst = lds_base + ((it + 1) & 1) * kPageBytes;
 
         const uint32_t page_base = (uint32_t)(uintptr_t)buf;
-        uint32_t kb[2], vb[4];
-#pragma unroll
-        for (int par = 0; par < 2; ++par) kb[par] = page_base + kb_off[par];
-#pragma unroll
-        for (int m4 = 0; m4 < 4; ++m4) vb[m4] = page_base + vb_off[m4];
+        const uint32_t kb0 = page_base + kb_off, vb0 = page_base + vb_off;
+        const uint32_t kb[2] = {kb0, kb0 ^ 64u};
         const int key0 = ppage * kPage;
 
         auto read_k = [&](int kt, int ks) __attribute__((always_inline)) {
@@ -250,7 +248,7 @@ __device__ __forceinline__ void wide_worker(const DecodeParams& p, char (*lds_pa
         // 4*grp4 + m and 32kk + 16 + 4*grp4 + m, from two transposing reads of
         // 4 rows x 16 columns (lane l fetches row l/4, columns 4*(l%4)..+3).
         auto read_v = [&](int kk, int d) __attribute__((always_inline)) {
-          const uint32_t a = vb[d & 3] + (uint32_t)((d >> 2) * 1024);
+          const uint32_t a = (vb0 ^ (uint32_t)((d & 3) << 5)) + (uint32_t)((d >> 2) * 1024);
           const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(a + (uint32_t)((4 * kk + 0) * 9 * 1024)));
           const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(a + (uint32_t)((4 * kk + 2) * 9 * 1024)));
           return __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
@@ -258,7 +256,7 @@ __device__ __forceinline__ void wide_worker(const DecodeParams& p, char (*lds_pa
         // B operand for output row tile t of k-step kk: lane (col, grp4) gets
         // P[16t + col][slots 8*grp4 .. +7 of k-step kk].
         auto read_p = [&](int kk, int t) __attribute__((always_inline)) {
-          return *(lds_bf16x8*)(pr_off[kk] + (uint32_t)(t * 16 * kWidePRowBytes));
+          return *(lds_bf16x8*)(pr_off(kk) + (uint32_t)(t * 16 * kWidePRowBytes));
         };
 
         // ---- scores: S^T = K Q^T, 4 key tiles x 2 row tiles ----
@@ -363,7 +361,7 @@ __device__ __forceinline__ void wide_worker(const DecodeParams& p, char (*lds_pa
                 l_bf[j] = add_bf16x2(l_bf[j], pk[i][h]);
               }
             // Slot 8*grp4 + 4*i + e of k-step kk holds key 32kk + 16i + 4*grp4 + e.
-            *(__attribute__((address_space(3))) u32x4*)(pr_off[kk] + pw_base + (uint32_t)(j * 16 * kWidePRowBytes)) =
+            *(__attribute__((address_space(3))) u32x4*)(pr_off(kk) + pw_base + (uint32_t)(j * 16 * kWidePRowBytes)) =
                 u32x4{pk[0][0], pk[0][1], pk[1][0], pk[1][1]};
           }
         }
