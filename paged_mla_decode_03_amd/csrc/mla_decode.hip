@@ -351,6 +351,9 @@ __device__ __forceinline__ void decode_role(const DecodeParams& p, DecodeShared<
     }
     const int n_vis_min = p.causal ? L - p.s_q + row_tok(0) + 1 : L;
     float m_ref = kNegInf;
+    // Derived from m_ref wherever it is set: the exponent offset (0 for a row
+    // without a reference) and the score above which the pass overflows.
+    float m_mu = 0.f, m_lim = kNegInf;
     bool second_pass = false;
     float m_seen, l_run, l_bf;   // l_run: exact sum of the weights (for lse); l_bf: of their bf16 roundings (for O)
     int overflow;
@@ -433,22 +436,25 @@ __device__ __forceinline__ void decode_role(const DecodeParams& p, DecodeShared<
 #pragma unroll
               for (int e = 0; e < 4; ++e) x[i][e] = s[i][e];
             if (key0 + kHalfRows > n_vis_min) {
+              // Key key0 + 16*i + 4*grp4 + e is visible iff 16*i + e < lim.
+              const int lim = n_vis - key0 - 4 * grp4;
 #pragma unroll
               for (int i = 0; i < 2; ++i)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                  const int key = key0 + 16 * i + 4 * grp4 + e;
-                  x[i][e] = key < n_vis ? x[i][e] : kNegInf;
-                }
+                for (int e = 0; e < 4; ++e) x[i][e] = 16 * i + e < lim ? x[i][e] : kNegInf;
             }
             float xm = max2(max2(max2(x[0][0], x[0][1]), max2(x[0][2], x[0][3])),
                             max2(max2(x[1][0], x[1][1]), max2(x[1][2], x[1][3])));
             xm *= p.scale_log2;
             // The segment's first half page sets each row's reference.
-            if (!second_pass && hp == 0) m_ref = row_max4(xm);
-            overflow |= xm > m_ref + kOverflowThreshold;
+            if (!second_pass && hp == 0) {
+              m_ref = row_max4(xm);
+              m_mu = m_ref == kNegInf ? 0.f : m_ref;
+              m_lim = m_ref + kOverflowThreshold;
+            }
+            overflow |= xm > m_lim;
             m_seen = max2(m_seen, xm);
-            const float mu = m_ref == kNegInf ? 0.f : m_ref;
+            const float mu = m_mu;
             uint32_t pk[2][2];
 #pragma unroll
             for (int i = 0; i < 2; ++i)
@@ -540,7 +546,11 @@ __device__ __forceinline__ void decode_role(const DecodeParams& p, DecodeShared<
       // Overflow: rerun the segment with each row's maximum as reference.
       // The output waves drain their DMAs and restart the load pipeline at
       // the segment's first half page.
-      if constexpr (scorer) m_ref = row_max4(m_seen);
+      if constexpr (scorer) {
+        m_ref = row_max4(m_seen);
+        m_mu = m_ref == kNegInf ? 0.f : m_ref;
+        m_lim = m_ref + kOverflowThreshold;
+      }
       second_pass = true;
       {
         wait_dma_all();

@@ -325,13 +325,14 @@ __device__ __forceinline__ void wide_worker(const DecodeParams& p, char (*lds_pa
 #pragma unroll
             for (int e = 0; e < 4; ++e) x[kt][e] = s[kt][j][e];
           if (key0 + kPage > n_vis_min) {
+            // Key key0 + 16*kt + 4*grp4 + e is visible iff 16*kt + e < lim:
+            // one subtraction per row, compile-time offsets per key (the key
+            // indices themselves would be formed on every page).
+            const int lim = n_vis[j] - key0 - 4 * grp4;
 #pragma unroll
             for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-              for (int e = 0; e < 4; ++e) {
-                const int key = key0 + 16 * kt + 4 * grp4 + e;
-                x[kt][e] = key < n_vis[j] ? x[kt][e] : kNegInf;
-              }
+              for (int e = 0; e < 4; ++e) x[kt][e] = 16 * kt + e < lim ? x[kt][e] : kNegInf;
           }
           // This lane's maximum raw score (the scale is > 0), in log2 units.
           float xm = kNegInf;
