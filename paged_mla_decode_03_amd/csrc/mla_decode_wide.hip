@@ -104,6 +104,7 @@ __device__ __forceinline__ void wide_worker(const DecodeParams& p, char (*lds_pa
   int cb = meta_b0, cpage = ld_uniform(meta + 1), cend = segment_end(meta, p.seqlens, cb);
   if (cpage >= cend) return;
   int lb = cb, lpage = cpage, lend = cend, lp0 = cpage;
+  size_t lrow = 0;   // lb * max_pages: the load cursor's block_table row
   const int nrb = p.row_blocks;
   bool lvalid = true;
 
@@ -169,6 +170,7 @@ __device__ __forceinline__ void wide_worker(const DecodeParams& p, char (*lds_pa
     lvalid = next_page(meta, p.seqlens, lb, lpage, lend, lp0);
     stage_page<kWideDmaPerWave>(page_rsrc(kv_head, first_pid, p.num_pages, page_stride_bytes, page_span),
                                 lane_src_off, row_stride_bytes, lds_base, wave);
+    lrow = (size_t)lb * p.max_pages;
     if (lvalid) next_pid = page_id(p, lb, page_in_order(lpage, lp0, lend, rb, nrb));
   }
 
@@ -305,10 +307,29 @@ __device__ __forceinline__ void wide_worker(const DecodeParams& p, char (*lds_pa
         }(std::make_integer_sequence<int, kFrags>{});
 
         // The load cursor moves on and the id of the page after the next is
-        // read here, where waiting for the scalar load costs nothing.
+        // read; its scalar load lands during the softmax.  Inside a segment
+        // that is a few scalar instructions (for two row blocks the page
+        // order is a select, the table row's offset is kept, and the table
+        // index is clamped into the row instead of branching around the
+        // load); a segment's end takes the full walk to the next sequence.
         if (lvalid) {
-          lvalid = next_page(meta, p.seqlens, lb, lpage, lend, lp0);
-          if (lvalid) next_pid = page_id(p, lb, page_in_order(lpage, lp0, lend, rb, nrb));
+          if (lpage + 1 < lend) {
+            ++lpage;
+            int j;
+            if (nrb == 2) {
+              const int jj = lpage - lp0 - 1;
+              const int base = lp0 + 1 + (jj & ~1);
+              j = (jj < 0 || base + 2 > lend) ? lpage : base + ((jj & 1) ^ rb);
+            } else {
+              j = page_in_order(lpage, lp0, lend, rb, nrb);
+            }
+            const int pid = ld_uniform(p.block_table + lrow + min(j, p.max_pages - 1));
+            next_pid = j < p.max_pages ? pid : -1;
+          } else {
+            lvalid = next_page(meta, p.seqlens, lb, lpage, lend, lp0);
+            lrow = (size_t)lb * p.max_pages;
+            if (lvalid) next_pid = page_id(p, lb, page_in_order(lpage, lp0, lend, rb, nrb));
+          }
         }
 
         // ---- softmax weights (base 2) against the row references ----
@@ -434,6 +455,7 @@ __device__ __forceinline__ void wide_worker(const DecodeParams& p, char (*lds_pa
         lvalid = next_page(meta, p.seqlens, lb, lpage, lend, lp0);
         stage_page<kWideDmaPerWave>(page_rsrc(kv_head, first_pid, p.num_pages, page_stride_bytes, page_span),
                                     lane_src_off, row_stride_bytes, lds_base + (it & 1) * kPageBytes, wave);
+        lrow = (size_t)lb * p.max_pages;
         if (lvalid) next_pid = page_id(p, lb, page_in_order(lpage, lp0, lend, rb, nrb));
       }
     }
