@@ -73,6 +73,19 @@ def test_worker_counts(W):
     compare(o, lse, O, LSE, label=f"W={W} splits={np.diff(ns).tolist()}")
 
 
+@pytest.mark.parametrize("W", [1, 3, 17])
+@pytest.mark.parametrize("s_q,h_kv", [(2, 1), (3, 1), (3, 2)])
+def test_worker_counts_128_row_blocks(W, s_q, h_kv):
+    """Few workers over heads of 256, 384 and 2 x 192 query rows (two or three
+    128-row blocks, one or two latent heads): every worker's load cursor
+    walks many pages of a sequence and crosses into the next one, in the
+    page order of two row blocks and of three."""
+    inp = _custom(3, s_q, 128, h_kv, True, [70, 1300, 5], seed=40 + W + s_q)
+    o, lse, _, ns = run_gpu(inp, num_workers=W)
+    O, LSE = oracle(inp)
+    compare(o, lse, O, LSE, label=f"s_q={s_q} h_kv={h_kv} W={W} splits={np.diff(ns).tolist()}")
+
+
 def test_softmax_scale_argument():
     inp = _custom(2, 1, 32, 1, False, [90, 3], seed=5)
     o, lse, _, _ = run_gpu(inp, softmax_scale=0.02)
