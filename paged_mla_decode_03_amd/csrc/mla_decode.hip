@@ -184,9 +184,10 @@ __device__ __forceinline__ void decode_role(const DecodeParams& p, DecodeShared<
     const __amdgpu_buffer_rsrc_t rsrc = page_rsrc(kv_head, lpid, p.num_pages, page_stride_bytes, page_span);
     const uint32_t dst =
         ring_base + (uint32_t)(ring_slot(gq) * kHalfBytes) + (uint32_t)((trow * 9 + kCol0) * 1024);
-    const int soff0 = (kHalfRows * lhalf + 8 * trow) * row_stride_bytes + kCol0 * 128;
-#pragma unroll
-    for (int j = 0; j < kDma; ++j) lds_dma16(dst + (uint32_t)(j * 1024), lane_src_off, rsrc, (uint32_t)(soff0 + j * 128));
+    const uint32_t soff0 = (uint32_t)((kHalfRows * lhalf + 8 * trow) * row_stride_bytes + kCol0 * 128);
+    [&]<int... j>(std::integer_sequence<int, j...>) __attribute__((always_inline)) {
+      (lds_dma16_at<j * 1024, j * 128>(dst, lane_src_off, rsrc, soff0), ...);
+    }(std::make_integer_sequence<int, kDma>{});
     ++gq;
     if (lhalf == 0) {
       lhalf = 1;

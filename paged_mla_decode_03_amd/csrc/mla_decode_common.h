@@ -3,6 +3,8 @@
 // reductions, and the worker's page cursor.
 #pragma once
 
+#include <utility>
+
 #include "mla_kernels.h"
 
 namespace mla {
@@ -79,12 +81,6 @@ __device__ inline __amdgpu_buffer_rsrc_t page_rsrc(const char* kv_head, int pid,
   return page_resource(kv_head + (ok ? (size_t)pid * page_stride : (size_t)0), ok ? page_bytes : 0u);
 }
 
-// DMA number k (0 .. kPerWave-1) of this wave for one page, when each of the
-// workgroup's waves issues kPerWave of the page's 72: tile j = kPerWave *
-// wave + k, i.e. tile row j / 9 (rows 8*(j/9) ..+7) x tile column j % 9
-// (chunks 8*(j%9) ..+7).  Both addresses are a per-wave base plus a
-// compile-time offset (k is a constant in every call), so the page's DMAs
-// hold no scalar registers across the page loop.
 // One wave-wide DMA: lane u reads 16 bytes at the resource's base +
 // lane_off(u) + soff, and LDS receives them at m0 + 16u.
 __device__ inline void lds_dma16(uint32_t m0, uint32_t lane_off, __amdgpu_buffer_rsrc_t rsrc, uint32_t soff) {
@@ -94,20 +90,49 @@ __device__ inline void lds_dma16(uint32_t m0, uint32_t lane_off, __amdgpu_buffer
                : "memory", "m0");
 }
 
+// The same DMA with compile-time offsets: LDS at m0_base + kLds, source at
+// soff + kSrc.  The instruction's offset field adds kSrc to the source and
+// to the LDS address alike, so M0 is set to m0_base + kLds - kSrc by one
+// scalar add; the tiles of one tile row (source 128 bytes apart, LDS 1 KB
+// apart) then share one base and one source offset register.
+template <int kLds, int kSrc>
+__device__ inline void lds_dma16_at(uint32_t m0_base, uint32_t lane_off, __amdgpu_buffer_rsrc_t rsrc, uint32_t soff) {
+  static_assert(kSrc >= 0 && kSrc < 4096 && kLds >= kSrc, "12-bit offset field; M0 at or above the base");
+  asm volatile("s_add_u32 m0, %0, %4\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen offset:%5 lds"
+               :
+               : "s"(m0_base), "v"(lane_off), "s"(rsrc), "s"(soff), "i"(kLds - kSrc), "i"(kSrc)
+               : "memory", "m0", "scc");
+}
+
+// DMA number k (0 .. kPerWave-1) of this wave for one page, when each of the
+// workgroup's waves issues kPerWave of the page's 72: tile j = kPerWave *
+// wave + k, i.e. tile row j / 9 (rows 8*(j/9) ..+7) x tile column j % 9
+// (chunks 8*(j%9) ..+7).  m0_wave is the LDS address of the wave's first
+// tile (the page buffer + kPerWave KB per wave) and soff_rows[r] the source
+// offset of its tile row r (8 rows per tile row); the tile column is a
+// compile-time offset.
 template <int kPerWave>
-__device__ inline void stage_tile(__amdgpu_buffer_rsrc_t rsrc, uint32_t lane_off, int row_stride_bytes,
-                                  uint32_t lds_dst, int wave, int k) {
+struct WaveTiles {
   static_assert(kPerWave % 9 == 0 && (kPageBytes / 1024) % kPerWave == 0, "whole tile rows per wave");
-  const uint32_t m0 = lds_dst + (uint32_t)(wave * kPerWave * 1024) + (uint32_t)(k * 1024);
-  const uint32_t soff = (wave * (kPerWave / 9) + k / 9) * 8 * row_stride_bytes + (k % 9) * 128;
-  lds_dma16(m0, lane_off, rsrc, soff);
+  uint32_t soff_rows[kPerWave / 9];
+  __device__ WaveTiles(int wave, int row_stride_bytes) {
+#pragma unroll
+    for (int r = 0; r < kPerWave / 9; ++r) soff_rows[r] = (uint32_t)((wave * (kPerWave / 9) + r) * 8 * row_stride_bytes);
+  }
+};
+
+template <int kPerWave, int k>
+__device__ inline void stage_tile(__amdgpu_buffer_rsrc_t rsrc, uint32_t lane_off, uint32_t m0_wave,
+                                  const WaveTiles<kPerWave>& t) {
+  lds_dma16_at<k * 1024, (k % 9) * 128>(m0_wave, lane_off, rsrc, t.soff_rows[k / 9]);
 }
 
 template <int kPerWave>
-__device__ inline void stage_page(__amdgpu_buffer_rsrc_t rsrc, uint32_t lane_off, int row_stride_bytes,
-                                  uint32_t lds_dst, int wave) {
-#pragma unroll
-  for (int k = 0; k < kPerWave; ++k) stage_tile<kPerWave>(rsrc, lane_off, row_stride_bytes, lds_dst, wave, k);
+__device__ inline void stage_page(__amdgpu_buffer_rsrc_t rsrc, uint32_t lane_off, uint32_t m0_wave,
+                                  const WaveTiles<kPerWave>& t) {
+  [&]<int... k>(std::integer_sequence<int, k...>) __attribute__((always_inline)) {
+    (stage_tile<kPerWave, k>(rsrc, lane_off, m0_wave, t), ...);
+  }(std::make_integer_sequence<int, kPerWave>{});
 }
 
 // Zero rows [valid, 64) of a staged page (its cache slots lie past the

@@ -113,6 +113,8 @@ __device__ __forceinline__ void wide_worker(const DecodeParams& p, char (*lds_pa
   const uint32_t page_span = (uint32_t)(kPage * row_stride_bytes);              // resource size
   const char* kv_head = (const char*)p.kv + (size_t)g * kRowBytes;
   const uint32_t lane_src_off = (lane >> 3) * row_stride_bytes + ((lane & 7) ^ (lane >> 3)) * 16;
+  const WaveTiles<kWideDmaPerWave> tiles(wave, row_stride_bytes);
+  const uint32_t wave_tiles_lds = (uint32_t)(wave * kWideDmaPerWave * 1024);   // the wave's first tile in a page buffer
 
   // Page-independent per-lane LDS offsets; a fragment read adds the page
   // buffer's base and a compile-time offset below 64 KB.
@@ -169,7 +171,7 @@ __device__ __forceinline__ void wide_worker(const DecodeParams& p, char (*lds_pa
     const int first_pid = page_id(p, lb, page_in_order(lpage, lp0, lend, rb, nrb));
     lvalid = next_page(meta, p.seqlens, lb, lpage, lend, lp0);
     stage_page<kWideDmaPerWave>(page_rsrc(kv_head, first_pid, p.num_pages, page_stride_bytes, page_span),
-                                lane_src_off, row_stride_bytes, lds_base, wave);
+                                lane_src_off, lds_base + wave_tiles_lds, tiles);
     lrow = (size_t)lb * p.max_pages;
     if (lvalid) next_pid = page_id(p, lb, page_in_order(lpage, lp0, lend, rb, nrb));
   }
@@ -235,7 +237,7 @@ __device__ __forceinline__ void wide_worker(const DecodeParams& p, char (*lds_pa
         // size 0 and write zeros into the free buffer.
         const __amdgpu_buffer_rsrc_t dma_rsrc =
             page_rsrc(kv_head, lvalid ? next_pid : -1, p.num_pages, page_stride_bytes, page_span);
-        const uint32_t dma_dst = lds_base + ((it + 1) & 1) * kPageBytes;
+        const uint32_t dma_m0 = lds_base + ((it + 1) & 1) * kPageBytes + wave_tiles_lds;
 
         const uint32_t page_base = (uint32_t)(uintptr_t)buf;
         const uint32_t kb0 = page_base + kb_off, vb0 = page_base + vb_off;
@@ -278,7 +280,7 @@ __device__ __forceinline__ void wide_worker(const DecodeParams& p, char (*lds_pa
         static_assert(kDmaStart + kDmaEvery * (kWideDmaPerWave - 1) < kQk, "every DMA inside the score stream");
         auto dma_step = [&]<int G>() __attribute__((always_inline)) {
           if constexpr (G >= kDmaStart && (G - kDmaStart) % kDmaEvery == 0 && (G - kDmaStart) / kDmaEvery < kWideDmaPerWave) {
-            stage_tile<kWideDmaPerWave>(dma_rsrc, lane_src_off, row_stride_bytes, dma_dst, wave, (G - kDmaStart) / kDmaEvery);
+            stage_tile<kWideDmaPerWave, (G - kDmaStart) / kDmaEvery>(dma_rsrc, lane_src_off, dma_m0, tiles);
           }
         };
         f32x4 s[4][2];
@@ -454,7 +456,7 @@ __device__ __forceinline__ void wide_worker(const DecodeParams& p, char (*lds_pa
         const int first_pid = page_id(p, lb, page_in_order(lpage, lp0, lend, rb, nrb));
         lvalid = next_page(meta, p.seqlens, lb, lpage, lend, lp0);
         stage_page<kWideDmaPerWave>(page_rsrc(kv_head, first_pid, p.num_pages, page_stride_bytes, page_span),
-                                    lane_src_off, row_stride_bytes, lds_base + (it & 1) * kPageBytes, wave);
+                                    lane_src_off, lds_base + (it & 1) * kPageBytes + wave_tiles_lds, tiles);
         lrow = (size_t)lb * p.max_pages;
         if (lvalid) next_pid = page_id(p, lb, page_in_order(lpage, lp0, lend, rb, nrb));
       }
