@@ -351,6 +351,13 @@ __device__ __forceinline__ void decode_role(const DecodeParams& p, DecodeShared<
       n_vis = p.causal ? L - p.s_q + row_tok(srow) + 1 : L;
     }
     const int n_vis_min = p.causal ? L - p.s_q + row_tok(0) + 1 : L;
+    // Half pages that can hold keys at or past n_vis_min (rows to zero past
+    // the sequence end, keys to mask) start at step index hp_attn: the page
+    // order moves a page by at most one place, so the half page at step hp
+    // lies in page seg_page0 + hp/2 + 1 or below, whose keys end before
+    // n_vis_min while hp < hp_attn.  Earlier steps skip the page-order
+    // arithmetic.
+    const int hp_attn = 2 * (n_vis_min / kPage - seg_page0 - 1);
     float m_ref = kNegInf;
     // Derived from m_ref wherever it is set: the exponent offset (0 for a row
     // without a reference) and the score above which the pass overflows.
@@ -383,10 +390,12 @@ __device__ __forceinline__ void decode_role(const DecodeParams& p, DecodeShared<
       for (int k = -1; k < nhalf; ++k) {
         // Tail of half page k+1 (read by the score waves now and the output
         // waves next step): rows past the sequence end hold anything.
-        // Page of half page k+1 (its tail here, its scores below).
-        const int ppage1 = page_in_order_le2(seg_page0 + (k + 1) / 2, seg_page0, cend, rb, nrb);
-        if (k + 1 < nhalf) {
+        // Page of half page k+1 (its tail here, its masking below).
+        const bool attn = k + 1 >= hp_attn;
+        int ppage1 = 0;
+        if (attn && k + 1 < nhalf) {
           const int hp = k + 1;
+          ppage1 = page_in_order_le2(seg_page0 + hp / 2, seg_page0, cend, rb, nrb);
           const int valid = min(kHalfRows, L - ppage1 * kPage - kHalfRows * (hp & 1));
           if (valid < kHalfRows) {
             char* half = &sh.ring[ring_slot(gbase + hp)][0];
@@ -436,7 +445,7 @@ __device__ __forceinline__ void decode_role(const DecodeParams& p, DecodeShared<
             for (int i = 0; i < 2; ++i)
 #pragma unroll
               for (int e = 0; e < 4; ++e) x[i][e] = s[i][e];
-            if (key0 + kHalfRows > n_vis_min) {
+            if (attn && key0 + kHalfRows > n_vis_min) {
               // Key key0 + 16*i + 4*grp4 + e is visible iff 16*i + e < lim.
               const int lim = n_vis - key0 - 4 * grp4;
 #pragma unroll

@@ -226,11 +226,20 @@ __device__ __forceinline__ void wide_worker(const DecodeParams& p, char (*lds_pa
         wait_dma_all();
         __syncthreads();
         char* buf = lds_page[it & 1];
-        const int ppage = page_in_order(cpage, seg_page0, cend, rb, nrb);   // the page this step processes
-        const int valid = min(kPage, L - ppage * kPage);
-        if (valid < kPage) {
-          zero_tail_rows<kWideThreads>(buf, valid, tid);
-          __syncthreads();
+        // The page this step processes, needed only where its keys can reach
+        // n_vis_min (rows past the sequence end to zero, keys to mask): the
+        // page order moves a page by at most nrb - 1 places, so before page
+        // n_vis_min / 64 - nrb + 1 of the segment's walk every key is
+        // visible.
+        const bool attn = cpage > n_vis_min / kPage - nrb;
+        int ppage = 0;
+        if (attn) {
+          ppage = page_in_order(cpage, seg_page0, cend, rb, nrb);
+          const int valid = min(kPage, L - ppage * kPage);
+          if (valid < kPage) {
+            zero_tail_rows<kWideThreads>(buf, valid, tid);
+            __syncthreads();
+          }
         }
         // The next page's DMAs go out in every step, so that the score stream
         // holds no branch: with no page left they read from a resource of
@@ -347,7 +356,7 @@ __device__ __forceinline__ void wide_worker(const DecodeParams& p, char (*lds_pa
           for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
             for (int e = 0; e < 4; ++e) x[kt][e] = s[kt][j][e];
-          if (key0 + kPage > n_vis_min) {
+          if (attn && key0 + kPage > n_vis_min) {
             // Key key0 + 16*kt + 4*grp4 + e is visible iff 16*kt + e < lim:
             // one subtraction per row, compile-time offsets per key (the key
             // indices themselves would be formed on every page).
