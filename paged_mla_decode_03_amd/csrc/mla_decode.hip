@@ -32,10 +32,10 @@
 //     XOR-swizzled by row) and two 4 KB P buffers (half page q's weights in
 //     buffer q % 2).  Pages move HBM -> LDS with buffer_load_dwordx4 ... lds
 //     (no VGPR staging; the buffer resource bounds every read to the page).
-//     During step k the waves issue the DMAs of half page k+3 (output waves
-//     6 each before their MFMAs, score waves 3 each after their softmax) and,
-//     before the step's barrier, wait for their share of half page k+2,
-//     which the score waves read in step k+1.
+//     During step k the output waves issue the DMAs of half page k+3 (9
+//     each, before their MFMAs) and, before the step's barrier, wait for
+//     their share of half page k+2, which the score waves read in step k+1.
+//     (bf16; the fp8 cache's staging below uses all eight waves.)
 //   * Softmax runs in base 2 with the scale folded into one multiply.  Each
 //     row keeps a reference point m (its maximum over the segment's first half
 //     page) and accumulates unnormalised weights 2^(s - m) <= 2^48; that is
@@ -67,12 +67,13 @@ constexpr int kRawUnits = kRawHalfBytes / 1024;       // 18 wave-wide 1 KB DMAs
 constexpr int kPRowBytes = 2 * kHalfRows;           // one row of P: 32 bf16
 constexpr int kPBytes = kRowsPerBlock * kPRowBytes;   // 4 KB per P buffer
 // A half page is 36 wave-wide DMAs: tile row r (rows 8r..8r+7) x 9 tile
-// columns.  Tile row r is issued by score wave r (columns 6..8, after its
-// softmax, where it would otherwise wait at the barrier) and output wave 4+r
-// (columns 0..5, before its MFMAs): a DMA stalls its wave at issue for about
-// a hundred cycles while the memory queue is full.
-constexpr int kScoreDma = 3;
-constexpr int kOutputDma = 6;
+// columns.  Output wave 4+r issues tile row r, before its MFMAs.  The score
+// waves, whose scores and softmax make the longer half of a step, issue
+// none and keep no load cursor of their own in the step loop (a DMA stalls
+// its wave at issue for about a hundred cycles while the memory queue is
+// full, and the output waves otherwise wait at the step's barrier).
+constexpr int kScoreDma = 0;
+constexpr int kOutputDma = 9;
 static_assert(kScoreDma + kOutputDma == kHalfRows * kChunksPerRow / 64 / 4, "9 tile columns per tile row");
 
 // page_in_order for at most two row blocks, all this kernel meets (it
@@ -95,13 +96,17 @@ __device__ inline uint32_t p_unit_offset(int r, int u) {
 // DMAs of one half page) are in flight, in inline assembly like wait_dma_all.
 template <int n>
 __device__ inline void wait_dma_keep() {
-  static_assert(n >= 2 && n <= 7, "wait counts written out below");
+  static_assert(n >= 0 && n <= 9, "wait counts written out below");
+  if constexpr (n == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  if constexpr (n == 1) asm volatile("s_waitcnt vmcnt(1)" ::: "memory");
   if constexpr (n == 2) asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
   if constexpr (n == 3) asm volatile("s_waitcnt vmcnt(3)" ::: "memory");
   if constexpr (n == 4) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
   if constexpr (n == 5) asm volatile("s_waitcnt vmcnt(5)" ::: "memory");
   if constexpr (n == 6) asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
   if constexpr (n == 7) asm volatile("s_waitcnt vmcnt(7)" ::: "memory");
+  if constexpr (n == 8) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+  if constexpr (n == 9) asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
 }
 
 }  // namespace
@@ -482,8 +487,10 @@ __device__ __forceinline__ void decode_role(const DecodeParams& p, DecodeShared<
           }
           // This wave's share of half page gbase+k+3, then wait for its share
           // of half page gbase+k+2 (see the output waves).
-          const bool issued = stage_step(gbase + k + 3);
-          wait_next(issued);
+          if constexpr (kFp8 || kDma > 0) {
+            const bool issued = stage_step(gbase + k + 3);
+            wait_next(issued);
+          }
         } else {
           // ---- output waves: DMAs of half page gbase+k+3, outputs of half page k ----
           // (The last step of the previous segment already issued this
