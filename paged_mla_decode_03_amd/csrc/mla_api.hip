@@ -580,7 +580,7 @@ namespace {
 
 int launch_absorb(const mla::AbsorbParams& p, bool query, hipStream_t stream) {
   const int n = query ? 512 : mla::kDh;
-  const dim3 grid(p.H, n / mla::kAbsorbTileN, (p.T + mla::kAbsorbTileT - 1) / mla::kAbsorbTileT);
+  const dim3 grid(p.H, n / mla::kAbsorbTileN);   // every workgroup walks all token tiles
   if (query)
     hipLaunchKernelGGL((mla::mla_absorb_kernel<mla::kDh, 512>), grid, dim3(mla::kAbsorbThreads), 0, stream, p);
   else
@@ -590,9 +590,7 @@ int launch_absorb(const mla::AbsorbParams& p, bool query, hipStream_t stream) {
 
 int check_absorb_sizes(int tokens, int h_q) {
   if (tokens <= 0 || h_q <= 0) return MLA_ERR_INVALID_ARG;
-  if ((long long)tokens * h_q * MLA_D_QK >= (1LL << 31) || h_q > 65535 ||
-      (tokens + mla::kAbsorbTileT - 1) / mla::kAbsorbTileT > 65535)
-    return MLA_ERR_UNSUPPORTED;
+  if ((long long)tokens * h_q * MLA_D_QK >= (1LL << 31) || h_q > 65535) return MLA_ERR_UNSUPPORTED;
   return MLA_OK;
 }
 

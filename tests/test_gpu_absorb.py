@@ -23,7 +23,7 @@ def _close(got, want):
     assert (np.abs(g - want) <= bound).all(), float(np.abs(g - want).max())
 
 
-@pytest.mark.parametrize("tokens,h", [(1, 128), (15, 16), (64, 128), (65, 3), (264, 128), (130, 7)])
+@pytest.mark.parametrize("tokens,h", [(1, 128), (15, 16), (64, 128), (65, 3), (264, 128), (130, 7), (1000, 5)])
 def test_absorb_q_parity(tokens, h):
     rng = np.random.Generator(np.random.PCG64(tokens * 1000 + h))
     print(f"[absorb_q] tokens={tokens} h={h}", flush=True)
@@ -36,7 +36,7 @@ def test_absorb_q_parity(tokens, h):
     assert torch.equal(got[..., 512:].cpu(), qr)            # the RoPE part is copied bit for bit
 
 
-@pytest.mark.parametrize("tokens,h", [(1, 128), (15, 16), (64, 128), (65, 3), (264, 128), (130, 7)])
+@pytest.mark.parametrize("tokens,h", [(1, 128), (15, 16), (64, 128), (65, 3), (264, 128), (130, 7), (1000, 5)])
 def test_absorb_o_parity(tokens, h):
     rng = np.random.Generator(np.random.PCG64(tokens * 1000 + h + 7))
     print(f"[absorb_o] tokens={tokens} h={h}", flush=True)
