@@ -22,8 +22,8 @@
 // lies inside b's pages), so min/max over b are found with LDS atomics at
 // those two, which makes the result independent of thread order, and the
 // interior workers' rows are written without a lookup (one thread per
-// sequence walks its workers: a long sequence split many ways costs a loop
-// of plain stores, not of dependent LDS reads).
+// sequence walks its workers, or, for a sequence split more than eight ways,
+// its whole wave: plain stores, not dependent LDS reads).
 //
 // One workgroup, no host synchronisation: the kernel runs on the stream after
 // whatever wrote cache_seqlens.
@@ -118,6 +118,25 @@ __global__ __launch_bounds__(kSchedThreads) void mla_sched_kernel(SchedParams p)
     }
     row[5] = 0; row[6] = 0; row[7] = 0;
   }
+  // Row of worker w for sequence b (pages from unit first_unit, n of them,
+  // workers wf..wl).
+  auto write_row = [&](long long w, int b, long long first_unit, int n, long long wf, long long wl)
+      __attribute__((always_inline)) {
+    int32_t* row = p.meta + (size_t)w * kMetaInts;
+    const bool interior = w > wf && w < wl;
+    if (interior || first_seq[w] == b) {
+      const long long lo = w * Q - first_unit;
+      row[0] = b;
+      row[1] = (int32_t)(lo > 0 ? lo : 0);
+      row[4] = (int32_t)(w - wf);
+    }
+    if (interior || last_seq[w] == b) {
+      const long long hi = (w + 1) * Q - first_unit;
+      row[2] = b;
+      row[3] = (int32_t)(hi < n ? hi : n);
+    }
+  };
+  const int lane = tid & 63;
   start_carry = 0;
   for (int base = 0; base < B; base += kSchedThreads) {
     const int b = base + tid;
@@ -125,23 +144,24 @@ __global__ __launch_bounds__(kSchedThreads) void mla_sched_kernel(SchedParams p)
     long long chunk_cost;
     const long long s_b = start_carry + block_exclusive_scan(b < B ? (long long)F + n : 0, scan_tmp, chunk_cost);
     start_carry += chunk_cost;
-    if (n == 0) continue;
     const long long first_unit = s_b + H;
-    const long long wf = first_unit / Q, wl = (first_unit + n - 1) / Q;
-    for (long long w = wf; w <= wl; ++w) {
-      int32_t* row = p.meta + (size_t)w * kMetaInts;
-      const bool interior = w > wf && w < wl;
-      if (interior || first_seq[w] == b) {
-        const long long lo = w * Q - first_unit;
-        row[0] = b;
-        row[1] = (int32_t)(lo > 0 ? lo : 0);
-        row[4] = (int32_t)(w - wf);
-      }
-      if (interior || last_seq[w] == b) {
-        const long long hi = (w + 1) * Q - first_unit;
-        row[2] = b;
-        row[3] = (int32_t)(hi < n ? hi : n);
-      }
+    const long long wf = n > 0 ? first_unit / Q : 0, wl = n > 0 ? (first_unit + n - 1) / Q : -1;
+    // A sequence over a few workers walks them alone; one over more than
+    // kWalkAlone is walked by its whole wave, 64 workers at a time, so a
+    // sequence split a hundred ways costs two passes, not a hundred.
+    constexpr long long kWalkAlone = 8;
+    const bool shared = wl - wf >= kWalkAlone;
+    if (!shared)
+      for (long long w = wf; w <= wl; ++w) write_row(w, b, first_unit, n, wf, wl);
+    unsigned long long todo = __ballot(shared);
+    while (todo) {
+      const int src = __builtin_ctzll(todo);
+      todo &= todo - 1;
+      const int b_s = __shfl(b, src);
+      const int n_s = __shfl(n, src);
+      const long long fu_s = __shfl(first_unit, src);
+      const long long wf_s = __shfl(wf, src), wl_s = __shfl(wl, src);
+      for (long long w = wf_s + lane; w <= wl_s; w += 64) write_row(w, b_s, fu_s, n_s, wf_s, wl_s);
     }
   }
 }
