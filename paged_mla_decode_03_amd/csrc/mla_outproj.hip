@@ -131,14 +131,22 @@ __global__ __launch_bounds__(kOutProjThreads, 1) void mla_outproj_kernel(OutProj
         for (int r = 0; r < 4; ++r)
           acc[d][r] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[B][h][d], af[B][h][r], acc[d][r], 0, 0, 0);
   };
+  // The scheduling barriers keep each pair's loads ahead of the other
+  // buffer's MFMAs: left free, the compiler moves the loads down to just
+  // before their own MFMAs (fewer live registers) and waits for them there,
+  // so nothing is in flight during the MFMAs.
   if (pairs > 0) {
     load_pair.template operator()<0>(0);
     int pp = 0;
     for (; pp + 2 <= pairs; pp += 2) {
       load_pair.template operator()<1>(pp + 1);
+      __builtin_amdgcn_sched_barrier(0);
       mma_pair.template operator()<0>();
+      __builtin_amdgcn_sched_barrier(0);
       load_pair.template operator()<0>(pp + 2);
+      __builtin_amdgcn_sched_barrier(0);
       mma_pair.template operator()<1>();
+      __builtin_amdgcn_sched_barrier(0);
     }
     if (pp < pairs) mma_pair.template operator()<0>();   // the last pair of an odd count, in buffer 0
   }
