@@ -64,9 +64,10 @@ def parse():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=15.0)
-    ap.add_argument("--op", choices=["decode", "append", "absorb", "outproj", "fp8"], default="decode",
+    ap.add_argument("--op", choices=["decode", "append", "absorb", "outproj", "fp8", "lds"], default="decode",
                     help="append: time the cache append of the workload's new tokens instead; absorb: the "
-                         "per-head projections before and after the decode (each prints its own JSON line)")
+                         "per-head projections before and after the decode (each prints its own JSON line); "
+                         "lds: the LDS read rate of one wave, by read kind, at one and two waves per SIMD")
     ap.add_argument("--append-tokens", type=int, default=0,
                     help="new tokens per sequence for --op append (default: the workload's s_q)")
     ap.add_argument("--copy-mb", type=int, default=0,
@@ -652,6 +653,37 @@ def measure_workload(name: str, args, dev, want_cpu: bool) -> dict:
     return res
 
 
+def bench_lds(args):
+    """The rate at which one wave reads LDS (mla_lds_read_rate): for each read
+    kind, one workgroup per CU of four waves (one per SIMD, as the 128-row
+    decode workgroup) and of eight (two per SIMD, as the 64-row one); cycles
+    are the shader clock's (s_memtime) over each workgroup's loop, median over
+    the workgroups of the third of three launches.  A decode stream whose
+    fragment reads per MFMA exceed this rate waits on LDS, not on the matrix
+    core."""
+    import torch
+    sys.path.insert(0, ROOT)
+    from paged_mla_decode_03_amd.binding import LDS_READ_KINDS, lds_read_rate
+    dev = torch.device("cuda", 0)
+    blocks = torch.cuda.get_device_properties(dev).multi_processor_count
+    iters = 1024
+    rates = {}
+    for kind, (_, lane_bytes) in LDS_READ_KINDS.items():
+        for waves in (4, 8):
+            for _ in range(3):
+                cyc = lds_read_rate(kind, waves, iters, blocks, dev)
+            torch.cuda.synchronize()
+            c = float(np.median(cyc.cpu().numpy()))
+            reads = 64 * iters
+            rates[f"{kind}/{waves}w"] = {"cycles_per_read": round(c / reads, 2),
+                                         "bytes_per_cycle_per_wave": round(reads * 64 * lane_bytes / c, 2),
+                                         "bytes_per_cycle_per_cu": round(waves * reads * 64 * lane_bytes / c, 1)}
+    print(json.dumps({"metric": "LDS read rate of one wave", "unit": "cycles per read",
+                      "config": {"workload": "lds_read_rate", "blocks": blocks, "reads_per_wave": 64 * iters,
+                                 "in_flight_per_wave": 8},
+                      "rates": rates}))
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -670,6 +702,9 @@ def main():
         return
     if args.op == "fp8":
         bench_fp8(args)
+        return
+    if args.op == "lds":
+        bench_lds(args)
         return
 
     import torch

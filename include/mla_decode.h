@@ -300,6 +300,23 @@ int mla_pages_release(int32_t* free_pages, int32_t* state, int num_pages, const 
  * in the (never expected) case that the folded data match a fixed pattern. */
 int mla_stream_read(const void* src, size_t bytes, void* sink, void* stream);
 
+/* Measurement helper, not a step of the method: the rate at which one wave
+ * reads LDS, the resource that feeds the decode's MFMAs their K, V and P
+ * fragments.  Launches `blocks` workgroups of `waves` waves (4: one per SIMD,
+ * as the 128-row decode workgroup; 8: two per SIMD, as the 64-row one); every
+ * wave issues 64 * iters conflict-free reads of one kind from a 64 KB LDS
+ * buffer, eight in flight, and each workgroup's first wave stores the shader
+ * clock cycles (s_memtime) of its loop in cycles[block].  The rate per wave is
+ * 64 * iters * (bytes per read) / cycles, bytes per read being 64 lanes
+ * times 16, 8, 8 or 4 for kind 0 (ds_read_b128), 1 (ds_read_b64), 2
+ * (ds_read_b64_tr_b16) or 3 (ds_read_b32).
+ *   cycles [dev] int64 [blocks], written.  sink [dev] 16 bytes, written only
+ *   in the (never expected) case that the folded data match a fixed pattern.
+ * Errors (returned, nothing launched): MLA_ERR_INVALID_ARG for null pointers,
+ * kind outside 0..3, waves other than 4 or 8, non-positive iters or blocks;
+ * MLA_ERR_UNSUPPORTED for misaligned pointers. */
+int mla_lds_read_rate(int kind, int waves, int iters, int blocks, int64_t* cycles, void* sink, void* stream);
+
 /* The step before decode: write the latent rows of new tokens into the
  * paged cache.  The cache keeps the [c^KV (512); k^R (64)] row of every
  * token already seen, and a step computes only the new token's row and adds

@@ -85,6 +85,8 @@ def _load():
     lib.mla_pages_release.argtypes = [vp, vp, c_int, vp, vp, c_int, vp, c_int, vp]
     lib.mla_stream_read.restype = c_int
     lib.mla_stream_read.argtypes = [vp, c_size_t, vp, vp]
+    lib.mla_lds_read_rate.restype = c_int
+    lib.mla_lds_read_rate.argtypes = [c_int, c_int, c_int, c_int, vp, vp, vp]
     lib.mla_decode_paged_fp8.restype = c_int
     lib.mla_decode_paged_fp8.argtypes = [vp, vp, c_float] + decode_args[2:]
     lib.mla_kvcache_append_fp8.restype = c_int
@@ -485,6 +487,24 @@ def stream_read(src: torch.Tensor, sink: Optional[torch.Tensor] = None) -> None:
         sink = torch.empty(4, dtype=torch.int32, device=device)
     _check("mla_stream_read", _load().mla_stream_read(src.data_ptr(), src.numel() * src.element_size(),
                                                       sink.data_ptr(), _stream_handle(device)))
+
+
+LDS_READ_KINDS = {"ds_read_b128": (0, 16), "ds_read_b64": (1, 8), "ds_read_b64_tr_b16": (2, 8), "ds_read_b32": (3, 4)}
+
+
+def lds_read_rate(kind: str, waves: int, iters: int, blocks: int, device) -> torch.Tensor:
+    """Launch the library's LDS-rate probe (a measurement helper): returns the
+    int64 [blocks] tensor of shader-clock cycles each workgroup's loop took
+    (64 * iters reads of `kind` per wave; see LDS_READ_KINDS for the bytes
+    per lane).  Not synchronised."""
+    if kind not in LDS_READ_KINDS:
+        raise ValueError(f"kind must be one of {sorted(LDS_READ_KINDS)}")
+    cycles = torch.zeros(blocks, dtype=torch.int64, device=device)
+    sink = torch.empty(4, dtype=torch.int32, device=device)
+    _check("mla_lds_read_rate", _load().mla_lds_read_rate(LDS_READ_KINDS[kind][0], waves, iters, blocks,
+                                                          cycles.data_ptr(), sink.data_ptr(),
+                                                          _stream_handle(torch.device(device))))
+    return cycles
 
 
 def kvcache_append_fp8(kv_new: torch.Tensor, kvcache_fp8: torch.Tensor, kv_scale: float, block_table: torch.Tensor,

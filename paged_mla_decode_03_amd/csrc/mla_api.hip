@@ -502,6 +502,21 @@ int mla_stream_read(const void* src, size_t bytes, void* sink, void* stream) {
   return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
 
+int mla_lds_read_rate(int kind, int waves, int iters, int blocks, int64_t* cycles, void* sink, void* stream) {
+  if (!cycles || !sink || iters <= 0 || blocks <= 0) return MLA_ERR_INVALID_ARG;
+  if (kind < 0 || kind > 3 || (waves != 4 && waves != 8)) return MLA_ERR_INVALID_ARG;
+  if (!aligned(cycles, 8) || !aligned(sink, 16)) return MLA_ERR_UNSUPPORTED;
+  using Kernel = void (*)(int, long long*, uint4*);
+  static const Kernel kernels[2][4] = {
+      {mla::mla_lds_rate_kernel<0, 4>, mla::mla_lds_rate_kernel<1, 4>, mla::mla_lds_rate_kernel<2, 4>,
+       mla::mla_lds_rate_kernel<3, 4>},
+      {mla::mla_lds_rate_kernel<0, 8>, mla::mla_lds_rate_kernel<1, 8>, mla::mla_lds_rate_kernel<2, 8>,
+       mla::mla_lds_rate_kernel<3, 8>}};
+  hipLaunchKernelGGL(kernels[waves == 8][kind], dim3(blocks), dim3(waves * 64), 0, (hipStream_t)stream, iters,
+                     (long long*)cycles, (uint4*)sink);
+  return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
 int mla_pages_init(int32_t* free_pages, int32_t* state, int num_pages, void* stream) {
   if (!free_pages || !state || num_pages <= 0) return MLA_ERR_INVALID_ARG;
   if (!aligned(free_pages, 4) || !aligned(state, 4)) return MLA_ERR_UNSUPPORTED;

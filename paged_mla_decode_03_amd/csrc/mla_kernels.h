@@ -80,6 +80,7 @@ struct SchedParams {
 
 constexpr int kCheckThreads = 1024;
 constexpr int kStreamThreads = 512;
+constexpr int kLdsRateBytes = 65536;              // LDS the LDS-rate probe reads
 constexpr int kPagesThreads = 1024;
 
 // Whole-page allocator: a stack of free page ids in device memory.
@@ -111,6 +112,8 @@ __global__ void mla_combine_wide_kernel(CombineParams p);
 __global__ void mla_sched_kernel(SchedParams p);
 __global__ void mla_check_kernel(CheckParams p);
 __global__ void mla_stream_read_kernel(const uint4* __restrict__ src, size_t n16, uint4* sink);
+template <int kKind, int kWavesIn>
+__global__ void mla_lds_rate_kernel(int iters, long long* cycles, uint4* sink);
 __global__ void mla_pages_init_kernel(PagesParams p);
 __global__ void mla_pages_reserve_kernel(PagesParams p);
 __global__ void mla_pages_release_kernel(PagesParams p);

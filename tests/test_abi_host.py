@@ -219,3 +219,20 @@ def test_outproj_rejects_invalid_arguments():
     assert lib.mla_outproj(FAKE, FAKE, FAKE, 4, 200, 128, FAKE, 1 << 30, None) == -2    # k % 128
     assert lib.mla_outproj(FAKE, FAKE, FAKE, 4, 256, 100, FAKE, 1 << 30, None) == -2    # n % 128
     assert lib.mla_outproj(FAKE + 8, FAKE, FAKE, 4, 256, 128, FAKE, 1 << 30, None) == -2
+
+
+def test_lds_read_rate_rejects_invalid_arguments():
+    lib = _lib()
+    c = ctypes.c_int
+    vp = ctypes.c_void_p
+    lib.mla_lds_read_rate.restype = c
+    lib.mla_lds_read_rate.argtypes = [c, c, c, c, vp, vp, vp]
+    good = vp(4096)   # never dereferenced: every call below fails its argument checks first
+    assert lib.mla_lds_read_rate(0, 4, 1, 1, None, good, None) != 0
+    assert lib.mla_lds_read_rate(0, 4, 1, 1, good, None, None) != 0
+    assert lib.mla_lds_read_rate(4, 4, 1, 1, good, good, None) != 0
+    assert lib.mla_lds_read_rate(-1, 4, 1, 1, good, good, None) != 0
+    assert lib.mla_lds_read_rate(0, 6, 1, 1, good, good, None) != 0
+    assert lib.mla_lds_read_rate(0, 4, 0, 1, good, good, None) != 0
+    assert lib.mla_lds_read_rate(0, 4, 1, 0, good, good, None) != 0
+    assert lib.mla_lds_read_rate(0, 4, 1, 1, vp(4100), good, None) != 0
