@@ -33,21 +33,31 @@ namespace mla {
 
 namespace {
 
-// Exclusive scan over one value per thread of the workgroup; `total` gets the sum.
+// Exclusive scan over one value per thread of the workgroup; `total` gets the
+// sum.  Each wave scans its 64 values with lane shifts, the waves' totals
+// meet in LDS, and every thread adds those of the waves before it: two
+// barriers a scan.
 __device__ long long block_exclusive_scan(long long v, long long* tmp, long long& total) {
   const int tid = threadIdx.x;
-  tmp[tid] = v;
-  __syncthreads();
-  for (int off = 1; off < kSchedThreads; off <<= 1) {
-    long long add = tid >= off ? tmp[tid - off] : 0;
-    __syncthreads();
-    tmp[tid] += add;
-    __syncthreads();
+  const int lane = tid & 63, wave = tid >> 6;
+  long long x = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const long long y = __shfl_up(x, off);
+    if (lane >= off) x += y;
   }
-  long long incl = tmp[tid];
-  total = tmp[kSchedThreads - 1];
+  if (lane == 63) tmp[wave] = x;
   __syncthreads();
-  return incl - v;
+  long long before = 0, sum = 0;
+#pragma unroll
+  for (int w = 0; w < kSchedThreads / 64; ++w) {
+    const long long t = tmp[w];
+    before += w < wave ? t : 0;
+    sum += t;
+  }
+  total = sum;
+  __syncthreads();   // tmp is rewritten by the next scan
+  return before + x - v;
 }
 
 // Pages of a sequence of `seqlen` tokens (0 for seqlen <= 0; no overflow
@@ -68,11 +78,19 @@ __global__ __launch_bounds__(kSchedThreads) void mla_sched_kernel(SchedParams p)
     last_seq[w] = -1;
   }
 
+  // Page counts, read once for the first kSchedThreads sequences (every
+  // sequence of a batch that fits the workgroup) and again per later chunk.
+  const int n0 = tid < B ? pages_of(p.seqlens[tid]) : 0;
+  auto pages_at = [&](int base) __attribute__((always_inline)) {
+    const int b = base + tid;
+    return base == 0 ? n0 : (b < B ? pages_of(p.seqlens[b]) : 0);
+  };
+
   // Total cost T and quota Q.
   long long T = 0;
   for (int base = 0; base < B; base += kSchedThreads) {
     const int b = base + tid;
-    const long long cost = b < B ? (long long)F + pages_of(p.seqlens[b]) : 0;
+    const long long cost = b < B ? (long long)F + pages_at(base) : 0;
     long long chunk_total;
     block_exclusive_scan(cost, scan_tmp, chunk_total);
     T += chunk_total;
@@ -83,7 +101,7 @@ __global__ __launch_bounds__(kSchedThreads) void mla_sched_kernel(SchedParams p)
   long long start_carry = 0, split_carry = 0;
   for (int base = 0; base < B; base += kSchedThreads) {
     const int b = base + tid;
-    const int n = b < B ? pages_of(p.seqlens[b]) : 0;
+    const int n = pages_at(base);
     long long chunk_cost, chunk_splits;
     const long long s_b = start_carry + block_exclusive_scan(b < B ? (long long)F + n : 0, scan_tmp, chunk_cost);
     const long long first_unit = s_b + H;
@@ -140,7 +158,7 @@ __global__ __launch_bounds__(kSchedThreads) void mla_sched_kernel(SchedParams p)
   start_carry = 0;
   for (int base = 0; base < B; base += kSchedThreads) {
     const int b = base + tid;
-    const int n = b < B ? pages_of(p.seqlens[b]) : 0;
+    const int n = pages_at(base);
     long long chunk_cost;
     const long long s_b = start_carry + block_exclusive_scan(b < B ? (long long)F + n : 0, scan_tmp, chunk_cost);
     start_carry += chunk_cost;

@@ -36,6 +36,9 @@ def test_workload_metadata_bit_exact(name):
     ([5] * 3000, None),              # batch larger than the scheduler's workgroup
     ([1], 1),
     ([100000, 3, 0, 5000], 4096),
+    ([64 * (i % 37) + i % 5 for i in range(256)], None),    # exactly one workgroup of sequences
+    ([64 * (i % 41) + i % 7 for i in range(257)], 300),     # one past it
+    ([(i * 7919) % 20000 for i in range(1000)], 333),       # four chunks, ragged lengths and zeros
 ])
 def test_edge_metadata_bit_exact(seqlens, W):
     _check(seqlens, 128, 1, W)
