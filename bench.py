@@ -70,6 +70,10 @@ def parse():
                          "lds: the LDS read rate of one wave, by read kind, at one and two waves per SIMD")
     ap.add_argument("--append-tokens", type=int, default=0,
                     help="new tokens per sequence for --op append (default: the workload's s_q)")
+    ap.add_argument("--cache", choices=["streamed", "resident"], default="streamed",
+                    help="resident: remap every sequence's pages into the first 64 pages of one pool (4.7 MB, "
+                         "held in L2 / MALL), the same decode without HBM streaming, to separate its cost; "
+                         "streamed (default): the workload as generated, over pools rotated per step")
     ap.add_argument("--copy-mb", type=int, default=0,
                     help="before the timed steps, run one plain device copy of this many MiB: the known-size "
                          "kernel that scales the decode kernel's HBM counters in a rocprofv3 --pmc run")
@@ -511,6 +515,11 @@ def measure_workload(name: str, args, dev, want_cpu: bool) -> dict:
     seqlens = inp.cache_seqlens.to(dev)
     kv_bytes = inp.kvcache.numel() * 2
     n_pools = max(2, -(-2 * MALL_BYTES // kv_bytes) + 1)
+    if getattr(args, "cache", "streamed") == "resident":
+        # Same shapes and lengths; every page id folded into the pool's first
+        # 64 pages, so the decode reads a cache that stays on chip.
+        bt = torch.where(bt >= 0, bt % 64, bt)
+        n_pools = 1
     pools = [inp.kvcache.to(dev)]
     for _ in range(1, n_pools):
         pools.append(pools[0].clone())
@@ -613,7 +622,7 @@ def measure_workload(name: str, args, dev, want_cpu: bool) -> dict:
         "config": {"workload": name, "batch": w.batch, "s_q": w.s_q, "h_q": w.h_q, "h_kv": w.h_kv, "d_qk": 576,
                    "dv": 512, "page_size": 64, "causal": w.causal, "seqlen_total": int(L.sum()),
                    "seqlen_max": int(L.max()), "seed": args.seed, "kv_pools": n_pools, "num_workers": W,
-                   "max_splits": int(splits.max())},
+                   "max_splits": int(splits.max()), "cache": getattr(args, "cache", "streamed")},
         "us_per_step": round(ms_per_step * 1e3, 2),
         "step_event_us": round(event_ms_per_step * 1e3, 2),
         "step_us": {"median": round(float(np.median(step_us)), 2), "p10": round(_pct(step_us, 10), 2),
@@ -635,7 +644,7 @@ def measure_workload(name: str, args, dev, want_cpu: bool) -> dict:
                           "tflops": round(counts["flops"] / kernel_mean_s / 1e12, 2),
                           "hbm_frac": round(decode_bytes / kernel_mean_s / 1e9 / HBM_PEAK_GBS, 4),
                           "mfma_frac": round(counts["flops"] / kernel_mean_s / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
-                          "traffic": measured_traffic(w)},
+                          "traffic": measured_traffic(w) if getattr(args, "cache", "streamed") == "streamed" else None},
         "algorithmic_bytes": counts["total_bytes"],
         "algorithmic_flops": counts["flops"],
         "combine_bytes": combine_bytes,
