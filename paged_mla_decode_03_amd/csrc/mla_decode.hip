@@ -268,13 +268,15 @@ __device__ __forceinline__ void decode_role(const DecodeParams& p, DecodeShared<
       if (i < 2 || units == 3) {
         const u32x4 codes = *(const __attribute__((address_space(3))) u32x4*)(raw + (uint32_t)(i * 8 * 1024));
         u32x4 o[2];
+        // Two codes to two bf16 in one instruction (scale 1: every E4M3
+        // value is a bf16 value, so the conversion is exact).
 #pragma unroll
         for (int h = 0; h < 4; ++h) {
-          typedef float f32x2 __attribute__((ext_vector_type(2)));
-          const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)codes[h], false);
-          const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)codes[h], true);
-          o[h >> 1][2 * (h & 1)] = pack_bf16x2(lo[0], lo[1]);
-          o[h >> 1][2 * (h & 1) + 1] = pack_bf16x2(hi[0], hi[1]);
+          typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+          const bf16x2 lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes[h], 1.0f, false);
+          const bf16x2 hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes[h], 1.0f, true);
+          o[h >> 1][2 * (h & 1)] = __builtin_bit_cast(uint32_t, lo);
+          o[h >> 1][2 * (h & 1) + 1] = __builtin_bit_cast(uint32_t, hi);
         }
         *(u32x4*)(half + raw_t0[i]) = o[0];
         *(u32x4*)(half + raw_t1[i]) = o[1];

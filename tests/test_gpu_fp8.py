@@ -147,3 +147,27 @@ def test_fp8_append_then_decode_end_to_end():
     torch.cuda.synchronize()
     O, LSE = mo.mla_decode_fp8_ref(inp.q, want, scale, bt, L.numpy(), 512)
     compare(o.float().cpu().double().numpy(), lse.cpu().double().numpy(), O, LSE, label="fp8 append then decode")
+
+
+def test_fp8_one_token_returns_every_code_exactly():
+    """A sequence of one token gives that token's value row as O, with weight
+    exactly 1: at kv_scale 1 every output element is the E4M3 value of its
+    code, which bf16 holds exactly.  The row carries all 254 finite codes
+    (twice over the 512 columns), so the decode's code-to-bf16 conversion is
+    checked bit for bit against the format's definition."""
+    inp = _custom(1, 16, 1, False, [1, 1], seed=3)
+    kv = inp.kvcache.clone()
+    codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF)] * 3, dtype=np.uint8)[:512]
+    bt = inp.block_table.numpy()
+    for b in range(2):
+        kv[int(bt[b, 0]), 0, 0, :512] = torch.from_numpy(np.roll(codes, 37 * b))
+    inp.kvcache = kv
+    inp.extra["kv_scale"] = 1.0
+    o, lse, _ = _run(inp)
+    for b in range(2):
+        want = mo.fp8_e4m3_decode_ref(np.roll(codes, 37 * b))
+        got = o[b, 0]                                   # [h_q][512]
+        assert np.array_equal(got, np.broadcast_to(want, got.shape)), (b, np.abs(got - want).max())
+    O, LSE = _oracle(inp)
+    np.testing.assert_allclose(lse, LSE, atol=1e-3)
+
